@@ -1,1 +1,193 @@
-"""Grouped-query attention over a paged (HND) KV cache with per-head sinks."""
+"""Grouped-query attention over a paged (HND) KV cache with per-head sinks.
+
+Thin ctypes binding of the C ABI in include/attn_sinks.h (libattn_sinks.so,
+built for gfx950 by ``python -m gqa_paged_attention_amd.build``).  The
+functions below only marshal torch tensors into pointers and sizes; every
+step of the computation runs in the library's HIP kernels.  PyTorch supplies
+device memory and the current stream.  There is no CPU fallback: if the
+library is missing, calling any entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # imported first so the library binds to the HIP runtime torch loaded
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libattn_sinks.so")
+
+ATTN_DTYPE_F32 = 0
+ATTN_DTYPE_BF16 = 1
+_DTYPE_CODE = {torch.float32: ATTN_DTYPE_F32, torch.bfloat16: ATTN_DTYPE_BF16}
+PAGE_SIZE = 16
+
+_lib = None
+
+
+class AttnSinksError(RuntimeError):
+    """A nonzero status from the library (nothing was enqueued unless ATTN_ERR_HIP)."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"attn_sinks status {status}: {message}")
+        self.status = status
+
+
+def library():
+    """Load libattn_sinks.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m gqa_paged_attention_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    I, P, F, Z = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    lib.attn_sinks_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.attn_sinks_decode_workspace_bytes.restype = Z
+    lib.attn_sinks_decode.argtypes = [I] * 9 + [P] * 6 + [F, P, P, Z, P]
+    lib.attn_sinks_decode.restype = I
+    lib.attn_sinks_prefill.argtypes = [I] * 11 + [P] * 7 + [F, P, P]
+    lib.attn_sinks_prefill.restype = I
+    lib.attn_sinks_status_string.argtypes = [I]
+    lib.attn_sinks_status_string.restype = ctypes.c_char_p
+    lib.attn_sinks_version.argtypes = []
+    lib.attn_sinks_version.restype = I
+    _lib = lib
+    return lib
+
+
+def attn_sinks_status_string(status: int) -> str:
+    return library().attn_sinks_status_string(int(status)).decode()
+
+
+def attn_sinks_version() -> int:
+    return int(library().attn_sinks_version())
+
+
+def attn_sinks_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                      head_dim: int, max_seq_len: int) -> int:
+    return int(library().attn_sinks_decode_workspace_bytes(
+        int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim), int(max_seq_len)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _check_dense(name: str, t: Optional[torch.Tensor], dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _raise(status: int):
+    if status != 0:
+        raise AttnSinksError(status, attn_sinks_status_string(status))
+
+
+def attn_sinks_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_table: torch.Tensor, seq_lens: torch.Tensor,
+                      sinks: Optional[torch.Tensor], scale: float, out: torch.Tensor,
+                      workspace: Optional[torch.Tensor], max_seq_len: int, stream=None) -> None:
+    """Enqueue attn_sinks_decode on `stream` (default: torch's current stream).
+
+    q [B][Hq][d], k_cache/v_cache [num_pages][Hkv][16][d], block_table
+    [B][max_pages] int32, seq_lens [B] int32, sinks [Hq] fp32 or None, out like
+    q, workspace a byte (uint8) tensor of at least
+    attn_sinks_decode_workspace_bytes(...) bytes.
+    """
+    dt = _DTYPE_CODE.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out)):
+        _check_dense(name, t, q.dtype)
+    _check_dense("block_table", block_table, torch.int32)
+    _check_dense("seq_lens", seq_lens, torch.int32)
+    _check_dense("sinks", sinks, torch.float32)
+    _check_dense("workspace", workspace)
+    B, Hq, d = q.shape
+    num_pages, Hkv, P, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != (B, Hq, d):
+        raise ValueError("q / k_cache / v_cache / out shapes disagree")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError("block_table / seq_lens do not match the batch")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    status = library().attn_sinks_decode(
+        dt, B, Hq, Hkv, d, P, num_pages, block_table.shape[1], int(max_seq_len),
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(sinks),
+        ctypes.c_float(scale), _ptr(out), _ptr(workspace), ctypes.c_size_t(ws_bytes),
+        _stream_handle(stream))
+    _raise(status)
+
+
+def attn_sinks_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       block_table: torch.Tensor, seq_lens: torch.Tensor,
+                       cu_seqlens_q: torch.Tensor, sinks: Optional[torch.Tensor], scale: float,
+                       out: torch.Tensor, max_q_len: int, max_seq_len: int, stream=None) -> None:
+    """Enqueue attn_sinks_prefill on `stream` (default: torch's current stream).
+
+    q [total_q][Hq][d] ragged by cu_seqlens_q [B+1] int32; out like q.
+    """
+    dt = _DTYPE_CODE.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out)):
+        _check_dense(name, t, q.dtype)
+    _check_dense("block_table", block_table, torch.int32)
+    _check_dense("seq_lens", seq_lens, torch.int32)
+    _check_dense("cu_seqlens_q", cu_seqlens_q, torch.int32)
+    _check_dense("sinks", sinks, torch.float32)
+    T, Hq, d = q.shape
+    num_pages, Hkv, P, d2 = k_cache.shape
+    B = seq_lens.numel()
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != (T, Hq, d):
+        raise ValueError("q / k_cache / v_cache / out shapes disagree")
+    if block_table.dim() != 2 or block_table.shape[0] != B or cu_seqlens_q.numel() != B + 1:
+        raise ValueError("block_table / cu_seqlens_q do not match the batch")
+    status = library().attn_sinks_prefill(
+        dt, B, Hq, Hkv, d, P, num_pages, block_table.shape[1], T, int(max_q_len),
+        int(max_seq_len), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), _ptr(cu_seqlens_q), _ptr(sinks), ctypes.c_float(scale), _ptr(out),
+        _stream_handle(stream))
+    _raise(status)
+
+
+# ------------------------------------------------------------ conveniences
+
+def decode_batch(batch, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Run attn_sinks_decode on a workloads.PagedBatch already on the GPU."""
+    if out is None:
+        out = torch.empty_like(batch.q)
+    if workspace is None:
+        nbytes = attn_sinks_decode_workspace_bytes(batch.num_seqs, batch.num_q_heads,
+                                                   batch.num_kv_heads, batch.head_dim,
+                                                   batch.max_seq_len)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=batch.q.device)
+    attn_sinks_decode(batch.q, batch.k_cache, batch.v_cache, batch.block_table, batch.seq_lens,
+                      batch.sinks, batch.scale, out, workspace, batch.max_seq_len, stream)
+    return out
+
+
+def prefill_batch(batch, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Run attn_sinks_prefill on a workloads.PagedBatch already on the GPU."""
+    if out is None:
+        out = torch.empty_like(batch.q)
+    attn_sinks_prefill(batch.q, batch.k_cache, batch.v_cache, batch.block_table, batch.seq_lens,
+                       batch.cu_seqlens_q, batch.sinks, batch.scale, out, batch.max_q_len,
+                       batch.max_seq_len, stream)
+    return out

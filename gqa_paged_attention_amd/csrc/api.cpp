@@ -1,0 +1,256 @@
+// C ABI of the library: host-side checks, launch configuration, dispatch.
+// Every check runs before anything is enqueued; see include/attn_sinks.h.
+#include "attn_sinks.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdlib>
+#include <mutex>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int kPageSize = 16;
+constexpr int kMaxGroup = 16;
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+// Debug override of the decode split length (tokens per workgroup), read once.
+// Must be a positive multiple of 32 * kDecodeWaves; anything else is ignored.
+int split_override()
+{
+    static int value = 0;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        const char *s = std::getenv("ATTN_SINKS_SPLIT_TOKENS");
+        if (s) {
+            long v = std::strtol(s, nullptr, 10);
+            if (v > 0 && v <= (1 << 20) && v % (32 * attn::kDecodeWaves) == 0)
+                value = (int)v;
+        }
+    });
+    return value;
+}
+
+// Tokens per decode split: the smallest power of two >= 128 for which the
+// grid upper bound (num_seqs * Hkv * ceil(max_seq_len / C)) stays within
+// 8192 workgroups.  Only host integers decide it, so the launch shape never
+// depends on device data and the call can be captured into a graph.
+int decode_split_tokens(int num_seqs, int num_kv_heads, int max_seq_len)
+{
+    if (int o = split_override())
+        return o;
+    const long long pairs = (long long)num_seqs * num_kv_heads;
+    int c = 32 * attn::kDecodeWaves;
+    while (c < (1 << 20)) {
+        const long long splits = (max_seq_len + (long long)c - 1) / c;
+        if (pairs * splits <= 8192)
+            break;
+        c *= 2;
+    }
+    return c;
+}
+
+int check_common(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                 int page_size, int num_pages, int max_pages_per_seq, int max_seq_len)
+{
+    if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16)
+        return ATTN_ERR_UNSUPPORTED;
+    if (!supported_head_dim(head_dim) || page_size != kPageSize)
+        return ATTN_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_pages < 0 ||
+        max_pages_per_seq < 0 || max_seq_len < 0)
+        return ATTN_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0)
+        return ATTN_ERR_SHAPE;
+    if (num_q_heads / num_kv_heads > kMaxGroup)
+        return ATTN_ERR_UNSUPPORTED;
+    // launch grids put sequences and heads on the y/z dimensions (<= 65535)
+    if (num_seqs > 65535 || num_q_heads > 65535)
+        return ATTN_ERR_SHAPE;
+    if ((long long)max_seq_len > (long long)max_pages_per_seq * page_size)
+        return ATTN_ERR_SHAPE;
+    if (max_seq_len > 0 && num_pages == 0)
+        return ATTN_ERR_SHAPE;
+    // element offsets of the pool must fit the kernels' 64-bit arithmetic and
+    // the per-sequence token index must fit an int
+    if ((long long)max_pages_per_seq * page_size > INT_MAX)
+        return ATTN_ERR_SHAPE;
+    return ATTN_OK;
+}
+
+size_t decode_workspace(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                        int max_seq_len, int *splits_out, int *split_tokens_out)
+{
+    const int c = decode_split_tokens(num_seqs, num_kv_heads, max_seq_len);
+    const int splits = (int)(((long long)max_seq_len + c - 1) / c);
+    if (splits_out)
+        *splits_out = splits;
+    if (split_tokens_out)
+        *split_tokens_out = c;
+    return (size_t)num_seqs * (size_t)splits * (size_t)num_q_heads * (size_t)(head_dim + 2) *
+           sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_sinks_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int max_seq_len)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 ||
+        !supported_head_dim(head_dim) || num_q_heads % num_kv_heads != 0 ||
+        num_q_heads / num_kv_heads > kMaxGroup)
+        return 0;
+    return decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, nullptr,
+                            nullptr);
+}
+
+int attn_sinks_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int page_size, int num_pages, int max_pages_per_seq, int max_seq_len,
+                      const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_table, const int32_t *seq_lens, const float *sinks,
+                      float scale, void *out, void *workspace, size_t workspace_bytes,
+                      void *stream)
+{
+    int rc = check_common(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                          num_pages, max_pages_per_seq, max_seq_len);
+    if (rc != ATTN_OK)
+        return rc;
+    if (!std::isfinite(scale))
+        return ATTN_ERR_SHAPE;
+    if (num_seqs == 0)
+        return ATTN_OK;
+    if (!q || !out || !seq_lens || (max_seq_len > 0 && (!k_cache || !v_cache || !block_table)))
+        return ATTN_ERR_NULL;
+    const void *vec[] = {q, k_cache, v_cache, out, workspace};
+    for (const void *p : vec)
+        if (p && !aligned16(p))
+            return ATTN_ERR_ALIGN;
+    const void *words[] = {block_table, seq_lens, sinks};
+    for (const void *p : words)
+        if (p && !aligned4(p))
+            return ATTN_ERR_ALIGN;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    if (dtype == ATTN_DTYPE_F32) {
+        hipError_t e = attn::launch_rows_f32(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             max_pages_per_seq, num_seqs, q, k_cache, v_cache,
+                                             block_table, seq_lens, nullptr, sinks, scale, out,
+                                             s);
+        return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    }
+
+    int splits = 0, split_tokens = 0;
+    const size_t need = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         max_seq_len, &splits, &split_tokens);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return workspace ? ATTN_ERR_WORKSPACE : ATTN_ERR_NULL;
+    attn::DecodeLaunch p;
+    p.dtype = dtype;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.head_dim = head_dim;
+    p.max_pages_per_seq = max_pages_per_seq;
+    p.max_splits = splits;
+    p.split_tokens = split_tokens;
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_table = block_table;
+    p.seq_lens = seq_lens;
+    p.sinks = sinks;
+    p.scale = scale;
+    p.out = out;
+    float *ws = static_cast<float *>(workspace);
+    const size_t rows = (size_t)num_seqs * splits * num_q_heads;
+    p.part_ml = ws;
+    p.part_acc = ws ? ws + rows * 2 : nullptr;
+    p.stream = s;
+    return attn::launch_decode_bf16(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_sinks_prefill(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                       int page_size, int num_pages, int max_pages_per_seq, int total_q,
+                       int max_q_len, int max_seq_len, const void *q, const void *k_cache,
+                       const void *v_cache, const int32_t *block_table, const int32_t *seq_lens,
+                       const int32_t *cu_seqlens_q, const float *sinks, float scale, void *out,
+                       void *stream)
+{
+    int rc = check_common(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                          num_pages, max_pages_per_seq, max_seq_len);
+    if (rc != ATTN_OK)
+        return rc;
+    if (total_q < 0 || max_q_len < 0 || max_q_len > max_seq_len || max_q_len > total_q)
+        return ATTN_ERR_SHAPE;
+    if (!std::isfinite(scale))
+        return ATTN_ERR_SHAPE;
+    if (num_seqs == 0 || total_q == 0)
+        return ATTN_OK;
+    if (!q || !out || !seq_lens || !cu_seqlens_q || !k_cache || !v_cache || !block_table)
+        return ATTN_ERR_NULL;
+    const void *vec[] = {q, k_cache, v_cache, out};
+    for (const void *p : vec)
+        if (p && !aligned16(p))
+            return ATTN_ERR_ALIGN;
+    const void *words[] = {block_table, seq_lens, cu_seqlens_q, sinks};
+    for (const void *p : words)
+        if (p && !aligned4(p))
+            return ATTN_ERR_ALIGN;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    if (dtype == ATTN_DTYPE_F32) {
+        hipError_t e = attn::launch_rows_f32(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             max_pages_per_seq, total_q, q, k_cache, v_cache,
+                                             block_table, seq_lens, cu_seqlens_q, sinks, scale,
+                                             out, s);
+        return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    }
+    attn::PrefillLaunch p;
+    p.dtype = dtype;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.head_dim = head_dim;
+    p.max_pages_per_seq = max_pages_per_seq;
+    p.total_q = total_q;
+    p.max_q_len = max_q_len;
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_table = block_table;
+    p.seq_lens = seq_lens;
+    p.cu_seqlens_q = cu_seqlens_q;
+    p.sinks = sinks;
+    p.scale = scale;
+    p.out = out;
+    p.stream = s;
+    return attn::launch_prefill_bf16(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+const char *attn_sinks_status_string(int status)
+{
+    switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "sizes are inconsistent or out of range";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, page_size or group size";
+    case ATTN_ERR_WORKSPACE: return "decode workspace is smaller than required";
+    case ATTN_ERR_ALIGN: return "a pointer is not aligned as required";
+    case ATTN_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    default: return "unknown status";
+    }
+}
+
+int attn_sinks_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct DecodeLaunch {
+    int dtype;  // 0 f32, 1 bf16
+    int num_seqs, num_q_heads, num_kv_heads, head_dim;
+    int max_pages_per_seq;
+    int max_splits;     // grid size along the KV length
+    int split_tokens;   // tokens per split (a multiple of 32 * waves)
+    const void *q, *k_cache, *v_cache;
+    const int32_t *block_table, *seq_lens;
+    const float *sinks;
+    float scale;
+    void *out;
+    float *part_ml;     // [num_seqs][max_splits][Hq][2]
+    float *part_acc;    // [num_seqs][max_splits][Hq][head_dim]
+    hipStream_t stream;
+};
+
+struct PrefillLaunch {
+    int dtype;
+    int num_seqs, num_q_heads, num_kv_heads, head_dim;
+    int max_pages_per_seq, total_q, max_q_len;
+    const void *q, *k_cache, *v_cache;
+    const int32_t *block_table, *seq_lens, *cu_seqlens_q;
+    const float *sinks;
+    float scale;
+    void *out;
+    hipStream_t stream;
+};
+
+// Waves per decode split workgroup; each wave takes split_tokens / kDecodeWaves
+// consecutive tokens of the split.
+constexpr int kDecodeWaves = 4;
+
+hipError_t launch_decode_bf16(const DecodeLaunch &p);
+hipError_t launch_prefill_bf16(const PrefillLaunch &p);
+// fp32 path (full rows, no split), used for both decode and prefill.
+hipError_t launch_rows_f32(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int max_pages_per_seq, int total_q, const void *q,
+                           const void *k_cache, const void *v_cache, const int32_t *block_table,
+                           const int32_t *seq_lens, const int32_t *cu_seqlens_q,
+                           const float *sinks, float scale, void *out, hipStream_t stream);
+
+}  // namespace attn

@@ -75,10 +75,14 @@ class PagedBatch:
 
     @property
     def max_q_len(self) -> int:
+        if "max_q_len" in self.meta:
+            return self.meta["max_q_len"]
         return int(self.q_lens.max().item()) if self.num_seqs else 0
 
     @property
     def max_seq_len(self) -> int:
+        if "max_seq_len" in self.meta:
+            return self.meta["max_seq_len"]
         return int(self.seq_lens.max().item()) if self.num_seqs else 0
 
     @property
@@ -94,10 +98,17 @@ class PagedBatch:
         return bool(torch.all(self.q_lens == 1).item())
 
     def to(self, device) -> "PagedBatch":
-        """Copy every tensor to `device` (the logical K/V stay on the CPU)."""
+        """Copy every tensor to `device` (the logical K/V stay on the CPU).
+
+        The host-side maxima are computed first and kept, so a GPU batch never
+        needs a device-to-host read to size a call."""
         mv = lambda t: None if t is None else t.to(device)
+        meta = dict(self.meta)
+        meta["max_q_len"] = self.max_q_len
+        meta["max_seq_len"] = self.max_seq_len
         return replace(
             self,
+            meta=meta,
             seq_lens=mv(self.seq_lens),
             cu_seqlens_q=mv(self.cu_seqlens_q),
             q=mv(self.q),
@@ -111,8 +122,10 @@ class PagedBatch:
         """Sequences [start, stop) as a batch that shares the same page pool."""
         cu = self.cu_seqlens_q
         q0, q1 = int(cu[start]), int(cu[stop])
+        meta = {k: v for k, v in self.meta.items() if k not in ("max_q_len", "max_seq_len")}
         return replace(
             self,
+            meta=meta,
             seq_lens=self.seq_lens[start:stop].contiguous(),
             cu_seqlens_q=(cu[start:stop + 1] - q0).to(torch.int32).contiguous(),
             q=self.q[q0:q1].contiguous(),
@@ -206,19 +219,22 @@ def _lay_out(dtype, seq_lens, q_lens, perm, pages_per_seq, max_pages, q, k, v, s
     for b, n in enumerate(pages_per_seq):
         block_table[b, :n] = perm[off:off + n]
         off += n
-    total_kv = int(seq_lens.to(torch.int64).sum())
     fill = float("nan") if poison else 0.0
     k_cache = torch.full((num_pages, num_kv_heads, page_size, head_dim), fill, dtype=tdt)
     v_cache = torch.full_like(k_cache, fill)
     kv_offsets = torch.zeros(B + 1, dtype=torch.int64)
     kv_offsets[1:] = torch.cumsum(seq_lens.to(torch.int64), 0)
-    if total_kv:
-        seq_of_tok = torch.repeat_interleave(torch.arange(B), seq_lens.to(torch.int64))
-        j = torch.arange(total_kv, dtype=torch.int64) - kv_offsets[seq_of_tok]
-        page = block_table[seq_of_tok, j // page_size].to(torch.int64)
-        slot = j % page_size
-        k_cache[page, :, slot, :] = k
-        v_cache[page, :, slot, :] = v
+    # sequence by sequence: logical rows -> [pages][16][Hkv][d] -> HND pages
+    for b in range(B):
+        L, n = int(seq_lens[b]), pages_per_seq[b]
+        if L == 0:
+            continue
+        o = int(kv_offsets[b])
+        ids = block_table[b, :n].to(torch.int64)
+        for src, dst in ((k, k_cache), (v, v_cache)):
+            blk = torch.full((n * page_size, num_kv_heads, head_dim), fill, dtype=tdt)
+            blk[:L] = src[o:o + L]
+            dst[ids] = blk.view(n, page_size, num_kv_heads, head_dim).transpose(1, 2)
 
     cu = torch.zeros(B + 1, dtype=torch.int32)
     cu[1:] = torch.cumsum(q_lens, 0).to(torch.int32)

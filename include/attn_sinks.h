@@ -1,0 +1,158 @@
+/*
+ * attn_sinks.h -- C ABI of the MI355X (gfx950) library for grouped-query
+ * attention over a paged KV cache with per-head attention sinks.
+ *
+ * The operation (both entry points compute it; decode is the case of one
+ * query token per sequence):
+ *
+ *   Each query head h owns a sink logit that joins the softmax as a virtual
+ *   token: it takes part in the maximum and in the sum of exponentials and
+ *   contributes a zero value vector ("GPT OSS" model notes, TensorSharp
+ *   docs/models/gptoss.md, sections 1, 3 "Forward graph" and 4.1; the
+ *   "GPT-OSS on day 0" post, section "Sink Attention").  With G = Hq / Hkv,
+ *   query head h reads KV head g = h / G (GQA, model notes section 4.1).
+ *   For query token i of sequence b (Lq_b query tokens, L_b visible keys,
+ *   the query tokens being the last Lq_b of them):
+ *
+ *     p   = L_b - Lq_b + i                      causal, aligned to the end
+ *     s_j = scale * <q_i,h , K_b,g[j]>          j = 0 .. p
+ *     m   = max(max_j s_j, sink_h)
+ *     out = sum_j e^(s_j - m) V_b,g[j] / (sum_j e^(s_j - m) + e^(sink_h - m))
+ *
+ *   The scale multiplies q.k only; the sink enters unscaled.  A sink of -inf
+ *   (or sinks == NULL) is plain softmax attention.  A row with no visible key
+ *   and a -inf sink yields 0.
+ *
+ * KV page layout (HND, "Hosting Qwen on Blackwell": heads major, the tokens of
+ * one head contiguous):
+ *
+ *   k_cache, v_cache : [num_pages][num_kv_heads][page_size][head_dim]
+ *   token j of sequence b, KV head g lives at
+ *     cache[block_table[b * max_pages_per_seq + j / page_size]][g][j % page_size][:]
+ *   Slots past a sequence's end may hold anything (NaN included); they are
+ *   never read into a result.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers except where noted; sizes are host ints.
+ *   - dtype is ATTN_DTYPE_F32 or ATTN_DTYPE_BF16 and applies to q, k_cache,
+ *     v_cache and out together.  sinks are always fp32.
+ *   - All tensors are dense and row-major without padding.  q, k_cache,
+ *     v_cache, out and the workspace must be 16-byte aligned; the int32 and
+ *     fp32 side arrays 4-byte aligned.
+ *   - stream is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; the caller keeps every buffer alive until the stream
+ *     has passed the call.  The library allocates nothing, frees nothing and
+ *     keeps no pointer after returning, never synchronises and never copies
+ *     device data to the host, so calls can be captured into a HIP graph.
+ *   - Arguments are checked on the host before anything is enqueued; a
+ *     nonzero return value means nothing was enqueued, except ATTN_ERR_HIP,
+ *     which reports a failed launch.  Device data (page ids, lengths, query
+ *     offsets) is not checked: page ids must lie in [0, num_pages), every
+ *     0 <= L_b <= max_seq_len, Lq_b <= L_b, and cu_seqlens_q must be
+ *     non-decreasing from 0 to total_q.  Violations are undefined behaviour.
+ *   - Faults of the device work surface at the caller's next synchronisation.
+ *   - Calls are re-entrant; the library's only state is a read-once cache of
+ *     debug environment settings.
+ */
+#ifndef ATTN_SINKS_H
+#define ATTN_SINKS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_dtype {
+    ATTN_DTYPE_F32 = 0,
+    ATTN_DTYPE_BF16 = 1
+};
+
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    ATTN_ERR_SHAPE = 2,       /* sizes inconsistent or out of range             */
+    ATTN_ERR_UNSUPPORTED = 3, /* dtype / head_dim / page_size / group size      */
+    ATTN_ERR_WORKSPACE = 4,   /* decode workspace smaller than required         */
+    ATTN_ERR_ALIGN = 5,       /* a pointer is not aligned as required          */
+    ATTN_ERR_HIP = 6          /* the HIP runtime rejected a launch              */
+};
+
+/* Supported: head_dim 64 or 128; page_size 16; Hq % Hkv == 0 with
+ * Hq / Hkv <= 16; dtype f32 or bf16.  Other values return
+ * ATTN_ERR_UNSUPPORTED. */
+
+/*
+ * attn_sinks_decode_workspace_bytes -- bytes of device scratch that
+ * attn_sinks_decode needs for these sizes (split-KV partial results: one fp32
+ * running max, one fp32 running sum and head_dim fp32 weighted values per
+ * sequence, split and query head).  Returns 0 for sizes that
+ * attn_sinks_decode would reject.  Depends on host integers only.
+ */
+size_t attn_sinks_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int max_seq_len);
+
+/*
+ * attn_sinks_decode -- one query token per sequence ("decode"), split along
+ * the KV length and merged: each split keeps a running maximum and sum
+ * ("GPT-OSS on day 0", section "Sink Attention": online softmax with a
+ * running max and scale, parallel over heads and over the KV length), and
+ * the sink is folded in once, in the final merge of the splits, so it is
+ * counted exactly once however the KV range was split.
+ *
+ *   q            [num_seqs][num_q_heads][head_dim]          dtype
+ *   k_cache      [num_pages][num_kv_heads][page_size][head_dim] dtype
+ *   v_cache      same shape as k_cache
+ *   block_table  [num_seqs][max_pages_per_seq] int32 page ids
+ *   seq_lens     [num_seqs] int32 visible keys L_b (the new token included)
+ *   sinks        [num_q_heads] fp32, or NULL for "no sink" (-inf)
+ *   scale        softmax scale applied to q.k (finite)
+ *   out          [num_seqs][num_q_heads][head_dim]          dtype (written)
+ *   workspace    device scratch of workspace_bytes bytes, at least
+ *                attn_sinks_decode_workspace_bytes(...); contents on entry do
+ *                not matter and are overwritten.
+ *   max_seq_len  host upper bound of every seq_lens[b]; must not exceed
+ *                max_pages_per_seq * page_size.
+ */
+int attn_sinks_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int page_size, int num_pages, int max_pages_per_seq, int max_seq_len,
+                      const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_table, const int32_t *seq_lens, const float *sinks,
+                      float scale, void *out, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/*
+ * attn_sinks_prefill -- ragged batch of query chunks with causal masking
+ * (model notes section 3: causal mask before the sink softmax).  The chunk of
+ * sequence b is query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and sits at
+ * the end of that sequence's L_b visible keys, so the rows of a chunk over a
+ * cached prefix see the whole prefix.  The sink is folded into each row's
+ * final normalisation.
+ *
+ *   q             [total_q][num_q_heads][head_dim]          dtype
+ *   k_cache/v_cache, block_table, sinks, scale: as for decode
+ *   seq_lens      [num_seqs] int32 visible keys L_b, chunk included
+ *   cu_seqlens_q  [num_seqs + 1] int32 query offsets, 0 .. total_q
+ *   out           [total_q][num_q_heads][head_dim]          dtype (written)
+ *   max_q_len     host upper bound of every chunk length Lq_b
+ *   max_seq_len   host upper bound of every L_b (<= max_pages_per_seq*page_size)
+ */
+int attn_sinks_prefill(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                       int page_size, int num_pages, int max_pages_per_seq, int total_q,
+                       int max_q_len, int max_seq_len, const void *q, const void *k_cache,
+                       const void *v_cache, const int32_t *block_table, const int32_t *seq_lens,
+                       const int32_t *cu_seqlens_q, const float *sinks, float scale, void *out,
+                       void *stream);
+
+/* Static English text for a status code (never NULL). */
+const char *attn_sinks_status_string(int status);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int attn_sinks_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_SINKS_H */
