@@ -1,0 +1,404 @@
+#!/usr/bin/env python3
+"""Benchmark of paged GQA attention with per-head sinks on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode|all]
+
+One step is one decode pass (split pass + merge pass) of the gpt-oss-20b-shaped
+decode workload: 64 sequences x 1 query token, 64 q / 8 KV heads, head_dim 64,
+context lengths uniform in [1024, 8192], 16-token HND pages, bf16, seeded
+synthetic data.  Inputs are resident in HBM before timing starts.  L2 and the
+Infinity Cache are flushed (a 1 GiB write) before every step, outside the
+timed events.  The headline value is decode KV-read GB/s; the same line also
+carries the causal prefill (TFLOP/s), the Qwen3-235B-shaped decode and the
+mixed batch, each against its own roofline, plus the fp64 CPU oracle timed on
+the host cores (a baseline, not a target).
+
+Modes used to make the committed profiles:
+    --profile-run            decode + prefill only, no oracle (run under rocprofv3)
+    --summarize DIR NAME     turn rocprofv3 output under DIR into profiles/NAME.txt
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, TFLOP/s (256 CU x 2.4 GHz x 4096)
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "decode_split_bf16_gptoss_decode_traffic.txt")
+DECODE_SOURCES = ["gqa_paged_attention_amd/csrc/decode.hip", "gqa_paged_attention_amd/csrc/common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------ algorithmic work
+
+def decode_bytes(batch) -> int:
+    """Bytes a decode pass must move: K and V of every visible token, q, out,
+    the used page-table entries, seq_lens and sinks."""
+    elem = 4 if batch.dtype == "f32" else 2
+    L = batch.seq_lens.to("cpu").long()
+    kv = int(L.sum()) * batch.num_kv_heads * batch.head_dim * 2 * elem
+    qo = 2 * batch.num_seqs * batch.num_q_heads * batch.head_dim * elem
+    table = int(((L + 15) // 16).sum()) * 4
+    return kv + qo + table + 4 * batch.num_seqs + 4 * batch.num_q_heads
+
+
+def prefill_flops(batch) -> int:
+    """4 * d * Hq per visible (query, key) pair (QK^T and PV, 2 flops per MAC)."""
+    L = batch.seq_lens.to("cpu").long()
+    Lq = batch.q_lens.to("cpu").long()
+    pairs = int((Lq * (L - Lq) + Lq * (Lq + 1) // 2).sum())
+    return 4 * batch.head_dim * batch.num_q_heads * pairs
+
+
+# ------------------------------------------------------------------ timing
+
+class Timer:
+    """Per-stage HIP-event timing of a list of launches on the current stream."""
+
+    def __init__(self, torch, flush_buf):
+        self.torch = torch
+        self.flush_buf = flush_buf
+
+    def run(self, stages, steps, warmup, flush=True):
+        torch = self.torch
+        n = len(stages)
+        for _ in range(warmup):
+            if flush:
+                self.flush_buf.fill_(1)
+            for _, fn in stages:
+                fn()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+                  for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            if flush:
+                self.flush_buf.fill_(k & 0xff)
+            ev = events[k]
+            ev[0].record()
+            for i, (_, fn) in enumerate(stages):
+                fn()
+                ev[i + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per_stage = {name: [events[k][i].elapsed_time(events[k][i + 1]) for k in range(steps)]
+                     for i, (name, _) in enumerate(stages)}
+        total = [events[k][0].elapsed_time(events[k][n]) for k in range(steps)]
+        return {"stage_ms": {k: sum(v) / len(v) for k, v in per_stage.items()},
+                "stage_ms_min": {k: min(v) for k, v in per_stage.items()},
+                "step_ms": sum(total) / len(total),
+                "step_ms_median": sorted(total)[len(total) // 2],
+                "wall_s": wall}
+
+
+# --------------------------------------------------------------- workloads
+
+def decode_stages(ga, g, out, ws):
+    msl = g.max_seq_len
+    return [
+        ("decode_split", lambda: ga.attn_sinks_decode_partials(
+            g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.scale, ws, msl)),
+        ("decode_merge", lambda: ga.attn_sinks_decode_merge(
+            g.seq_lens, g.sinks, ws, out, g.num_kv_heads, msl)),
+    ]
+
+
+def decode_workspace(torch, ga, g):
+    n = ga.attn_sinks_decode_workspace_bytes(g.num_seqs, g.num_q_heads, g.num_kv_heads,
+                                             g.head_dim, g.max_seq_len)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
+
+
+def bench_decode(torch, ga, timer, batch_cpu, steps, warmup, label):
+    g = batch_cpu.to("cuda")
+    out = torch.empty_like(g.q)
+    ws = decode_workspace(torch, ga, g)
+    nbytes = decode_bytes(batch_cpu)
+    cold = timer.run(decode_stages(ga, g, out, ws), steps, warmup, flush=True)
+    warm = timer.run(decode_stages(ga, g, out, ws), steps, warmup, flush=False)
+    gbs = nbytes / (cold["step_ms"] * 1e-3) / 1e9
+    split_gbs = nbytes / (cold["stage_ms"]["decode_split"] * 1e-3) / 1e9
+    res = {
+        "workload": label,
+        "algorithmic_bytes": nbytes,
+        "ms": round(cold["step_ms"], 4),
+        "GB_per_s": round(gbs, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "split_ms": round(cold["stage_ms"]["decode_split"], 4),
+        "merge_ms": round(cold["stage_ms"]["decode_merge"], 4),
+        "split_GB_per_s": round(split_gbs, 1),
+        "warm_GB_per_s": round(nbytes / (warm["step_ms"] * 1e-3) / 1e9, 1),
+    }
+    return res, out, (g, ws)
+
+
+def bench_prefill(torch, ga, timer, batch_cpu, steps, warmup, label):
+    g = batch_cpu.to("cuda")
+    out = torch.empty_like(g.q)
+    mq, ms = batch_cpu.max_q_len, batch_cpu.max_seq_len
+    stage = [("prefill", lambda: ga.attn_sinks_prefill(
+        g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.cu_seqlens_q, g.sinks, g.scale,
+        out, mq, ms))]
+    r = timer.run(stage, steps, warmup, flush=True)
+    flops = prefill_flops(batch_cpu)
+    tf = flops / (r["step_ms"] * 1e-3) / 1e12
+    return {"workload": label, "algorithmic_flops": flops, "ms": round(r["step_ms"], 4),
+            "TFLOP_per_s": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}, out
+
+
+def bench_mixed(torch, ga, timer, steps, warmup, wl):
+    full, dec, pre = wl.mixed(0)
+    gd, gp = dec.to("cuda"), pre.to("cuda")
+    out_d, out_p = torch.empty_like(gd.q), torch.empty_like(gp.q)
+    ws = decode_workspace(torch, ga, gd)
+    stages = decode_stages(ga, gd, out_d, ws) + [("prefill", lambda: ga.attn_sinks_prefill(
+        gp.q, gp.k_cache, gp.v_cache, gp.block_table, gp.seq_lens, gp.cu_seqlens_q, gp.sinks,
+        gp.scale, out_p, pre.max_q_len, pre.max_seq_len))]
+    r = timer.run(stages, steps, warmup, flush=True)
+    nb, fl = decode_bytes(dec), prefill_flops(pre)
+    dec_ms = r["stage_ms"]["decode_split"] + r["stage_ms"]["decode_merge"]
+    bound_ms = (nb / (HBM_PEAK_GBS * 1e9) + fl / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    return {"workload": "mixed: 32 decode seqs (ctx U[2048,16384]) + 2 prefill chunks of 2048 "
+                        "on 8192-token prefixes, 64/8 heads, d=64, bf16, sinks N(0,2)",
+            "ms": round(r["step_ms"], 4),
+            "decode_ms": round(dec_ms, 4),
+            "decode_GB_per_s": round(nb / (dec_ms * 1e-3) / 1e9, 1),
+            "prefill_ms": round(r["stage_ms"]["prefill"], 4),
+            "prefill_TFLOP_per_s": round(fl / (r["stage_ms"]["prefill"] * 1e-3) / 1e12, 1),
+            "serial_bound_ms": round(bound_ms, 4),
+            "frac_of_serial_bound": round(bound_ms / r["step_ms"], 4)}
+
+
+# ------------------------------------------------------------ cpu baseline
+
+def cpu_baseline(batch_cpu, gpu_out, sample_seqs):
+    """The fp64 oracle on the first `sample_seqs` sequences of the decode
+    workload, timed on this host's cores; the GPU output is checked on the
+    same rows (the correctness gate before the timings are reported)."""
+    import numpy as np
+    import oracle
+    sub = batch_cpu.rows(0, sample_seqs)
+    threads = oracle.default_threads()
+    oracle.attention(sub.rows(0, 1), threads=threads)  # load + warm
+    t0 = time.perf_counter()
+    ref = oracle.attention(sub, threads=threads)
+    dt = time.perf_counter() - t0
+    got = gpu_out[:sample_seqs].double().cpu().numpy()
+    err = np.abs(got - ref)
+    ok = bool(np.all(np.isfinite(got)) and np.all(err <= 1e-2 + 2e-2 * np.abs(ref)))
+    nbytes = decode_bytes(sub)
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {sample_seqs} of 64 sequences of the gpt-oss decode workload "
+                      f"({nbytes / 1e6:.1f} MB of K/V), all 64 heads, fp64, {dt:.2f} s",
+            "seconds": round(dt, 3),
+            "gpu_matches_oracle": ok, "gpu_max_abs_err": float(err.max())}
+
+
+def read_traffic():
+    """HBM traffic per split-pass launch from the committed counter summary,
+    or None when the summary is missing or the kernel changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != source_hash(DECODE_SOURCES):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------- profile summarising
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize(outdir: str, name: str, command: str):
+    """Write profiles/<name>.txt from rocprofv3 CSV output found under outdir."""
+    lines = [f"# rocprofv3 summary: {name}", f"command: {command}"]
+    stats = glob.glob(os.path.join(outdir, "**", "*kernel_stats.csv"), recursive=True)
+    for path in stats:
+        rows = _read_csv(path)
+        lines.append("")
+        lines.append("kernel | calls | avg_us | min_us | max_us | total_ms | pct")
+        for r in rows:
+            nm = r.get("Name", "")
+            short = nm.split("(")[0][-90:]
+            lines.append(f"{short} | {r.get('Calls')} | "
+                         f"{float(r.get('AverageNs', 0)) / 1e3:.2f} | "
+                         f"{float(r.get('MinNs', 0)) / 1e3:.2f} | "
+                         f"{float(r.get('MaxNs', 0)) / 1e3:.2f} | "
+                         f"{float(r.get('TotalDurationNs', 0)) / 1e6:.3f} | "
+                         f"{float(r.get('Percentage', 0)):.2f}")
+    counters = glob.glob(os.path.join(outdir, "**", "*counter_collection.csv"), recursive=True)
+    for path in counters:
+        rows = _read_csv(path)
+        agg = {}
+        for r in rows:
+            kn = r.get("Kernel_Name", "").split("(")[0][-90:]
+            cn = r.get("Counter_Name", "")
+            agg.setdefault((kn, cn), []).append(float(r.get("Counter_Value", 0)))
+        lines.append("")
+        lines.append("kernel | counter | dispatches | mean_per_dispatch")
+        for (kn, cn), vals in sorted(agg.items()):
+            lines.append(f"{kn} | {cn} | {len(vals)} | {sum(vals) / len(vals):.1f}")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, name + ".txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# -------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["decode", "all"], default="all")
+    ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--summarize", nargs=2, metavar=("DIR", "NAME"))
+    ap.add_argument("--command", default="", help="command line recorded by --summarize")
+    args = ap.parse_args()
+
+    if args.summarize:
+        summarize(args.summarize[0], args.summarize[1], args.command)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library's path runs on a single MI355X "
+              "and has no multi-GPU mode; run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import gqa_paged_attention_amd as ga
+    from gqa_paged_attention_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 2
+    ga.library()
+    torch.cuda.set_device(0)
+    flush_buf = torch.empty(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB
+    timer = Timer(torch, flush_buf)
+    K, W = args.steps, args.warmup
+
+    log("generating gpt-oss decode workload")
+    dec = wl.gptoss_decode(0)
+    label = ("gpt-oss-20b-shaped decode, bf16: 64 seqs x 1 token, 64 q / 8 KV heads, "
+             "head_dim 64, ctx U[1024,8192], 16-token HND pages, random page table, "
+             "q/k/v/sinks N(0,1), seed 0")
+    log("timing decode")
+    d_res, d_out, _ = bench_decode(torch, ga, timer, dec, K, W, label)
+    log(json.dumps(d_res))
+
+    extra = {}
+    if args.only == "all" or args.profile_run:
+        log("generating gpt-oss prefill workload")
+        pre = wl.gptoss_prefill(0)
+        p_res, _ = bench_prefill(torch, ga, timer, pre, K, W,
+                                 "gpt-oss-shaped causal prefill, bf16: 8 seqs x 4096 tokens, "
+                                 "64 q / 8 KV heads, head_dim 64, sinks N(0,1), seed 0")
+        log(json.dumps(p_res))
+        extra["prefill"] = p_res
+    if args.only == "all" and not args.profile_run:
+        log("generating mixed workload")
+        extra["mixed"] = bench_mixed(torch, ga, timer, K, W, wl)
+        log(json.dumps(extra["mixed"]))
+        log("generating qwen decode workload (about a minute)")
+        qw = wl.qwen_decode(0)
+        q_res, _, keep = bench_decode(torch, ga, timer, qw, max(K // 2, 3), max(W // 2, 1),
+                                      "Qwen3-235B-shaped decode, bf16: 128 seqs x 1 token, "
+                                      "64 q / 4 KV heads, head_dim 128, ctx U[4096,32768], "
+                                      "sinks -inf, seed 0")
+        del keep, qw
+        extra["qwen_decode"] = q_res
+        log(json.dumps(q_res))
+
+    if args.profile_run:
+        # a plain 1 GiB device copy: its FETCH_SIZE / WRITE_SIZE counters give
+        # the factor between counter units and bytes
+        src = torch.empty(1 << 28, dtype=torch.int32, device="cuda").fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(json.dumps({"profile_run": True, "decode": d_res, **extra,
+                        "copy_calibration_bytes": src.numel() * 4}))
+        return 0
+
+    log("cpu baseline: oracle on the host cores")
+    cpu = cpu_baseline(dec, d_out.cpu(), sample_seqs=64)
+    log(json.dumps(cpu))
+    if not cpu["gpu_matches_oracle"]:
+        print("GPU decode output does not match the oracle; refusing to report", file=sys.stderr)
+        return 1
+
+    traffic = read_traffic()
+    split_launch_bytes = d_res["algorithmic_bytes"]
+    achieved = d_res["split_GB_per_s"]
+    line = {
+        "metric": "decode KV-read GB/s (% HBM peak); prefill attention TFLOPS (% MFMA peak)",
+        "value": d_res["GB_per_s"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": d_res["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": label, "parallelism": "single GPU",
+                   "hbm_frac": d_res["hbm_frac"], "warm_GB_per_s": d_res["warm_GB_per_s"],
+                   "split_ms": d_res["split_ms"], "merge_ms": d_res["merge_ms"]},
+        "roofline": {"bound": "hbm", "kernel": "decode_split_bf16<64>",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": split_launch_bytes},
+        "cpu_baseline": {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
+        **extra,
+    }
+    if "prefill" in extra:
+        p = extra["prefill"]
+        line["prefill_roofline"] = {"bound": "mfma", "kernel": "prefill_bf16<64>",
+                                    "achieved": p["TFLOP_per_s"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": p["mfma_frac"], "traffic": None}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

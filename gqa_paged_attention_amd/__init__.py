@@ -49,6 +49,10 @@ def library():
     lib.attn_sinks_decode_workspace_bytes.restype = Z
     lib.attn_sinks_decode.argtypes = [I] * 9 + [P] * 6 + [F, P, P, Z, P]
     lib.attn_sinks_decode.restype = I
+    lib.attn_sinks_decode_partials.argtypes = [I] * 9 + [P] * 5 + [F, P, Z, P]
+    lib.attn_sinks_decode_partials.restype = I
+    lib.attn_sinks_decode_merge.argtypes = [I] * 6 + [P, P, P, Z, P, P]
+    lib.attn_sinks_decode_merge.restype = I
     lib.attn_sinks_prefill.argtypes = [I] * 11 + [P] * 7 + [F, P, P]
     lib.attn_sinks_prefill.restype = I
     lib.attn_sinks_status_string.argtypes = [I]
@@ -131,6 +135,47 @@ def attn_sinks_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(sinks),
         ctypes.c_float(scale), _ptr(out), _ptr(workspace), ctypes.c_size_t(ws_bytes),
         _stream_handle(stream))
+    _raise(status)
+
+
+def attn_sinks_decode_partials(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                               block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                               workspace: torch.Tensor, max_seq_len: int, stream=None) -> None:
+    """Enqueue the split pass of decode (bf16): partial results into workspace."""
+    dt = _DTYPE_CODE.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_dense(name, t, q.dtype)
+    _check_dense("block_table", block_table, torch.int32)
+    _check_dense("seq_lens", seq_lens, torch.int32)
+    _check_dense("workspace", workspace)
+    B, Hq, d = q.shape
+    num_pages, Hkv, P, _ = k_cache.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    status = library().attn_sinks_decode_partials(
+        dt, B, Hq, Hkv, d, P, num_pages, block_table.shape[1], int(max_seq_len),
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+        ctypes.c_float(scale), _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream))
+    _raise(status)
+
+
+def attn_sinks_decode_merge(seq_lens: torch.Tensor, sinks: Optional[torch.Tensor],
+                            workspace: torch.Tensor, out: torch.Tensor, num_kv_heads: int,
+                            max_seq_len: int, stream=None) -> None:
+    """Enqueue the merge pass of decode: splits + sink -> out [B][Hq][d]."""
+    dt = _DTYPE_CODE.get(out.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {out.dtype}")
+    _check_dense("out", out)
+    _check_dense("seq_lens", seq_lens, torch.int32)
+    _check_dense("sinks", sinks, torch.float32)
+    _check_dense("workspace", workspace)
+    B, Hq, d = out.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    status = library().attn_sinks_decode_merge(
+        dt, B, Hq, int(num_kv_heads), d, int(max_seq_len), _ptr(seq_lens), _ptr(sinks),
+        _ptr(workspace), ctypes.c_size_t(ws_bytes), _ptr(out), _stream_handle(stream))
     _raise(status)
 
 

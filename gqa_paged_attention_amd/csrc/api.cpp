@@ -99,6 +99,66 @@ size_t decode_workspace(int num_seqs, int num_q_heads, int num_kv_heads, int hea
            sizeof(float);
 }
 
+// Checks shared by the decode entry points; fills the launch description.
+// `reads_kv`: the call reads q and the page pool; `writes_out`: it writes out.
+int prepare_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                   int page_size, int num_pages, int max_pages_per_seq, int max_seq_len,
+                   const void *q, const void *k_cache, const void *v_cache,
+                   const int32_t *block_table, const int32_t *seq_lens, const float *sinks,
+                   float scale, void *out, void *workspace, size_t workspace_bytes,
+                   void *stream, bool reads_kv, bool writes_out, attn::DecodeLaunch *p)
+{
+    int rc = check_common(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                          num_pages, max_pages_per_seq, max_seq_len);
+    if (rc != ATTN_OK)
+        return rc;
+    if (!std::isfinite(scale))
+        return ATTN_ERR_SHAPE;
+    if (num_seqs == 0)
+        return ATTN_OK;
+    if (!seq_lens || (writes_out && !out))
+        return ATTN_ERR_NULL;
+    if (reads_kv && (!q || (max_seq_len > 0 && (!k_cache || !v_cache || !block_table))))
+        return ATTN_ERR_NULL;
+    const void *vec[] = {q, k_cache, v_cache, out, workspace};
+    for (const void *ptr : vec)
+        if (ptr && !aligned16(ptr))
+            return ATTN_ERR_ALIGN;
+    const void *words[] = {block_table, seq_lens, sinks};
+    for (const void *ptr : words)
+        if (ptr && !aligned4(ptr))
+            return ATTN_ERR_ALIGN;
+    int splits = 0, split_tokens = 0;
+    const size_t need = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         max_seq_len, &splits, &split_tokens);
+    // the fp32 path of attn_sinks_decode works on full rows and needs no scratch
+    const bool uses_workspace = !(dtype == ATTN_DTYPE_F32 && reads_kv && writes_out);
+    if (uses_workspace && need > 0 && (!workspace || workspace_bytes < need))
+        return workspace ? ATTN_ERR_WORKSPACE : ATTN_ERR_NULL;
+    p->dtype = dtype;
+    p->num_seqs = num_seqs;
+    p->num_q_heads = num_q_heads;
+    p->num_kv_heads = num_kv_heads;
+    p->head_dim = head_dim;
+    p->max_pages_per_seq = max_pages_per_seq;
+    p->max_splits = splits;
+    p->split_tokens = split_tokens;
+    p->q = q;
+    p->k_cache = k_cache;
+    p->v_cache = v_cache;
+    p->block_table = block_table;
+    p->seq_lens = seq_lens;
+    p->sinks = sinks;
+    p->scale = scale;
+    p->out = out;
+    float *ws = static_cast<float *>(workspace);
+    const size_t rows = (size_t)num_seqs * splits * num_q_heads;
+    p->part_ml = ws;
+    p->part_acc = ws ? ws + rows * 2 : nullptr;
+    p->stream = reinterpret_cast<hipStream_t>(stream);
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -121,62 +181,59 @@ int attn_sinks_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads
                       float scale, void *out, void *workspace, size_t workspace_bytes,
                       void *stream)
 {
-    int rc = check_common(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
-                          num_pages, max_pages_per_seq, max_seq_len);
-    if (rc != ATTN_OK)
+    attn::DecodeLaunch p;
+    int rc = prepare_decode(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                            num_pages, max_pages_per_seq, max_seq_len, q, k_cache, v_cache,
+                            block_table, seq_lens, sinks, scale, out, workspace, workspace_bytes,
+                            stream, true, true, &p);
+    if (rc != ATTN_OK || num_seqs == 0)
         return rc;
-    if (!std::isfinite(scale))
-        return ATTN_ERR_SHAPE;
-    if (num_seqs == 0)
-        return ATTN_OK;
-    if (!q || !out || !seq_lens || (max_seq_len > 0 && (!k_cache || !v_cache || !block_table)))
-        return ATTN_ERR_NULL;
-    const void *vec[] = {q, k_cache, v_cache, out, workspace};
-    for (const void *p : vec)
-        if (p && !aligned16(p))
-            return ATTN_ERR_ALIGN;
-    const void *words[] = {block_table, seq_lens, sinks};
-    for (const void *p : words)
-        if (p && !aligned4(p))
-            return ATTN_ERR_ALIGN;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-
     if (dtype == ATTN_DTYPE_F32) {
         hipError_t e = attn::launch_rows_f32(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                              max_pages_per_seq, num_seqs, q, k_cache, v_cache,
                                              block_table, seq_lens, nullptr, sinks, scale, out,
-                                             s);
+                                             p.stream);
         return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
     }
+    if (attn::launch_decode_split_bf16(p) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return attn::launch_decode_merge(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
 
-    int splits = 0, split_tokens = 0;
-    const size_t need = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                         max_seq_len, &splits, &split_tokens);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return workspace ? ATTN_ERR_WORKSPACE : ATTN_ERR_NULL;
+int attn_sinks_decode_partials(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                               int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                               int max_seq_len, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *block_table,
+                               const int32_t *seq_lens, float scale, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    if (dtype != ATTN_DTYPE_BF16)
+        return ATTN_ERR_UNSUPPORTED;
     attn::DecodeLaunch p;
-    p.dtype = dtype;
-    p.num_seqs = num_seqs;
-    p.num_q_heads = num_q_heads;
-    p.num_kv_heads = num_kv_heads;
-    p.head_dim = head_dim;
-    p.max_pages_per_seq = max_pages_per_seq;
-    p.max_splits = splits;
-    p.split_tokens = split_tokens;
-    p.q = q;
-    p.k_cache = k_cache;
-    p.v_cache = v_cache;
-    p.block_table = block_table;
-    p.seq_lens = seq_lens;
-    p.sinks = sinks;
-    p.scale = scale;
-    p.out = out;
-    float *ws = static_cast<float *>(workspace);
-    const size_t rows = (size_t)num_seqs * splits * num_q_heads;
-    p.part_ml = ws;
-    p.part_acc = ws ? ws + rows * 2 : nullptr;
-    p.stream = s;
-    return attn::launch_decode_bf16(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    int rc = prepare_decode(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                            num_pages, max_pages_per_seq, max_seq_len, q, k_cache, v_cache,
+                            block_table, seq_lens, nullptr, scale, nullptr, workspace,
+                            workspace_bytes, stream, true, false, &p);
+    if (rc != ATTN_OK || num_seqs == 0)
+        return rc;
+    return attn::launch_decode_split_bf16(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_sinks_decode_merge(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                            int head_dim, int max_seq_len, const int32_t *seq_lens,
+                            const float *sinks, const void *workspace, size_t workspace_bytes,
+                            void *out, void *stream)
+{
+    attn::DecodeLaunch p;
+    // the merge reads no KV data: give the page-related checks neutral values
+    const int pages = (max_seq_len + kPageSize - 1) / kPageSize;
+    int rc = prepare_decode(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, kPageSize,
+                            pages > 0 ? pages : 1, pages, max_seq_len, nullptr, nullptr, nullptr,
+                            nullptr, seq_lens, sinks, 1.0f, out, const_cast<void *>(workspace),
+                            workspace_bytes, stream, false, true, &p);
+    if (rc != ATTN_OK || num_seqs == 0)
+        return rc;
+    return attn::launch_decode_merge(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_sinks_prefill(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

@@ -324,7 +324,7 @@ __global__ __launch_bounds__(64) void decode_merge(MergeArgs a)
 }
 
 template <int D>
-hipError_t launch_decode_d(const DecodeLaunch &p)
+hipError_t launch_split_d(const DecodeLaunch &p)
 {
     SplitArgs a;
     a.q = (const uint16_t *)p.q;
@@ -342,13 +342,14 @@ hipError_t launch_decode_d(const DecodeLaunch &p)
     a.split_tokens = p.split_tokens;
     a.wave_tokens = p.split_tokens / kDecodeWaves;
     a.scale_log2 = p.scale * kLog2e;
-    if (p.max_splits > 0) {
-        dim3 grid(p.max_splits, p.num_kv_heads, p.num_seqs);
-        hipLaunchKernelGGL(decode_split_bf16<D>, grid, dim3(64 * kDecodeWaves), 0, p.stream, a);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess)
-            return err;
-    }
+    dim3 grid(p.max_splits, p.num_kv_heads, p.num_seqs);
+    hipLaunchKernelGGL(decode_split_bf16<D>, grid, dim3(64 * kDecodeWaves), 0, p.stream, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_merge_d(const DecodeLaunch &p)
+{
     MergeArgs m;
     m.part_ml = p.part_ml;
     m.part_acc = p.part_acc;
@@ -358,18 +359,28 @@ hipError_t launch_decode_d(const DecodeLaunch &p)
     m.num_q_heads = p.num_q_heads;
     m.max_splits = p.max_splits;
     m.split_tokens = p.split_tokens;
-    hipLaunchKernelGGL((decode_merge<D, true>), dim3(p.num_q_heads, p.num_seqs), dim3(64), 0,
-                       p.stream, m);
+    const dim3 grid(p.num_q_heads, p.num_seqs);
+    if (p.dtype == 1)
+        hipLaunchKernelGGL((decode_merge<D, true>), grid, dim3(64), 0, p.stream, m);
+    else
+        hipLaunchKernelGGL((decode_merge<D, false>), grid, dim3(64), 0, p.stream, m);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeLaunch &p)
+hipError_t launch_decode_split_bf16(const DecodeLaunch &p)
+{
+    if (p.num_seqs == 0 || p.max_splits == 0)
+        return hipSuccess;
+    return p.head_dim == 64 ? launch_split_d<64>(p) : launch_split_d<128>(p);
+}
+
+hipError_t launch_decode_merge(const DecodeLaunch &p)
 {
     if (p.num_seqs == 0)
         return hipSuccess;
-    return p.head_dim == 64 ? launch_decode_d<64>(p) : launch_decode_d<128>(p);
+    return p.head_dim == 64 ? launch_merge_d<64>(p) : launch_merge_d<128>(p);
 }
 
 }  // namespace attn

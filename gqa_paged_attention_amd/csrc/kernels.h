@@ -38,7 +38,11 @@ struct PrefillLaunch {
 // consecutive tokens of the split.
 constexpr int kDecodeWaves = 4;
 
-hipError_t launch_decode_bf16(const DecodeLaunch &p);
+// Split pass: partial (max, sum, weighted values) per split into the workspace.
+hipError_t launch_decode_split_bf16(const DecodeLaunch &p);
+// Merge pass: combine the splits of each (sequence, head), fold the sink,
+// write out in p.dtype.
+hipError_t launch_decode_merge(const DecodeLaunch &p);
 hipError_t launch_prefill_bf16(const PrefillLaunch &p);
 // fp32 path (full rows, no split), used for both decode and prefill.
 hipError_t launch_rows_f32(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

@@ -123,6 +123,49 @@ int attn_sinks_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads
                       void *stream);
 
 /*
+ * The two passes of attn_sinks_decode, callable on their own (bf16 only for
+ * the first pass).  attn_sinks_decode is exactly partials followed by merge
+ * on the same stream with the same sizes.  Running them separately lets a
+ * caller time or overlap the passes, or combine partial results computed
+ * elsewhere (for example over a KV range held by another device), since the
+ * merge reads nothing but the workspace.
+ *
+ * Workspace layout for S = splits = ceil(max_seq_len / C), where C depends
+ * only on (num_seqs, num_kv_heads, max_seq_len) and the byte count is given
+ * by attn_sinks_decode_workspace_bytes:
+ *   float ml [num_seqs][S][num_q_heads][2]    running max in base-2 units
+ *                                             (scale * q.k * log2(e)), sum
+ *                                             of 2^(s_j - max) over the split
+ *   float acc[num_seqs][S][num_q_heads][head_dim]
+ *                                             sum of 2^(s_j - max) * V[j]
+ * Only splits s < ceil(L_b / C) of sequence b are written and read.  A split
+ * with no key has max = -inf, sum = 0 and acc = 0.
+ *
+ * attn_sinks_decode_partials -- the split pass (dtype must be
+ * ATTN_DTYPE_BF16); arguments as for attn_sinks_decode.  No sink is involved.
+ */
+int attn_sinks_decode_partials(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                               int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                               int max_seq_len, const void *q, const void *k_cache,
+                               const void *v_cache, const int32_t *block_table,
+                               const int32_t *seq_lens, float scale, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
+ * attn_sinks_decode_merge -- the merge pass: for each (sequence, head)
+ * combine the splits' partial results with the sink, counted once
+ * ("GPT-OSS on day 0", section "Sink Attention"):
+ *   M = max(max_s m_s, sink * log2(e))
+ *   out = sum_s acc_s 2^(m_s - M) / (sum_s l_s 2^(m_s - M) + 2^(sink*log2(e) - M))
+ * and write out [num_seqs][num_q_heads][head_dim] in dtype (f32 or bf16).
+ * The workspace is read only.
+ */
+int attn_sinks_decode_merge(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                            int head_dim, int max_seq_len, const int32_t *seq_lens,
+                            const float *sinks, const void *workspace, size_t workspace_bytes,
+                            void *out, void *stream);
+
+/*
  * attn_sinks_prefill -- ragged batch of query chunks with causal masking
  * (model notes section 3: causal mask before the sink softmax).  The chunk of
  * sequence b is query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and sits at

@@ -166,6 +166,24 @@ def test_prefill_rows_match_decode():
         compare(pre[i:i + 1], dec.double().numpy(), "bf16", f"row {i} prefill vs decode")
 
 
+def test_stage_entry_points_equal_decode():
+    """attn_sinks_decode == attn_sinks_decode_partials + attn_sinks_decode_merge."""
+    b = wl.small_batch(98, "bf16", [5000, 1, 700], [1, 1, 1], 16, 2, 128).to("cuda")
+    note("decode stages vs one-call decode")
+    ref = ga.decode_batch(b)
+    nbytes = ga.attn_sinks_decode_workspace_bytes(3, 16, 2, 128, b.max_seq_len)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(b.q)
+    ga.attn_sinks_decode_partials(b.q, b.k_cache, b.v_cache, b.block_table, b.seq_lens, b.scale,
+                                  ws, b.max_seq_len)
+    ga.attn_sinks_decode_merge(b.seq_lens, b.sinks, ws, out, b.num_kv_heads, b.max_seq_len)
+    out32 = torch.empty(out.shape, dtype=torch.float32, device="cuda")
+    ga.attn_sinks_decode_merge(b.seq_lens, b.sinks, ws, out32, b.num_kv_heads, b.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(out32.to(torch.bfloat16).view(torch.int16), ref.view(torch.int16))
+
+
 def test_empty_sequences_give_zero():
     b = wl.small_batch(95, "bf16", [1, 40], [1, 1], 8, 2, 64)
     b = replace(b, seq_lens=torch.tensor([0, 40], dtype=torch.int32))
