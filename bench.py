@@ -15,7 +15,9 @@ the host cores (a baseline, not a target).
 
 Modes used to make the committed profiles:
     --profile-run            decode + prefill only, no oracle (run under rocprofv3)
-    --summarize DIR NAME     turn rocprofv3 output under DIR into profiles/NAME.txt
+    --summarize-trace DIR NAME              kernel durations -> profiles/NAME.txt
+    --summarize-traffic FDIR WDIR KERNEL NAME
+                                            FETCH/WRITE_SIZE -> HBM bytes per launch
 """
 from __future__ import annotations
 
@@ -132,13 +134,14 @@ def decode_workspace(torch, ga, g):
     return torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
 
 
-def bench_decode(torch, ga, timer, batch_cpu, steps, warmup, label):
+def bench_decode(torch, ga, timer, batch_cpu, steps, warmup, label, with_warm=True):
     g = batch_cpu.to("cuda")
     out = torch.empty_like(g.q)
     ws = decode_workspace(torch, ga, g)
     nbytes = decode_bytes(batch_cpu)
     cold = timer.run(decode_stages(ga, g, out, ws), steps, warmup, flush=True)
-    warm = timer.run(decode_stages(ga, g, out, ws), steps, warmup, flush=False)
+    warm = timer.run(decode_stages(ga, g, out, ws), steps, warmup, flush=False) if with_warm \
+        else cold
     gbs = nbytes / (cold["step_ms"] * 1e-3) / 1e9
     split_gbs = nbytes / (cold["stage_ms"]["decode_split"] * 1e-3) / 1e9
     res = {
@@ -244,35 +247,66 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
-def summarize(outdir: str, name: str, command: str):
-    """Write profiles/<name>.txt from rocprofv3 CSV output found under outdir."""
-    lines = [f"# rocprofv3 summary: {name}", f"command: {command}"]
-    stats = glob.glob(os.path.join(outdir, "**", "*kernel_stats.csv"), recursive=True)
-    for path in stats:
-        rows = _read_csv(path)
-        lines.append("")
-        lines.append("kernel | calls | avg_us | min_us | max_us | total_ms | pct")
-        for r in rows:
-            nm = r.get("Name", "")
-            short = nm.split("(")[0][-90:]
-            lines.append(f"{short} | {r.get('Calls')} | "
-                         f"{float(r.get('AverageNs', 0)) / 1e3:.2f} | "
-                         f"{float(r.get('MinNs', 0)) / 1e3:.2f} | "
-                         f"{float(r.get('MaxNs', 0)) / 1e3:.2f} | "
-                         f"{float(r.get('TotalDurationNs', 0)) / 1e6:.3f} | "
-                         f"{float(r.get('Percentage', 0)):.2f}")
-    counters = glob.glob(os.path.join(outdir, "**", "*counter_collection.csv"), recursive=True)
-    for path in counters:
-        rows = _read_csv(path)
-        agg = {}
-        for r in rows:
-            kn = r.get("Kernel_Name", "").split("(")[0][-90:]
-            cn = r.get("Counter_Name", "")
-            agg.setdefault((kn, cn), []).append(float(r.get("Counter_Value", 0)))
-        lines.append("")
-        lines.append("kernel | counter | dispatches | mean_per_dispatch")
-        for (kn, cn), vals in sorted(agg.items()):
-            lines.append(f"{kn} | {cn} | {len(vals)} | {sum(vals) / len(vals):.1f}")
+def _short(name: str) -> str:
+    import re
+    name = name.replace("(anonymous namespace)::", "")
+    name = re.sub(r"^void ", "", name)
+    return re.sub(r"\(.*$", "", name)[:80]
+
+
+def _find(outdir, suffix):
+    hits = glob.glob(os.path.join(outdir, "**", "*" + suffix), recursive=True)
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {outdir}")
+    return hits[0]
+
+
+def summarize_trace(outdir: str, name: str, command: str):
+    """profiles/<name>.txt: per-kernel durations from a --kernel-trace --stats run."""
+    rows = _read_csv(_find(outdir, "kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel-trace summary: {name}", f"command: {command}", "",
+             "kernel | calls | avg_us | min_us | max_us | total_ms | pct"]
+    for r in rows:
+        lines.append(f"{_short(r['Name'])} | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}")
+    _write_profile(name, lines)
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, kernel: str, name: str, command: str):
+    """profiles/<name>.txt: HBM bytes per launch of `kernel` from one FETCH_SIZE
+    and one WRITE_SIZE run, each scaled by what the counter reads for the
+    1 GiB device copy made by --profile-run."""
+    calib = 1 << 30
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _read_csv(_find(d, "counter_collection.csv"))
+                if r["Counter_Name"] == counter]
+        copy = max((float(r["Counter_Value"]) for r in rows
+                    if "copyBuffer" in r["Kernel_Name"]), default=0.0)
+        vals = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"]]
+        if not copy or not vals:
+            raise SystemExit(f"{counter}: copy or {kernel} dispatches missing")
+        factor = calib / (copy * 1024.0)
+        out[counter] = (sum(vals) / len(vals), len(vals), copy, factor)
+    fetch, write = out["FETCH_SIZE"], out["WRITE_SIZE"]
+    traffic = (fetch[0] * fetch[3] + write[0] * write[3]) * 1024.0
+    lines = [f"# rocprofv3 HBM traffic summary: {name}", f"command: {command}",
+             f"kernel: {kernel}",
+             f"kernel_source_sha256_16: {source_hash(DECODE_SOURCES)}",
+             f"copy_calibration_bytes: {calib}",
+             f"fetch_kib_copy: {fetch[2]:.1f}",
+             f"fetch_scale: {fetch[3]:.4f}",
+             f"write_kib_copy: {write[2]:.1f}",
+             f"write_scale: {write[3]:.4f}",
+             f"fetch_kib_per_dispatch: {fetch[0]:.1f}  ({fetch[1]} dispatches)",
+             f"write_kib_per_dispatch: {write[0]:.1f}  ({write[1]} dispatches)",
+             f"traffic_bytes_per_launch: {traffic:.0f}"]
+    _write_profile(name, lines)
+
+
+def _write_profile(name, lines):
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, name + ".txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -288,12 +322,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["decode", "all"], default="all")
     ap.add_argument("--profile-run", action="store_true")
-    ap.add_argument("--summarize", nargs=2, metavar=("DIR", "NAME"))
-    ap.add_argument("--command", default="", help="command line recorded by --summarize")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "NAME"))
+    ap.add_argument("--summarize-traffic", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "KERNEL", "NAME"))
+    ap.add_argument("--command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
 
-    if args.summarize:
-        summarize(args.summarize[0], args.summarize[1], args.command)
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.command)
+        return 0
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.command)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library's path runs on a single MI355X "
@@ -319,7 +358,8 @@ def main():
              "head_dim 64, ctx U[1024,8192], 16-token HND pages, random page table, "
              "q/k/v/sinks N(0,1), seed 0")
     log("timing decode")
-    d_res, d_out, _ = bench_decode(torch, ga, timer, dec, K, W, label)
+    d_res, d_out, _ = bench_decode(torch, ga, timer, dec, K, W, label,
+                                   with_warm=not args.profile_run)
     log(json.dumps(d_res))
 
     extra = {}
