@@ -22,40 +22,50 @@ bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
-// Debug override of the decode split length (tokens per workgroup), read once.
-// Must be a positive multiple of 32 * kDecodeWaves; anything else is ignored.
-int split_override()
+// Debug override of the number of split-pass workgroups per head group, read
+// once.  Must be positive; anything else is ignored.
+int wgs_override()
 {
     static int value = 0;
     static std::once_flag once;
     std::call_once(once, [] {
-        const char *s = std::getenv("ATTN_SINKS_SPLIT_TOKENS");
+        const char *s = std::getenv("ATTN_SINKS_DECODE_WGS");
         if (s) {
             long v = std::strtol(s, nullptr, 10);
-            if (v > 0 && v <= (1 << 20) && v % (32 * attn::kDecodeWaves) == 0)
+            if (v > 0 && v <= (1 << 20))
                 value = (int)v;
         }
     });
     return value;
 }
 
-// Tokens per decode split: the smallest power of two >= 128 for which the
-// grid upper bound (num_seqs * Hkv * ceil(max_seq_len / C)) stays within
-// 8192 workgroups.  Only host integers decide it, so the launch shape never
-// depends on device data and the call can be captured into a graph.
-int decode_split_tokens(int num_seqs, int num_kv_heads, int max_seq_len)
+struct DecodeShape {
+    int heads_per_wg;  // waves per workgroup, one KV head each
+    int wgs;           // workgroups per head group
+};
+
+// Launch shape of the decode split pass.  Every workgroup takes an equal
+// share of the 32-token units, so the count only needs to fill the chip once;
+// it is capped by an upper bound of the unit count computed from host
+// integers, so the launch never depends on device data and the call can be
+// captured into a graph.
+DecodeShape decode_shape(int num_seqs, int num_kv_heads, int max_seq_len)
 {
-    if (int o = split_override())
-        return o;
-    const long long pairs = (long long)num_seqs * num_kv_heads;
-    int c = 32 * attn::kDecodeWaves;
-    while (c < (1 << 20)) {
-        const long long splits = (max_seq_len + (long long)c - 1) / c;
-        if (pairs * splits <= 8192)
-            break;
-        c *= 2;
+    DecodeShape s;
+    s.heads_per_wg = num_kv_heads < attn::kDecodeMaxHeadsPerWg ? num_kv_heads
+                                                               : attn::kDecodeMaxHeadsPerWg;
+    const int groups = (num_kv_heads + s.heads_per_wg - 1) / s.heads_per_wg;
+    const long long units_max = (long long)num_seqs * ((max_seq_len + 31) / 32);
+    long long w = wgs_override();
+    if (!w) {
+        w = attn::kDecodeTargetWaves / ((long long)s.heads_per_wg * groups);
+        if (w < 1)
+            w = 1;
     }
-    return c;
+    if (units_max < w)
+        w = units_max;
+    s.wgs = (int)w;
+    return s;
 }
 
 int check_common(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
@@ -86,17 +96,24 @@ int check_common(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, int
     return ATTN_OK;
 }
 
+// Workspace: ml [slots][Hq][2] then, 16-byte aligned, acc [slots][Hq][d]
+// (fp32), with slots = num_seqs + workgroups per head group.
 size_t decode_workspace(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                        int max_seq_len, int *splits_out, int *split_tokens_out)
+                        int max_seq_len, DecodeShape *shape_out, size_t *acc_offset_floats)
 {
-    const int c = decode_split_tokens(num_seqs, num_kv_heads, max_seq_len);
-    const int splits = (int)(((long long)max_seq_len + c - 1) / c);
-    if (splits_out)
-        *splits_out = splits;
-    if (split_tokens_out)
-        *split_tokens_out = c;
-    return (size_t)num_seqs * (size_t)splits * (size_t)num_q_heads * (size_t)(head_dim + 2) *
-           sizeof(float);
+    const DecodeShape shape = decode_shape(num_seqs, num_kv_heads, max_seq_len);
+    if (shape_out)
+        *shape_out = shape;
+    if (shape.wgs == 0) {
+        if (acc_offset_floats)
+            *acc_offset_floats = 0;
+        return 0;
+    }
+    const size_t slots = (size_t)num_seqs + (size_t)shape.wgs;
+    const size_t ml = (slots * num_q_heads * 2 + 3) / 4 * 4;
+    if (acc_offset_floats)
+        *acc_offset_floats = ml;
+    return (ml + slots * num_q_heads * (size_t)head_dim) * sizeof(float);
 }
 
 // Checks shared by the decode entry points; fills the launch description.
@@ -128,9 +145,10 @@ int prepare_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, i
     for (const void *ptr : words)
         if (ptr && !aligned4(ptr))
             return ATTN_ERR_ALIGN;
-    int splits = 0, split_tokens = 0;
+    DecodeShape shape;
+    size_t acc_offset = 0;
     const size_t need = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                         max_seq_len, &splits, &split_tokens);
+                                         max_seq_len, &shape, &acc_offset);
     // the fp32 path of attn_sinks_decode works on full rows and needs no scratch
     const bool uses_workspace = !(dtype == ATTN_DTYPE_F32 && reads_kv && writes_out);
     if (uses_workspace && need > 0 && (!workspace || workspace_bytes < need))
@@ -141,8 +159,8 @@ int prepare_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, i
     p->num_kv_heads = num_kv_heads;
     p->head_dim = head_dim;
     p->max_pages_per_seq = max_pages_per_seq;
-    p->max_splits = splits;
-    p->split_tokens = split_tokens;
+    p->num_wgs = shape.wgs;
+    p->heads_per_wg = shape.heads_per_wg;
     p->q = q;
     p->k_cache = k_cache;
     p->v_cache = v_cache;
@@ -152,9 +170,8 @@ int prepare_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, i
     p->scale = scale;
     p->out = out;
     float *ws = static_cast<float *>(workspace);
-    const size_t rows = (size_t)num_seqs * splits * num_q_heads;
     p->part_ml = ws;
-    p->part_acc = ws ? ws + rows * 2 : nullptr;
+    p->part_acc = ws ? ws + acc_offset : nullptr;
     p->stream = reinterpret_cast<hipStream_t>(stream);
     return ATTN_OK;
 }

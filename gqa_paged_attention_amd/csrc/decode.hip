@@ -7,11 +7,19 @@
 // the first part, which is the same arithmetic (the merge rescales every part
 // to a common maximum that includes the sink).
 //
-// Work decomposition:
-//   grid (max_splits, Hkv, B), 4 waves per workgroup.  Workgroup (s, g, b)
-//   owns tokens [s*C, min((s+1)*C, L_b)) of sequence b and KV head g, and all
-//   G = Hq/Hkv query heads that read KV head g.  Wave w takes the w-th quarter
-//   of that range in blocks of 32 tokens (two 16-token HND page slabs).
+// Work decomposition (persistent, balanced):
+//   A unit is one 32-token block (two 16-token HND pages) of one sequence b,
+//   for all KV heads of a head group; units are numbered sequence-major, and
+//   there are U = sum_b ceil(L_b / 32) of them.  A workgroup has one wave per
+//   KV head of its group (up to 8), and workgroup w of a group takes units
+//   [floor(w U / NWG), floor((w+1) U / NWG)).  Its waves walk the same token
+//   range, so the slabs of all heads of a page -- contiguous in the HND
+//   layout -- are requested together, and every workgroup streams the same
+//   number of blocks to within one.  NWG is sized from host integers to fill
+//   the chip once.  The part of sequence b covered by workgroup w is a
+//   "piece"; its partial result goes to slot (b + w), which is unique,
+//   depends only on the sequence lengths (never on page ids) and needs at
+//   most (num_seqs + NWG) slots.
 //
 // Per 32-token block, on the matrix cores (16x16x32 bf16 MFMA):
 //   S^T[16 tok x 16 heads] = K[16 tok x d] * Q^T[d x 16 heads]   (per slab)
@@ -23,10 +31,10 @@
 // in the token loop.  Heads beyond G (when G < 16) carry a zero query and are
 // discarded.
 //
-// The four waves then merge their (m, l, acc) through LDS into one partial per
-// (split, head); decode_merge combines the partials of all splits and the
-// sink: M = max(max_s m_s, sink), out = sum_s acc_s 2^(m_s - M) /
-// (sum_s l_s 2^(m_s - M) + 2^(sink - M)), all in base-2 units.
+// Loads run ahead of the matrix work (see run_piece).  decode_merge then combines
+// the pieces of each (sequence, head) in logical order together with the
+// sink: M = max(max_p m_p, sink), out = sum_p acc_p 2^(m_p - M) /
+// (sum_p l_p 2^(m_p - M) + 2^(sink - M)), all in base-2 units.
 #include "common.h"
 #include "kernels.h"
 
@@ -39,12 +47,85 @@ struct SplitArgs {
     const uint16_t *__restrict__ v_cache;
     const int32_t *__restrict__ block_table;
     const int32_t *__restrict__ seq_lens;
-    float *__restrict__ part_ml;
-    float *__restrict__ part_acc;
-    int num_q_heads, num_kv_heads, group;
-    int max_pages, max_splits, split_tokens, wave_tokens;
+    float *__restrict__ part_ml;   // [slots][G][2]
+    float *__restrict__ part_acc;  // [slots][G][D]
+    int num_seqs, num_q_heads, num_kv_heads, group, max_pages;
+    int num_wgs;        // workgroups per head group
+    int heads_per_wg;   // KV heads (waves) per workgroup
     float scale_log2;
 };
+
+constexpr int kUnitTokens = 32;
+
+__device__ __forceinline__ long long units_of(int L)
+{
+    return (L + kUnitTokens - 1) / kUnitTokens;
+}
+
+// First unit of workgroup w, and the workgroup that processes unit u (the
+// largest w whose first unit is <= u).
+__device__ __forceinline__ long long wave_first_unit(long long w, long long U, int nw)
+{
+    return w * U / nw;
+}
+__device__ __forceinline__ int wave_of_unit(long long u, long long U, int nw)
+{
+    return (int)(((u + 1) * nw - 1) / U);
+}
+
+// Wave-wide scan over the sequences.  Returns U, the total unit count; when
+// `target` >= 0 also returns the sequence that holds unit `target` and the
+// index of that sequence's first unit.
+__device__ long long scan_units(const int32_t *__restrict__ seq_lens, int num_seqs, int lane,
+                                long long target, int *b_out, long long *base_out)
+{
+    long long carry = 0;
+    bool found = false;
+    for (int b0 = 0; b0 < num_seqs; b0 += 64) {
+        const int b = b0 + lane;
+        const long long nb = b < num_seqs ? units_of(seq_lens[b]) : 0;
+        long long incl = nb;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const long long y = __shfl_up(incl, off, 64);
+            if (lane >= off)
+                incl += y;
+        }
+        if (target >= 0 && !found) {
+            const unsigned long long hit = __ballot(carry + incl > target);
+            if (hit) {
+                const int first = __builtin_ctzll(hit);
+                *b_out = b0 + first;
+                *base_out = carry + __shfl(incl - nb, first, 64);
+                found = true;
+            }
+        }
+        carry += __shfl(incl, 63, 64);
+    }
+    return carry;
+}
+
+// Values the wave agrees on but the compiler cannot prove uniform (they come
+// out of shuffles and ballots): moving them to scalar registers turns the
+// page-table and length reads into scalar loads, which are counted apart from
+// the vector loads in flight, so prefetched K/V blocks are not waited for.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ long long uniform64(long long v)
+{
+    const unsigned long long u = (unsigned long long)v;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+// Read-only int32 data (page table, lengths) at a wave-uniform index, through
+// the constant address space: the compiler may then use the scalar unit's
+// load path, which it only does for memory it knows is not written while the
+// kernel runs -- true of every input here.
+__device__ __forceinline__ int load_scalar(const int32_t *p, long long idx)
+{
+    return ((const __attribute__((address_space(4))) int32_t *)p)[idx];
+}
 
 template <int D>
 struct VRowT;
@@ -57,8 +138,9 @@ struct VRowT<128> {
     using type = u32x4_t;  // 8 bf16: dims 8n .. 8n+7
 };
 
-// Registers of one 32-token block: K operands of both slabs, and the V row
-// chunks of the 8 tokens this lane feeds to the PV product.
+// Registers of one 32-token block: K of both slabs as loaded (coalesced:
+// chunk j*64 + lane of a slab, 16 B each), and the V row chunks of the 8
+// tokens this lane feeds to the PV product.
 template <int D>
 struct Block {
     using VRow = typename VRowT<D>::type;
@@ -66,7 +148,22 @@ struct Block {
     VRow v[8];
 };
 
+// K slabs are read with whole rows per lane quad (consecutive lanes read
+// consecutive 16-byte chunks) and with the non-temporal hint, the form the
+// memory pipeline serves fastest, then moved through a per-wave LDS buffer
+// into the MFMA operand layout (lane n reads row n).  Chunk cc of row r is
+// stored at position cc ^ swz(r), which makes both the row writes and the
+// column-of-rows reads free of LDS bank conflicts.
 template <int D>
+__device__ __forceinline__ int k_swizzle(int r)
+{
+    return D == 64 ? ((r >> 1) & 7) : (r & 15);
+}
+
+// Load one 32-token block starting at token t0.  kFull: both slabs lie inside
+// the range (no branch, so the compiler can keep several blocks in flight).
+// Otherwise the second slab is loaded only when it holds a token < t_end.
+template <int D, bool kFull>
 __device__ __forceinline__ void load_block(Block<D> &blk, const uint16_t *__restrict__ kc,
                                            const uint16_t *__restrict__ vc,
                                            const int32_t *__restrict__ bt, int t0, int t_end,
@@ -74,23 +171,28 @@ __device__ __forceinline__ void load_block(Block<D> &blk, const uint16_t *__rest
 {
     using VRow = typename VRowT<D>::type;
     constexpr size_t slab = 16 * D;
-    const int page0 = bt[t0 >> 4];
+    const int lane = lg * 16 + n;
+    const int pg = uniform(t0 >> 4);
+    const int page0 = load_scalar(bt, pg);
     const size_t base0 = ((size_t)page0 * num_kv_heads + g) * slab;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-        blk.k[0][kk] = *(const u32x4_t *)(kc + base0 + n * D + kk * 32 + lg * 8);
+    for (int j = 0; j < D / 32; ++j)
+        blk.k[0][j] = __builtin_nontemporal_load((const u32x4_t *)(kc + base0 + (j * 64 + lane) * 8));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        blk.v[i] = *(const VRow *)(vc + base0 + (4 * lg + i) * D + n * (D / 16));
-    if (t0 + 16 < t_end) {
-        const int page1 = bt[(t0 >> 4) + 1];
+        blk.v[i] = __builtin_nontemporal_load(
+            (const VRow *)(vc + base0 + (4 * lg + i) * D + n * (D / 16)));
+    if (kFull || t0 + 16 < t_end) {
+        const int page1 = load_scalar(bt, pg + 1);
         const size_t base1 = ((size_t)page1 * num_kv_heads + g) * slab;
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-            blk.k[1][kk] = *(const u32x4_t *)(kc + base1 + n * D + kk * 32 + lg * 8);
+        for (int j = 0; j < D / 32; ++j)
+            blk.k[1][j] =
+                __builtin_nontemporal_load((const u32x4_t *)(kc + base1 + (j * 64 + lane) * 8));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            blk.v[4 + i] = *(const VRow *)(vc + base1 + (4 * lg + i) * D + n * (D / 16));
+            blk.v[4 + i] = __builtin_nontemporal_load(
+                (const VRow *)(vc + base1 + (4 * lg + i) * D + n * (D / 16)));
     } else {
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
@@ -108,17 +210,38 @@ struct WaveState {
     f32x4_t acc[D / 16];
 };
 
-template <int D>
+template <int D, bool kMasked>
 __device__ __forceinline__ void compute_block(WaveState<D> &st, Block<D> &blk,
                                               const u32x4_t (&qop)[D / 32], int t0, int t_end,
-                                              float scale_log2, int lg)
+                                              float scale_log2, int lg, u32x4_t *klds)
 {
     using VRow = typename VRowT<D>::type;
+    constexpr int kChunks = D / 8;  // 16-byte chunks per K row
+    const int n = threadIdx.x & 15, lane = threadIdx.x & 63;
+    // K rows -> LDS (swizzled), then the operand layout back: lane n, row n.
+    // The exchange stays within the wave, whose LDS operations the hardware
+    // performs in order; the wave barriers keep the compiler from moving the
+    // reads above the writes, or the next block's writes above these reads.
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int j = 0; j < D / 32; ++j) {
+            const int c = j * 64 + lane, r = c / kChunks, cc = c % kChunks;
+            klds[(s * 16 + r) * kChunks + (cc ^ k_swizzle<D>(r))] = blk.k[s][j];
+        }
+    __builtin_amdgcn_wave_barrier();
+    u32x4_t kop[2][D / 32];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+            kop[s][kk] = klds[(s * 16 + n) * kChunks + ((kk * 4 + lg) ^ k_swizzle<D>(n))];
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-        s0 = mfma16x16x32(blk.k[0][kk], qop[kk], s0);
-        s1 = mfma16x16x32(blk.k[1][kk], qop[kk], s1);
+        s0 = mfma16x16x32(kop[0][kk], qop[kk], s0);
+        s1 = mfma16x16x32(kop[1][kk], qop[kk], s1);
     }
     float x[8];
 #pragma unroll
@@ -126,7 +249,7 @@ __device__ __forceinline__ void compute_block(WaveState<D> &st, Block<D> &blk,
         x[i] = s0[i] * scale_log2;
         x[4 + i] = s1[i] * scale_log2;
     }
-    if (t0 + 32 > t_end) {
+    if (kMasked) {
         // tail block: mask scores and zero the V rows of tokens outside the
         // range (they may hold NaN, and 0 * NaN would poison every head)
 #pragma unroll
@@ -174,25 +297,20 @@ __device__ __forceinline__ void compute_block(WaveState<D> &st, Block<D> &blk,
     }
 }
 
+// One piece: tokens [t_begin, t_end) of segment (b, g); the result goes to `slot`.
 template <int D>
-__global__ __launch_bounds__(64 * kDecodeWaves) void decode_split_bf16(SplitArgs a)
+__device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int t_begin,
+                                          int t_end, long long slot, int n, int lg,
+                                          u32x4_t *klds)
 {
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int L = a.seq_lens[b];
-    const int wg_start = s * a.split_tokens;
-    if (wg_start >= L)
-        return;  // uniform over the workgroup, before any barrier
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n = lane & 15, lg = lane >> 4;
-    const int wg_end = min(wg_start + a.split_tokens, L);
-    const int t_begin = wg_start + wave * a.wave_tokens;
-    const int t_end = min(t_begin + a.wave_tokens, wg_end);
-
+    b = uniform(b);
+    g = uniform(g);
+    t_begin = uniform(t_begin);
+    t_end = uniform(t_end);
     // Q^T operand: column n = query head g*G + n, dims kk*32 + lg*8 .. +7
     u32x4_t qop[D / 32];
-    const int h = g * a.group + n;
     if (n < a.group) {
-        const uint16_t *qrow = a.q + ((size_t)b * a.num_q_heads + h) * D;
+        const uint16_t *qrow = a.q + ((size_t)b * a.num_q_heads + g * a.group + n) * D;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
             qop[kk] = *(const u32x4_t *)(qrow + kk * 32 + lg * 8);
@@ -201,7 +319,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_split_bf16(SplitArgs
         for (int kk = 0; kk < D / 32; ++kk)
             qop[kk] = u32x4_t{0, 0, 0, 0};
     }
-
     WaveState<D> st;
     st.m = kNegInf;
     st.lsum = 0.f;
@@ -210,60 +327,117 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_split_bf16(SplitArgs
         st.acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
-    const int nblocks = t_end > t_begin ? (t_end - t_begin + 31) >> 5 : 0;
-    Block<D> bufA, bufB;
-    if (nblocks > 0)
-        load_block<D>(bufA, a.k_cache, a.v_cache, bt, t_begin, t_end, g, a.num_kv_heads, n, lg);
-    for (int ib = 0; ib < nblocks; ib += 2) {
-        const int t0 = t_begin + 32 * ib;
-        if (ib + 1 < nblocks)
-            load_block<D>(bufB, a.k_cache, a.v_cache, bt, t0 + 32, t_end, g, a.num_kv_heads, n,
-                          lg);
-        compute_block<D>(st, bufA, qop, t0, t_end, a.scale_log2, lg);
-        if (ib + 1 >= nblocks)
-            break;
-        if (ib + 2 < nblocks)
-            load_block<D>(bufA, a.k_cache, a.v_cache, bt, t0 + 64, t_end, g, a.num_kv_heads, n,
-                          lg);
-        compute_block<D>(st, bufB, qop, t0 + 32, t_end, a.scale_log2, lg);
+    // Full blocks stream through a ring of register buffers with loads issued
+    // ahead of the matrix work (two blocks ahead at d = 64, one at d = 128,
+    // where a block is 16 KiB per wave).  Prefetches past the last full block
+    // re-read that block (a cache hit), so the loop body has no branches
+    // around loads.  A partial last block is handled after the loop.
+    const int nfull = (t_end - t_begin) / kUnitTokens;
+    const int t_last = t_begin + kUnitTokens * (nfull - 1);
+    auto at = [&](int ib) { return min(t_begin + kUnitTokens * ib, t_last); };
+    if (nfull > 0) {
+        if constexpr (D == 64) {
+            Block<D> b0, b1, b2;
+            load_block<D, true>(b0, a.k_cache, a.v_cache, bt, at(0), t_end, g, a.num_kv_heads, n,
+                                lg);
+            load_block<D, true>(b1, a.k_cache, a.v_cache, bt, at(1), t_end, g, a.num_kv_heads, n,
+                                lg);
+            for (int ib = 0; ib < nfull; ib += 3) {
+                const int t0 = t_begin + kUnitTokens * ib;
+                load_block<D, true>(b2, a.k_cache, a.v_cache, bt, at(ib + 2), t_end, g,
+                                    a.num_kv_heads, n, lg);
+                compute_block<D, false>(st, b0, qop, t0, t_end, a.scale_log2, lg, klds);
+                if (ib + 1 >= nfull)
+                    break;
+                load_block<D, true>(b0, a.k_cache, a.v_cache, bt, at(ib + 3), t_end, g,
+                                    a.num_kv_heads, n, lg);
+                compute_block<D, false>(st, b1, qop, t0 + 32, t_end, a.scale_log2, lg, klds);
+                if (ib + 2 >= nfull)
+                    break;
+                load_block<D, true>(b1, a.k_cache, a.v_cache, bt, at(ib + 4), t_end, g,
+                                    a.num_kv_heads, n, lg);
+                compute_block<D, false>(st, b2, qop, t0 + 64, t_end, a.scale_log2, lg, klds);
+            }
+        } else {
+            Block<D> b0, b1;
+            load_block<D, true>(b0, a.k_cache, a.v_cache, bt, at(0), t_end, g, a.num_kv_heads, n,
+                                lg);
+            for (int ib = 0; ib < nfull; ib += 2) {
+                const int t0 = t_begin + kUnitTokens * ib;
+                load_block<D, true>(b1, a.k_cache, a.v_cache, bt, at(ib + 1), t_end, g,
+                                    a.num_kv_heads, n, lg);
+                compute_block<D, false>(st, b0, qop, t0, t_end, a.scale_log2, lg, klds);
+                if (ib + 1 >= nfull)
+                    break;
+                load_block<D, true>(b0, a.k_cache, a.v_cache, bt, at(ib + 2), t_end, g,
+                                    a.num_kv_heads, n, lg);
+                compute_block<D, false>(st, b1, qop, t0 + 32, t_end, a.scale_log2, lg, klds);
+            }
+        }
+    }
+    if (t_begin + kUnitTokens * nfull < t_end) {
+        Block<D> bt_tail;
+        const int t0 = t_begin + kUnitTokens * nfull;
+        load_block<D, false>(bt_tail, a.k_cache, a.v_cache, bt, t0, t_end, g, a.num_kv_heads, n,
+                             lg);
+        compute_block<D, true>(st, bt_tail, qop, t0, t_end, a.scale_log2, lg, klds);
     }
     const float lsum = group4_sum(st.lsum);
-
-    // merge the waves' partial results through LDS
-    constexpr int kStride = D + 1;  // padding spreads the 16 heads over banks
-    __shared__ float s_m[kDecodeWaves][16];
-    __shared__ float s_l[kDecodeWaves][16];
-    __shared__ float s_acc[kDecodeWaves][16 * kStride];
-    if (lg == 0) {
-        s_m[wave][n] = st.m;
-        s_l[wave][n] = lsum;
-    }
-#pragma unroll
-    for (int e = 0; e < D / 16; ++e)
+    if (n < a.group) {
+        const size_t row = (size_t)slot * a.num_q_heads + (size_t)g * a.group + n;
+        if (lg == 0)
+            *(float2 *)(a.part_ml + row * 2) = make_float2(st.m, lsum);
+        // lane (n, lg) holds dims (D/16)*(4*lg + i) + e of head n
+        float *dst = a.part_acc + row * D;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            s_acc[wave][n * kStride + (D / 16) * (4 * lg + i) + e] = st.acc[e][i];
-    __syncthreads();
+#pragma unroll
+            for (int e4 = 0; e4 < D / 16; e4 += 4)
+                *(f32x4_t *)(dst + (D / 16) * (4 * lg + i) + e4) =
+                    f32x4_t{st.acc[e4][i], st.acc[e4 + 1][i], st.acc[e4 + 2][i],
+                            st.acc[e4 + 3][i]};
+    }
+}
 
-    const size_t part_row = ((size_t)b * a.max_splits + s) * a.num_q_heads + (size_t)g * a.group;
-    for (int idx = threadIdx.x; idx < a.group * D; idx += 64 * kDecodeWaves) {
-        const int hn = idx / D, d = idx - hn * D;
-        float M = kNegInf;
-#pragma unroll
-        for (int w = 0; w < kDecodeWaves; ++w)
-            M = fmaxf(M, s_m[w][hn]);
-        float acc = 0.f, l = 0.f;
-#pragma unroll
-        for (int w = 0; w < kDecodeWaves; ++w) {
-            const float mw = s_m[w][hn];
-            const float f = mw == kNegInf ? 0.f : exp2_fast(mw - M);
-            acc += f * s_acc[w][hn * kStride + d];
-            l += f * s_l[w][hn];
-        }
-        a.part_acc[(part_row + hn) * D + d] = acc;
-        if (d == 0) {
-            a.part_ml[(part_row + hn) * 2 + 0] = M;
-            a.part_ml[(part_row + hn) * 2 + 1] = l;
+template <int D>
+__global__ __launch_bounds__(512) void decode_split_bf16(SplitArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, lg = lane >> 4;
+    const int g = uniform(blockIdx.y * a.heads_per_wg + (threadIdx.x >> 6));
+    if (g >= a.num_kv_heads)
+        return;  // the last head group may be partial (waves are independent)
+    const int w = blockIdx.x;
+    // per-wave K staging buffer: one 32-token block of K
+    __shared__ u32x4_t s_k[kDecodeMaxHeadsPerWg][2 * 16 * (D / 8)];
+    u32x4_t *klds = s_k[threadIdx.x >> 6];
+    int b = 0;
+    long long base = 0;
+    const long long U = scan_units(a.seq_lens, a.num_seqs, lane, -1, &b, &base);
+    const long long u_begin = wave_first_unit(w, U, a.num_wgs);
+    const long long u_end = wave_first_unit(w + 1, U, a.num_wgs);
+    if (u_begin >= u_end)
+        return;  // no unit for this workgroup
+    scan_units(a.seq_lens, a.num_seqs, lane, u_begin, &b, &base);
+    b = uniform(b);
+    base = uniform64(base);
+    long long u = uniform64(u_begin);
+    const long long u_stop = uniform64(u_end);
+    while (u < u_stop) {
+        // sequence b holds units [base, base + nblk)
+        const int L = load_scalar(a.seq_lens, b);
+        const long long nblk = units_of(L);
+        const long long piece_end = min(u_stop, base + nblk);
+        const int t_begin = (int)(u - base) * kUnitTokens;
+        const int t_end = min((int)(piece_end - base) * kUnitTokens, L);
+        run_piece<D>(a, b, g, t_begin, t_end, (long long)b + w, n, lg, klds);
+        u = piece_end;
+        if (u < u_stop) {
+            // next sequence with at least one unit
+            base += nblk;
+            do {
+                ++b;
+            } while (load_scalar(a.seq_lens, b) == 0);
         }
     }
 }
@@ -274,52 +448,75 @@ struct MergeArgs {
     const int32_t *__restrict__ seq_lens;
     const float *__restrict__ sinks;
     void *__restrict__ out;
-    int num_q_heads, max_splits, split_tokens;
+    int num_seqs, num_q_heads, num_wgs;
 };
 
-// One wave per (query head, sequence): combine the splits and fold the sink.
+// One wave per (query head, sequence): combine the pieces of the sequence in
+// logical order and fold the sink.
 template <int D, bool kBf16Out>
 __global__ __launch_bounds__(64) void decode_merge(MergeArgs a)
 {
     const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-    const int L = a.seq_lens[b];
-    const int ns = (L + a.split_tokens - 1) / a.split_tokens;
     const float sink2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
-    const size_t row0 = (size_t)b * a.max_splits * a.num_q_heads + h;
-    const size_t sstride = a.num_q_heads;
+    const int L = a.seq_lens[b];
+    const long long nblk = units_of(L);
 
+    int w_lo = 0, w_hi = -1;
+    long long U = 0;
+    if (nblk > 0) {
+        int bb = 0;
+        long long base = 0;
+        U = scan_units(a.seq_lens, a.num_seqs, lane, -1, &bb, &base);
+        // units of the sequences before b
+        long long before = 0;
+        for (int b0 = 0; b0 < b; b0 += 64) {
+            const int bi = b0 + lane;
+            before += bi < b ? units_of(a.seq_lens[bi]) : 0;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            before += __shfl_xor(before, off, 64);
+        w_lo = wave_of_unit(before, U, a.num_wgs);
+        w_hi = wave_of_unit(before + nblk - 1, U, a.num_wgs);
+    }
+
+    // workgroups in [w_lo, w_hi] with an empty unit range (possible when
+    // there are fewer units than workgroups) wrote nothing and are skipped
     float M = sink2;
-    for (int s = lane; s < ns; s += 64)
-        M = fmaxf(M, a.part_ml[(row0 + s * sstride) * 2]);
+    for (int w = w_lo + lane; w <= w_hi; w += 64)
+        if (wave_first_unit(w, U, a.num_wgs) < wave_first_unit(w + 1, U, a.num_wgs))
+            M = fmaxf(M, a.part_ml[((size_t)(b + w) * a.num_q_heads + h) * 2]);
     M = wave_max(M);
 
     constexpr int kPer = D / 64;
     float acc[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j)
-        acc[j] = 0.f;
+    for (int k = 0; k < kPer; ++k)
+        acc[k] = 0.f;
     float den = 0.f;
     if (M != kNegInf) {
         den = sink2 == kNegInf ? 0.f : exp2_fast(sink2 - M);
-        for (int s = 0; s < ns; ++s) {
-            const size_t r = row0 + s * sstride;
-            const float ms = a.part_ml[r * 2];
-            const float f = ms == kNegInf ? 0.f : exp2_fast(ms - M);
+        for (int w = w_lo; w <= w_hi; ++w) {
+            if (wave_first_unit(w, U, a.num_wgs) == wave_first_unit(w + 1, U, a.num_wgs))
+                continue;
+            const size_t r = (size_t)(b + w) * a.num_q_heads + h;
+            const float mp = a.part_ml[r * 2];
+            const float f = mp == kNegInf ? 0.f : exp2_fast(mp - M);
             den += f * a.part_ml[r * 2 + 1];
 #pragma unroll
-            for (int j = 0; j < kPer; ++j)
-                acc[j] += f * a.part_acc[r * D + lane + 64 * j];
+            for (int k = 0; k < kPer; ++k)
+                acc[k] += f * a.part_acc[r * D + lane + 64 * k];
         }
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     const size_t o = ((size_t)b * a.num_q_heads + h) * D;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const float v = acc[j] * inv;
+    for (int k = 0; k < kPer; ++k) {
+        const float v = acc[k] * inv;
         if (kBf16Out)
-            ((__bf16 *)a.out)[o + lane + 64 * j] = (__bf16)v;
+            ((__bf16 *)a.out)[o + lane + 64 * k] = (__bf16)v;
         else
-            ((float *)a.out)[o + lane + 64 * j] = v;
+            ((float *)a.out)[o + lane + 64 * k] = v;
     }
 }
 
@@ -334,16 +531,16 @@ hipError_t launch_split_d(const DecodeLaunch &p)
     a.seq_lens = p.seq_lens;
     a.part_ml = p.part_ml;
     a.part_acc = p.part_acc;
+    a.num_seqs = p.num_seqs;
     a.num_q_heads = p.num_q_heads;
     a.num_kv_heads = p.num_kv_heads;
     a.group = p.num_q_heads / p.num_kv_heads;
     a.max_pages = p.max_pages_per_seq;
-    a.max_splits = p.max_splits;
-    a.split_tokens = p.split_tokens;
-    a.wave_tokens = p.split_tokens / kDecodeWaves;
+    a.num_wgs = p.num_wgs;
+    a.heads_per_wg = p.heads_per_wg;
     a.scale_log2 = p.scale * kLog2e;
-    dim3 grid(p.max_splits, p.num_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL(decode_split_bf16<D>, grid, dim3(64 * kDecodeWaves), 0, p.stream, a);
+    const dim3 grid(p.num_wgs, (p.num_kv_heads + p.heads_per_wg - 1) / p.heads_per_wg);
+    hipLaunchKernelGGL(decode_split_bf16<D>, grid, dim3(64 * p.heads_per_wg), 0, p.stream, a);
     return hipGetLastError();
 }
 
@@ -356,9 +553,9 @@ hipError_t launch_merge_d(const DecodeLaunch &p)
     m.seq_lens = p.seq_lens;
     m.sinks = p.sinks;
     m.out = p.out;
+    m.num_seqs = p.num_seqs;
     m.num_q_heads = p.num_q_heads;
-    m.max_splits = p.max_splits;
-    m.split_tokens = p.split_tokens;
+    m.num_wgs = p.num_wgs;
     const dim3 grid(p.num_q_heads, p.num_seqs);
     if (p.dtype == 1)
         hipLaunchKernelGGL((decode_merge<D, true>), grid, dim3(64), 0, p.stream, m);
@@ -371,7 +568,7 @@ hipError_t launch_merge_d(const DecodeLaunch &p)
 
 hipError_t launch_decode_split_bf16(const DecodeLaunch &p)
 {
-    if (p.num_seqs == 0 || p.max_splits == 0)
+    if (p.num_seqs == 0 || p.num_wgs == 0)
         return hipSuccess;
     return p.head_dim == 64 ? launch_split_d<64>(p) : launch_split_d<128>(p);
 }

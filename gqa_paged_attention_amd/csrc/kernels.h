@@ -10,15 +10,15 @@ struct DecodeLaunch {
     int dtype;  // 0 f32, 1 bf16
     int num_seqs, num_q_heads, num_kv_heads, head_dim;
     int max_pages_per_seq;
-    int max_splits;     // grid size along the KV length
-    int split_tokens;   // tokens per split (a multiple of 32 * waves)
+    int num_wgs;        // split-pass workgroups per KV-head group
+    int heads_per_wg;   // KV heads (one wave each) per split-pass workgroup
     const void *q, *k_cache, *v_cache;
     const int32_t *block_table, *seq_lens;
     const float *sinks;
     float scale;
     void *out;
-    float *part_ml;     // [num_seqs][max_splits][Hq][2]
-    float *part_acc;    // [num_seqs][max_splits][Hq][head_dim]
+    float *part_ml;     // [slots][Hq][2],   slots = num_seqs + num_wgs
+    float *part_acc;    // [slots][Hq][head_dim]
     hipStream_t stream;
 };
 
@@ -34,9 +34,10 @@ struct PrefillLaunch {
     hipStream_t stream;
 };
 
-// Waves per decode split workgroup; each wave takes split_tokens / kDecodeWaves
-// consecutive tokens of the split.
-constexpr int kDecodeWaves = 4;
+// Decode split pass: up to 8 KV heads (waves) per workgroup, and about 2048
+// waves in all (256 CUs x 8 waves), one full round on MI355X.
+constexpr int kDecodeMaxHeadsPerWg = 8;
+constexpr int kDecodeTargetWaves = 2048;
 
 // Split pass: partial (max, sum, weighted values) per split into the workspace.
 hipError_t launch_decode_split_bf16(const DecodeLaunch &p);

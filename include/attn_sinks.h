@@ -87,8 +87,9 @@ enum attn_status {
  * attn_sinks_decode_workspace_bytes -- bytes of device scratch that
  * attn_sinks_decode needs for these sizes (split-KV partial results: one fp32
  * running max, one fp32 running sum and head_dim fp32 weighted values per
- * sequence, split and query head).  Returns 0 for sizes that
- * attn_sinks_decode would reject.  Depends on host integers only.
+ * piece and query head; the layout is given with attn_sinks_decode_merge).
+ * Returns 0 for sizes that attn_sinks_decode would reject or that need no
+ * scratch (max_seq_len == 0).  Depends on host integers only.
  */
 size_t attn_sinks_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                          int head_dim, int max_seq_len);
@@ -130,16 +131,21 @@ int attn_sinks_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads
  * elsewhere (for example over a KV range held by another device), since the
  * merge reads nothing but the workspace.
  *
- * Workspace layout for S = splits = ceil(max_seq_len / C), where C depends
- * only on (num_seqs, num_kv_heads, max_seq_len) and the byte count is given
- * by attn_sinks_decode_workspace_bytes:
- *   float ml [num_seqs][S][num_q_heads][2]    running max in base-2 units
- *                                             (scale * q.k * log2(e)), sum
- *                                             of 2^(s_j - max) over the split
- *   float acc[num_seqs][S][num_q_heads][head_dim]
- *                                             sum of 2^(s_j - max) * V[j]
- * Only splits s < ceil(L_b / C) of sequence b are written and read.  A split
- * with no key has max = -inf, sum = 0 and acc = 0.
+ * Workspace layout.  Units are 32-token blocks of one sequence, numbered in
+ * sequence order; there are U = sum_b ceil(L_b / 32) of them.  The split pass
+ * runs W workgroups per group of up to 8 KV heads (W depends only on
+ * num_seqs, num_kv_heads and max_seq_len); workgroup w takes units
+ * [floor(w U / W), floor((w+1) U / W)) for every KV head of its group.  The
+ * part of sequence b covered by workgroup w is stored in slot b + w, for all
+ * query heads (slots = num_seqs + W):
+ *   float ml [slots][num_q_heads][2]   running max in base-2 units
+ *                                      (scale*q.k*log2 e) and the sum of
+ *                                      2^(s_j - max) over the piece
+ *   float acc[slots][num_q_heads][head_dim], starting at the first multiple
+ *                                      of 4 floats after ml: the sum of
+ *                                      2^(s_j - max) * V[j]
+ * Only slots of pieces that exist are written and read; the byte count is
+ * attn_sinks_decode_workspace_bytes.
  *
  * attn_sinks_decode_partials -- the split pass (dtype must be
  * ATTN_DTYPE_BF16); arguments as for attn_sinks_decode.  No sink is involved.
@@ -153,10 +159,10 @@ int attn_sinks_decode_partials(int dtype, int num_seqs, int num_q_heads, int num
 
 /*
  * attn_sinks_decode_merge -- the merge pass: for each (sequence, head)
- * combine the splits' partial results with the sink, counted once
+ * combine the pieces' partial results with the sink, counted once
  * ("GPT-OSS on day 0", section "Sink Attention"):
- *   M = max(max_s m_s, sink * log2(e))
- *   out = sum_s acc_s 2^(m_s - M) / (sum_s l_s 2^(m_s - M) + 2^(sink*log2(e) - M))
+ *   M = max(max_p m_p, sink * log2(e))
+ *   out = sum_p acc_p 2^(m_p - M) / (sum_p l_p 2^(m_p - M) + 2^(sink*log2(e) - M))
  * and write out [num_seqs][num_q_heads][head_dim] in dtype (f32 or bf16).
  * The workspace is read only.
  */

@@ -45,13 +45,26 @@ def test_status_strings_and_version(lib):
     assert ga.attn_sinks_version() >= 100
 
 
+def _expected_ws(B, Hq, Hkv, d, max_len, target_waves=2048):
+    """The layout the header documents: W workgroups per group of up to 8 KV
+    heads (about 2048 waves in all, capped by the unit count); slots = B + W;
+    ml [slots][Hq][2] padded to a multiple of 4 floats, then acc
+    [slots][Hq][d]."""
+    per_wg = min(Hkv, 8)
+    groups = -(-Hkv // per_wg)
+    w = max(target_waves // (per_wg * groups), 1)
+    w = min(w, B * ((max_len + 31) // 32))
+    if w == 0:
+        return 0
+    slots = B + w
+    ml = (slots * Hq * 2 + 3) // 4 * 4
+    return (ml + slots * Hq * d) * 4
+
+
 def test_workspace_bytes(lib):
-    # gpt-oss decode shape: 64 seqs, 64/8 heads, d=64, max 8192 keys.
-    n = ga.attn_sinks_decode_workspace_bytes(64, 64, 8, 64, 8192)
-    assert n > 0 and n % (64 * 64 * (64 + 2) * 4) == 0
-    # one float pair + d floats per (seq, split, head)
-    splits = n // (64 * 64 * 66 * 4)
-    assert 1 <= splits <= 64
+    for args in [(64, 64, 8, 64, 8192), (128, 64, 4, 128, 32768), (1, 4, 1, 64, 257),
+                 (3, 8, 2, 128, 100), (32, 64, 8, 64, 16384)]:
+        assert ga.attn_sinks_decode_workspace_bytes(*args) == _expected_ws(*args), args
     assert ga.attn_sinks_decode_workspace_bytes(64, 64, 8, 64, 0) == 0
     assert ga.attn_sinks_decode_workspace_bytes(64, 64, 8, 96, 8192) == 0   # head_dim
     assert ga.attn_sinks_decode_workspace_bytes(64, 64, 7, 64, 8192) == 0   # Hq % Hkv
