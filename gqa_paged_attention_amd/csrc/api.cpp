@@ -22,19 +22,33 @@ bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
-// Debug override of the number of split-pass workgroups per head group, read
-// once.  Must be positive; anything else is ignored.
+// Debug overrides of the split-pass launch shape, read once: the number of
+// workgroups per head group (ATTN_SINKS_DECODE_WGS) and the KV heads per
+// workgroup (ATTN_SINKS_DECODE_HEADS_PER_WG, 1..8).  Invalid values are
+// ignored.
+int env_int(const char *name, long lo, long hi)
+{
+    const char *s = std::getenv(name);
+    if (!s)
+        return 0;
+    const long v = std::strtol(s, nullptr, 10);
+    return (v >= lo && v <= hi) ? (int)v : 0;
+}
+
 int wgs_override()
 {
     static int value = 0;
     static std::once_flag once;
+    std::call_once(once, [] { value = env_int("ATTN_SINKS_DECODE_WGS", 1, 1 << 20); });
+    return value;
+}
+
+int heads_override()
+{
+    static int value = 0;
+    static std::once_flag once;
     std::call_once(once, [] {
-        const char *s = std::getenv("ATTN_SINKS_DECODE_WGS");
-        if (s) {
-            long v = std::strtol(s, nullptr, 10);
-            if (v > 0 && v <= (1 << 20))
-                value = (int)v;
-        }
+        value = env_int("ATTN_SINKS_DECODE_HEADS_PER_WG", 1, attn::kDecodeMaxHeadsPerWg);
     });
     return value;
 }
@@ -52,13 +66,18 @@ struct DecodeShape {
 DecodeShape decode_shape(int num_seqs, int num_kv_heads, int max_seq_len)
 {
     DecodeShape s;
-    s.heads_per_wg = num_kv_heads < attn::kDecodeMaxHeadsPerWg ? num_kv_heads
-                                                               : attn::kDecodeMaxHeadsPerWg;
+    const int cap = heads_override() ? heads_override() : attn::kDecodeMaxHeadsPerWg;
+    s.heads_per_wg = num_kv_heads < cap ? num_kv_heads : cap;
     const int groups = (num_kv_heads + s.heads_per_wg - 1) / s.heads_per_wg;
     const long long units_max = (long long)num_seqs * ((max_seq_len + 31) / 32);
     long long w = wgs_override();
     if (!w) {
-        w = attn::kDecodeTargetWaves / ((long long)s.heads_per_wg * groups);
+        // the same number of workgroups on every CU, at least 4 waves per CU
+        const int waves_per_cu = s.heads_per_wg > attn::kDecodeMinWavesPerCU
+                                     ? s.heads_per_wg
+                                     : attn::kDecodeMinWavesPerCU;
+        const long long total = (long long)attn::kDeviceCUs * waves_per_cu / s.heads_per_wg;
+        w = total / groups;
         if (w < 1)
             w = 1;
     }

@@ -11,7 +11,7 @@
 //   A unit is one 32-token block (two 16-token HND pages) of one sequence b,
 //   for all KV heads of a head group; units are numbered sequence-major, and
 //   there are U = sum_b ceil(L_b / 32) of them.  A workgroup has one wave per
-//   KV head of its group (up to 8), and workgroup w of a group takes units
+//   KV head of its group (up to 4), and workgroup w of a group takes units
 //   [floor(w U / NWG), floor((w+1) U / NWG)).  Its waves walk the same token
 //   range, so the slabs of all heads of a page -- contiguous in the HND
 //   layout -- are requested together, and every workgroup streams the same
@@ -408,9 +408,10 @@ __global__ __launch_bounds__(512) void decode_split_bf16(SplitArgs a)
     if (g >= a.num_kv_heads)
         return;  // the last head group may be partial (waves are independent)
     const int w = blockIdx.x;
-    // per-wave K staging buffer: one 32-token block of K
-    __shared__ u32x4_t s_k[kDecodeMaxHeadsPerWg][2 * 16 * (D / 8)];
-    u32x4_t *klds = s_k[threadIdx.x >> 6];
+    // per-wave K staging buffer: one 32-token block of K (dynamic LDS,
+    // heads_per_wg * 64 * D bytes)
+    extern __shared__ u32x4_t s_k[];
+    u32x4_t *klds = s_k + (threadIdx.x >> 6) * (2 * 16 * (D / 8));
     int b = 0;
     long long base = 0;
     const long long U = scan_units(a.seq_lens, a.num_seqs, lane, -1, &b, &base);
@@ -540,7 +541,8 @@ hipError_t launch_split_d(const DecodeLaunch &p)
     a.heads_per_wg = p.heads_per_wg;
     a.scale_log2 = p.scale * kLog2e;
     const dim3 grid(p.num_wgs, (p.num_kv_heads + p.heads_per_wg - 1) / p.heads_per_wg);
-    hipLaunchKernelGGL(decode_split_bf16<D>, grid, dim3(64 * p.heads_per_wg), 0, p.stream, a);
+    const size_t lds = (size_t)p.heads_per_wg * 2 * 16 * (D / 8) * sizeof(u32x4_t);
+    hipLaunchKernelGGL(decode_split_bf16<D>, grid, dim3(64 * p.heads_per_wg), lds, p.stream, a);
     return hipGetLastError();
 }
 

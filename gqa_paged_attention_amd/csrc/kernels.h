@@ -34,10 +34,12 @@ struct PrefillLaunch {
     hipStream_t stream;
 };
 
-// Decode split pass: up to 8 KV heads (waves) per workgroup, and about 2048
-// waves in all (256 CUs x 8 waves), one full round on MI355X.
-constexpr int kDecodeMaxHeadsPerWg = 8;
-constexpr int kDecodeTargetWaves = 2048;
+// Decode split pass: up to 4 KV heads (waves) per workgroup; the grid gives
+// every one of MI355X's 256 CUs the same number of workgroups, with at least
+// 4 waves per CU.
+constexpr int kDecodeMaxHeadsPerWg = 4;
+constexpr int kDeviceCUs = 256;
+constexpr int kDecodeMinWavesPerCU = 4;
 
 // Split pass: partial (max, sum, weighted values) per split into the workspace.
 hipError_t launch_decode_split_bf16(const DecodeLaunch &p);

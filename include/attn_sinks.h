@@ -133,7 +133,7 @@ int attn_sinks_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads
  *
  * Workspace layout.  Units are 32-token blocks of one sequence, numbered in
  * sequence order; there are U = sum_b ceil(L_b / 32) of them.  The split pass
- * runs W workgroups per group of up to 8 KV heads (W depends only on
+ * runs W workgroups per group of up to 4 KV heads (W depends only on
  * num_seqs, num_kv_heads and max_seq_len); workgroup w takes units
  * [floor(w U / W), floor((w+1) U / W)) for every KV head of its group.  The
  * part of sequence b covered by workgroup w is stored in slot b + w, for all

@@ -45,14 +45,14 @@ def test_status_strings_and_version(lib):
     assert ga.attn_sinks_version() >= 100
 
 
-def _expected_ws(B, Hq, Hkv, d, max_len, target_waves=2048):
-    """The layout the header documents: W workgroups per group of up to 8 KV
-    heads (about 2048 waves in all, capped by the unit count); slots = B + W;
-    ml [slots][Hq][2] padded to a multiple of 4 floats, then acc
-    [slots][Hq][d]."""
-    per_wg = min(Hkv, 8)
+def _expected_ws(B, Hq, Hkv, d, max_len):
+    """The layout the header documents: W workgroups per group of up to 4 KV
+    heads (256 CUs x max(4, heads per workgroup) waves in all, capped by the
+    unit count); slots = B + W; ml [slots][Hq][2] padded to a multiple of 4
+    floats, then acc [slots][Hq][d]."""
+    per_wg = min(Hkv, 4)
     groups = -(-Hkv // per_wg)
-    w = max(target_waves // (per_wg * groups), 1)
+    w = max((256 * max(4, per_wg) // per_wg) // groups, 1)
     w = min(w, B * ((max_len + 31) // 32))
     if w == 0:
         return 0
