@@ -6,34 +6,69 @@
 // sections 3 and 4.1).  The causal mask is aligned to the end of the visible
 // keys, so a chunk over a cached prefix sees the whole prefix.
 //
-// Work decomposition: one workgroup (4 waves) owns BM = 128 consecutive query
-// rows of one query head of one sequence; wave w owns rows 32w .. 32w+31.  The
-// 1-D grid is ordered so that every workgroup of one (sequence, KV head) runs
-// on the same XCD (its L2 then serves the K/V tiles to all of them) and the
-// query tiles with the most keys start first.  Keys are walked in tiles of
-// BN = 64 (four 16-token HND pages), double-buffered in LDS: while a tile is
-// multiplied, the next one is loaded into registers (whole rows per lane quad)
-// and then written to the other buffer, one barrier per tile.
+// Work decomposition.  A workgroup of 4 waves owns BM consecutive query rows
+// of one query head of one sequence; each wave owns NRB row blocks of 32 rows
+// (d = 64: NRB = 2, BM = 256; d = 128: NRB = 1, BM = 128).  The 1-D grid is
+// ordered so that every workgroup of one (sequence, KV head) runs on the same
+// XCD (its L2 then serves the K/V tiles to all of them) and the query tiles
+// with the most keys start first.
 //
-// Per tile and wave, on 32x32x16 bf16 matrix instructions:
+// Keys are consumed in blocks of 32.  Per block, row block and wave, on
+// 32x32x16 bf16 matrix instructions:
 //   S^T[32 keys x 32 rows] = K[32 x d] (LDS, row-major) * Q^T[d x 32] (regs)
 //   O^T[32 dims x 32 rows] += V^T[32 dims x 16 keys] * P^T[16 keys x 32 rows]
 // Lane l holds row l%32 of S^T's columns, so the S^T accumulators are already
-// the P^T operand and each row's softmax state stays in its two lanes.  V^T
-// comes from the row-major V tile with LDS transpose reads (ds_read_b64_tr_b16:
-// within 16 lanes, lane i gets element i%4 of the 8 bytes addressed by lane
-// 4j + i/4, j = 0..3, i.e. column i of 4 consecutive rows).  K and V rows are
-// stored with XOR-swizzled chunks so that these reads are free of bank
-// conflicts.
+// the P^T operand and each row's softmax state stays in its two lanes (l and
+// l^32, joined by a permlane32 swap).  The K and V^T operands read from LDS
+// serve all NRB row blocks of the wave, which is what keeps the LDS read rate
+// below the matrix rate at d = 64.  V^T comes from the row-major V tile with
+// LDS transpose reads (ds_read_b64_tr_b16: within 16 lanes, lane i gets
+// element i%4 of the 8 bytes addressed by lane 4j + i/4, i.e. column i of 4
+// consecutive rows).
+//
+// K/V reach LDS by direct global-to-LDS loads (no registers): tiles of BN
+// keys (64 at d = 64, 32 at d = 128; 16 KiB of K+V either way) rotate through
+// four LDS stages, issued two tiles ahead.  Each 1 KiB load instruction
+// covers whole key rows of one 16-token page; lanes fetch the 16-byte chunk
+// that belongs in their slot of the XOR-swizzled row, so the transposed and
+// column reads above are free of bank conflicts.  Rows past the sequence are
+// fetched as copies of its last row (finite), and the causal mask hides them.
+//
+// Softmax reference.  A row's reference maximum m is set exactly from its
+// first block and then kept: weights 2^(s - m) may exceed 1, which bf16 and
+// the fp32 accumulators absorb as long as they stay far from overflow.  The
+// block's weight sum (needed anyway) detects the rare block that would come
+// too close (sum > 2^64); only then is the exact block maximum taken, m
+// raised, the accumulators rescaled and the block's weights recomputed.  The
+// final division uses the same m, so the result does not depend on it.
+//
+// Per step b a wave issues S^T of block b and P*V of block b-1 (16 matrix
+// instructions at d = 64) and computes the weights of block b; the weights
+// of block b-1 feed this step's P*V, so the exponentials overlap the matrix
+// stream of the same wave.
 #include "common.h"
 #include "kernels.h"
 
 namespace attn {
 namespace {
 
-constexpr int kBM = 128;
-constexpr int kBN = 64;
 constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kKB = 32;          // keys per block: one 32x32 S^T tile
+constexpr int kStages = 4;       // LDS stages; tiles are fetched kStages - 2 ahead
+constexpr int kLoadsPerTile = 4; // 1 KiB direct loads per wave per tile (2 K + 2 V)
+// A block whose weight sum exceeds this (per lane) triggers an exact rescale.
+constexpr float kWeightSumLimit = 18446744073709551616.0f;  // 2^64
+
+template <int D>
+struct Cfg {
+    static constexpr int kNRB = D == 64 ? 2 : 1;        // row blocks per wave
+    static constexpr int kBM = 32 * kNRB * kWaves;      // rows per workgroup
+    static constexpr int kBN = D == 64 ? 64 : 32;       // keys per LDS tile
+    static constexpr int kBPT = kBN / kKB;              // blocks per tile
+    static constexpr int kRowsPerLoad = 1024 / (2 * D); // key rows per 1 KiB load
+    static constexpr int kTileElems = kBN * D;          // bf16 elements of K (or V) per tile
+};
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -63,6 +98,27 @@ __device__ __forceinline__ int load_scalar(const int32_t *p, long long idx)
     return ((const __attribute__((address_space(4))) int32_t *)p)[idx];
 }
 
+// v of lane l and of lane l ^ 32 (the two lanes that hold one row).
+__device__ __forceinline__ void halves(float v, float &x, float &y)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    x = __uint_as_float(r[0]);
+    y = __uint_as_float(r[1]);
+}
+
+// Wait until at most n of this wave's direct loads are still in flight (the
+// older ones have landed in LDS), then meet the other waves.  The loads are
+// not tracked by the compiler's own wait insertion, hence the explicit wait.
+__device__ __forceinline__ void wait_loads_and_sync(bool all_landed)
+{
+    static_assert(kLoadsPerTile * (kStages - 3) == 4, "wait count");
+    if (all_landed)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 struct PrefillArgs {
     const uint16_t *__restrict__ q;
     const uint16_t *__restrict__ k_cache;
@@ -78,159 +134,326 @@ struct PrefillArgs {
 };
 
 // LDS tile layouts (bf16 elements).  K: 16-byte chunk c of key row r stored at
-// chunk c ^ ksw(r); V: 8-byte chunk c stored at c ^ vsw(r).
+// slot c ^ ksw(r); V: 8-byte chunk c stored at c ^ vsw(r), where vsw is even
+// so 16-byte chunks stay whole.  Both keep every access of the kernel free of
+// bank conflicts whether the LDS serves 8 lanes x 16 B (128 B) or 16 lanes x
+// 16 B (256 B) per cycle: the K column reads (32 consecutive rows, one chunk),
+// the 1 KiB tile writes and the V transpose reads (4 consecutive rows x 32 or
+// 64 bytes).
 template <int D>
-struct Tile {
+struct Swz {
+    static __device__ __forceinline__ int ksw(int key)
+    {
+        return D == 64 ? (((key >> 1) & 7) ^ ((key & 1) << 2)) : (key & 15);
+    }
+    static __device__ __forceinline__ int vsw(int key)
+    {
+        // d = 128: (bits 3,2) and (bits 4,3) of the four patterns both differ
+        return D == 64 ? ((key & 3) << 2) : ((0x18140c00 >> (8 * (key & 3))) & 0xff);
+    }
     static __device__ __forceinline__ int k_at(int key, int chunk16)
     {
-        const int sw = D == 64 ? ((key >> 1) & 7) : (key & 15);
-        return key * D + ((chunk16 ^ sw) << 3);
+        return key * D + ((chunk16 ^ ksw(key)) << 3);
     }
     static __device__ __forceinline__ int v_at(int key, int chunk8)
     {
-        const int sw = D == 64 ? (((key >> 1) & 3) << 2) : ((key & 7) << 2);
-        return key * D + ((chunk8 ^ sw) << 2);
+        return key * D + ((chunk8 ^ vsw(key)) << 2);
     }
-    uint16_t k[kBN * D];
-    uint16_t v[kBN * D];
-};
-
-// Registers of one K/V tile in flight: each thread holds 16-byte chunks
-// c = tid + 256 i of the row-major tile (key c / (D/8), chunk c % (D/8)).
-template <int D>
-struct TileRegs {
-    static constexpr int kPer = kBN * D / 8 / kThreads;
-    u32x4_t k[kPer];
-    u32x4_t v[kPer];
 };
 
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D> &tr, const PrefillArgs &a,
-                                          const int32_t *__restrict__ bt, int kv0, int L, int g)
+struct Smem {
+    uint16_t k[kStages][Cfg<D>::kTileElems];
+    uint16_t v[kStages][Cfg<D>::kTileElems];
+};
+
+// Per-lane parts of this wave's direct loads (constant over tiles).  The wave
+// loads 1 KiB chunks j = wave and wave + 4 of each K and V tile; chunk j holds
+// key rows R*j .. R*j+R-1 (R = 1024 / (2 d)), all inside one 16-token page,
+// and lane l fetches the 16-byte chunk that belongs in slot l % (d/8) of row
+// R*j + l / (d/8) of the swizzled tile.
+template <int D>
+struct LoadLanes {
+    int key[2];       // key of this lane's row within the tile, per chunk
+    int koff[2];      // element offset within the page-head slab: row and K chunk
+    int voff[2];      // the same for V
+    int tail_koff[2]; // offsets when the row is past the sequence: its last row
+    int tail_voff[2];
+};
+
+template <int D>
+__device__ __forceinline__ LoadLanes<D> load_lanes(int wave, int lane, int L)
 {
-    constexpr size_t slab = 16 * D;
-    // the tile's four pages (scalar loads); pages past the sequence are not read
-    int pages[4];
+    using C = Cfg<D>;
+    constexpr int kChunks = D / 8;  // 16-byte chunks per key row
+    LoadLanes<D> ll;
+    const int last_row = (L - 1) & 15;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        pages[j] = kv0 + 16 * j < L ? load_scalar(bt, (kv0 >> 4) + j) : 0;
+    for (int i = 0; i < 2; ++i) {
+        const int j = wave + kWaves * i;
+        const int key = C::kRowsPerLoad * j + lane / kChunks;
+        const int slot = lane % kChunks;
+        const int kc = 8 * (slot ^ Swz<D>::ksw(key)), vc = 8 * (slot ^ (Swz<D>::vsw(key) >> 1));
+        ll.key[i] = key;
+        ll.koff[i] = (key & 15) * D + kc;
+        ll.voff[i] = (key & 15) * D + vc;
+        ll.tail_koff[i] = last_row * D + kc;
+        ll.tail_voff[i] = last_row * D + vc;
+    }
+    return ll;
+}
+
+// One direct global-to-LDS load: lane l's 16 bytes at gbase + voff land at
+// LDS byte address lds + 16 l.  Issued as inline assembly so that the
+// compiler does not tie its own LDS reads to these loads (it would wait for
+// every load in flight, the prefetches included); the kernel waits for them
+// explicitly (wait_loads_and_sync).  M0 holds the LDS address; one wait state
+// separates its write from the load that reads it.
+__device__ __forceinline__ void dma16(const uint16_t *gbase, uint32_t voff, const uint16_t *lds)
+{
+    const uint32_t lds_addr =
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t *)lds;
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(gbase), "{m0}"(lds_addr)
+                 : "memory");
+}
+
+// Issue this wave's direct loads of tile t (keys t*BN ..) into stage t % S.
+// Rows past the sequence repeat its last row (finite; the causal mask hides
+// them); their page index is clamped to the last page, which holds that row.
+template <int D>
+__device__ __forceinline__ void load_tile(Smem<D> &sm, const PrefillArgs &a,
+                                          const int32_t *__restrict__ bt, int t, int L,
+                                          int last_page, size_t head_off, int wave,
+                                          const LoadLanes<D> &ll)
+{
+    using C = Cfg<D>;
+    const int kv0 = t * C::kBN;
+    const int stage = t % kStages;
 #pragma unroll
-    for (int i = 0; i < TileRegs<D>::kPer; ++i) {
-        const int c = threadIdx.x + kThreads * i;
-        const int key = c / (D / 8), chunk = c % (D / 8);
-        const int pj = key >> 4;
-        const int page = pj == 0 ? pages[0] : pj == 1 ? pages[1] : pj == 2 ? pages[2] : pages[3];
-        const size_t off = ((size_t)page * a.num_kv_heads + g) * slab + (key & 15) * D + chunk * 8;
-        if (kv0 + key < L) {
-            tr.k[i] = *(const u32x4_t *)(a.k_cache + off);
-            tr.v[i] = *(const u32x4_t *)(a.v_cache + off);
-        } else {  // rows past the sequence are zero (they may hold NaN in memory)
-            tr.k[i] = u32x4_t{0, 0, 0, 0};
-            tr.v[i] = u32x4_t{0, 0, 0, 0};
-        }
+    for (int i = 0; i < 2; ++i) {
+        const int j = wave + kWaves * i;
+        const int page = load_scalar(bt, min((kv0 + C::kRowsPerLoad * j) >> 4, last_page));
+        const size_t slab = (size_t)page * a.num_kv_heads * 16 * D + head_off;
+        const bool in = kv0 + ll.key[i] < L;
+        dma16(a.k_cache + slab, 2 * (in ? ll.koff[i] : ll.tail_koff[i]), &sm.k[stage][512 * j]);
+        dma16(a.v_cache + slab, 2 * (in ? ll.voff[i] : ll.tail_voff[i]), &sm.v[stage][512 * j]);
     }
 }
 
 template <int D>
-__device__ __forceinline__ void store_tile(Tile<D> &t, const TileRegs<D> &tr)
-{
-#pragma unroll
-    for (int i = 0; i < TileRegs<D>::kPer; ++i) {
-        const int c = threadIdx.x + kThreads * i;
-        const int key = c / (D / 8), chunk = c % (D / 8);
-        *(u32x4_t *)&t.k[Tile<D>::k_at(key, chunk)] = tr.k[i];
-        // the two 8-byte halves stay adjacent: the V swizzle keeps bit 0
-        *(u32x4_t *)&t.v[Tile<D>::v_at(key, 2 * chunk)] = tr.v[i];
-    }
-}
-
-template <int D>
-struct RowState {
-    u32x4_t qop[D / 16];     // Q^T operand: row l%32, dims 16kk + 8(l/32) .. +7
-    f32x16_t acc[D / 32];    // O^T: dims 32db + 8(r/4) + 4(l/32) + r%4 of row l%32
-    float m;                 // reference maximum, base-2 units
-    float lsum;              // this lane's half of the row sum
-    int pos;                 // position of the row (its last visible key)
+struct WaveState {
+    static constexpr int kNRB = Cfg<D>::kNRB;
+    u32x4_t qop[kNRB][D / 16];   // Q^T operand: row l%32, dims 16kk + 8(l/32) .. +7
+    f32x16_t acc[kNRB][D / 32];  // O^T: dims 32db + 8(r/4) + 4(l/32) + r%4 of row l%32
+    u32x4_t pop[kNRB][2];        // P^T of the block whose P*V is next
+    float m[kNRB];               // reference maximum, base-2 units
+    float lsum[kNRB];            // this lane's half of the row sum
 };
 
-template <int D, bool kMasked>
-__device__ __forceinline__ void compute_tile(RowState<D> &rs, const Tile<D> &t, int kv0, int L,
-                                             float scale_log2, int lane)
+// K operands of keys key0 .. key0+31 of an LDS K tile.
+template <int D>
+__device__ __forceinline__ void read_k(u32x4_t (&kop)[D / 16], const uint16_t *kt, int key0,
+                                       int lane)
 {
     const int r32 = lane & 31, half = lane >> 5;
-    // S^T for the two 32-key blocks
-    f32x16_t s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16_t{};
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            const u32x4_t kop = *(const u32x4_t *)&t.k[Tile<D>::k_at(kb * 32 + r32, 2 * kk + half)];
-            s[kb] = mfma32x32x16(kop, rs.qop[kk], s[kb]);
-        }
-    }
-    if (kMasked) {
-        const int lim = min(rs.pos, L - 1);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (kv0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3) > lim)
-                    s[kb][r] = kNegInf;
-    }
-    // row maximum over the tile (raw scores; the scale is positive)
-    float bm = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            bm = fmaxf(bm, s[kb][r]);
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64)) * scale_log2;
-    const float m_new = (bm > rs.m + kRescaleSlack) ? bm : rs.m;
-    if (__any(m_new != rs.m)) {
-        const float alpha = exp2_fast(rs.m - m_new);
-        rs.lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-            rs.acc[db] *= alpha;
-        rs.m = m_new;
-    }
-    // a row whose keys are all masked so far keeps m = -inf and weights 0
-    const float neg_m = rs.m == kNegInf ? 0.f : -rs.m;
-    u32x4_t pop[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int kb = ks >> 1, r0 = 8 * (ks & 1);
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float p0 = exp2_fast(fmaf(s[kb][r0 + 2 * j], scale_log2, neg_m));
-            const float p1 = exp2_fast(fmaf(s[kb][r0 + 2 * j + 1], scale_log2, neg_m));
-            w[j] = pack_bf16(p0, p1);
-            rs.lsum = add_pair(w[j], rs.lsum);
-        }
-        pop[ks] = u32x4_t{w[0], w[1], w[2], w[3]};
-    }
-    // O^T += V^T * P^T; V^T operand by transpose reads of the row-major tile
-    const int g16 = lane >> 4, i16 = lane & 15;
+    for (int kk = 0; kk < D / 16; ++kk)
+        kop[kk] = *(const u32x4_t *)&kt[Swz<D>::k_at(key0 + r32, 2 * kk + half)];
+}
+
+// V^T operands of keys key0 .. key0+31 of an LDS V tile: vop[db][ks] covers
+// dims 32db .. 32db+31 and keys key0 + 16ks + {4h..4h+3, 8+4h..8+4h+3}.
+template <int D>
+__device__ __forceinline__ void read_v(u32x4_t (&vop)[D / 32][2], const uint16_t *vt, int key0,
+                                       int lane)
+{
+    const int half = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
     const int src_key = 4 * half + (i16 >> 2);        // row of this lane's 8-byte read
     const int src_dim = 16 * (g16 & 1) + 4 * (i16 & 3);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int key = 16 * ks + src_key;
+        for (int ks = 0; ks < 2; ++ks) {
+            const int key = key0 + 16 * ks + src_key;
             const int dim = 32 * db + src_dim;
-            const u32x2_t lo = lds_read_tr(&t.v[Tile<D>::v_at(key, dim >> 2)]);
-            const u32x2_t hi = lds_read_tr(&t.v[Tile<D>::v_at(key + 8, dim >> 2)]);
-            const u32x4_t aop = {lo[0], lo[1], hi[0], hi[1]};
-            rs.acc[db] = mfma32x32x16(aop, pop[ks], rs.acc[db]);
+            const u32x2_t lo = lds_read_tr(&vt[Swz<D>::v_at(key, dim >> 2)]);
+            const u32x2_t hi = lds_read_tr(&vt[Swz<D>::v_at(key + 8, dim >> 2)]);
+            vop[db][ks] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
         }
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void prefill_bf16(PrefillArgs a)
+__device__ __forceinline__ f32x16_t qk_mfma(const u32x4_t (&qop)[D / 16],
+                                            const u32x4_t (&kop)[D / 16])
 {
+    f32x16_t s = {};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        s = mfma32x32x16(kop[kk], qop[kk], s);
+    return s;
+}
+
+template <int D>
+__device__ __forceinline__ void pv_mfma(f32x16_t (&acc)[D / 32], const u32x4_t (&vop)[D / 32][2],
+                                        const u32x4_t (&pop)[2])
+{
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            acc[db] = mfma32x32x16(vop[db][ks], pop[ks], acc[db]);
+}
+
+// Keys of the block with offset > thr (the row's position minus the block
+// start, minus 4h for h = lane / 32) are invisible.
+__device__ __forceinline__ void apply_mask(f32x16_t &s, int thr)
+{
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > thr)
+            s[r] = kNegInf;
+}
+
+// Exact block maximum of the row, base-2 units.
+__device__ __forceinline__ float block_max(const f32x16_t &s, float scale_log2)
+{
+    float bm = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r)
+        bm = fmaxf(bm, s[r]);
+    float x, y;
+    halves(bm, x, y);
+    return fmaxf(x, y) * scale_log2;  // raw scores: the scale is positive
+}
+
+// Weights 2^(s*scale_log2 - m) of one S^T block as the P^T operands of its
+// two 16-key halves (pop[ks]: keys 16ks + {4h..4h+3, 8+4h..8+4h+3} of this
+// lane's row, the k order of the V^T operand); returns their sum (this lane).
+__device__ __forceinline__ float block_weights(const f32x16_t &s, float m, u32x4_t (&pop)[2],
+                                               float scale_log2)
+{
+    const float neg_m = -m;
+    float sum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        uint32_t pw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float p0 = exp2_fast(fmaf(s[8 * ks + 2 * j], scale_log2, neg_m));
+            const float p1 = exp2_fast(fmaf(s[8 * ks + 2 * j + 1], scale_log2, neg_m));
+            pw[j] = pack_bf16(p0, p1);
+            sum = add_pair(pw[j], sum);
+        }
+        pop[ks] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
+    }
+    return sum;
+}
+
+// LDS position of block j: stage (j / BPT) % S, key offset 32 (j % BPT).
+template <int D>
+__device__ __forceinline__ const uint16_t *k_block(const Smem<D> &sm, int j)
+{
+    return sm.k[(j / Cfg<D>::kBPT) % kStages] + kKB * (j % Cfg<D>::kBPT) * D;
+}
+
+template <int D>
+__device__ __forceinline__ const uint16_t *v_block(const Smem<D> &sm, int j)
+{
+    return sm.v[(j / Cfg<D>::kBPT) % kStages] + kKB * (j % Cfg<D>::kBPT) * D;
+}
+
+// Weights of block b for row block rb, relative to its reference maximum
+// (set from the block itself when kFirst).  If the weight sum comes too close
+// to overflow (rare), the reference is raised: the accumulators and the row
+// sum are rescaled (this step's P*V for rb, relative to the old reference,
+// was issued before) and S^T is recomputed from the K block, which is still
+// resident, to redo the weights.
+template <int D, bool kMasked, bool kFirst>
+__device__ __forceinline__ void row_block_weights(WaveState<D> &w, int rb, f32x16_t s,
+                                                  const uint16_t *kt, int thr, float scale_log2,
+                                                  int lane)
+{
+    if (kMasked)
+        apply_mask(s, thr);
+    // the first block sets the reference exactly; key 0 is visible to every
+    // row, so it is finite from then on
+    if (kFirst)
+        w.m[rb] = block_max(s, scale_log2);
+    u32x4_t pnew[2];
+    float psum = block_weights(s, w.m[rb], pnew, scale_log2);
+    if (!kFirst && __any(!(psum <= kWeightSumLimit))) {
+        u32x4_t kop[D / 16];
+        read_k<D>(kop, kt, 0, lane);
+        f32x16_t sr = qk_mfma<D>(w.qop[rb], kop);
+        if (kMasked)
+            apply_mask(sr, thr);
+        const float m_new = fmaxf(w.m[rb], block_max(sr, scale_log2));
+        const float alpha = exp2_fast(w.m[rb] - m_new);
+        w.lsum[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            w.acc[rb][db] *= alpha;
+        w.m[rb] = m_new;
+        psum = block_weights(sr, m_new, pnew, scale_log2);
+    }
+    w.lsum[rb] += psum;
+    w.pop[rb][0] = pnew[0];
+    w.pop[rb][1] = pnew[1];
+}
+
+// Step b (1 <= b < nb) of one wave: for each row block, S^T of block b, P*V of
+// block b-1 (whose weights w.pop holds) and the weights of block b.  The K and
+// V^T operands are read once for all row blocks; the weights of one row block
+// overlap the matrix instructions of the next.
+template <int D, bool kMasked>
+__device__ __forceinline__ void full_step(WaveState<D> &w, const Smem<D> &sm, int b, int thr0,
+                                          float scale_log2, int lane)
+{
+    constexpr int NRB = Cfg<D>::kNRB;
+    const uint16_t *kt = k_block<D>(sm, b);
+    u32x4_t kop[D / 16], vop[D / 32][2];
+    read_k<D>(kop, kt, 0, lane);
+    read_v<D>(vop, v_block<D>(sm, b - 1), 0, lane);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        const f32x16_t s = qk_mfma<D>(w.qop[rb], kop);
+        pv_mfma<D>(w.acc[rb], vop, w.pop[rb]);
+        row_block_weights<D, kMasked, false>(w, rb, s, kt, thr0 + 32 * rb, scale_log2, lane);
+    }
+}
+
+// Step 0: S^T of block 0 and its weights, which set the reference maxima.
+template <int D, bool kMasked>
+__device__ __forceinline__ void first_step(WaveState<D> &w, const Smem<D> &sm, int thr0,
+                                           float scale_log2, int lane)
+{
+    const uint16_t *kt = k_block<D>(sm, 0);
+    u32x4_t kop[D / 16];
+    read_k<D>(kop, kt, 0, lane);
+#pragma unroll
+    for (int rb = 0; rb < Cfg<D>::kNRB; ++rb)
+        row_block_weights<D, kMasked, true>(w, rb, qk_mfma<D>(w.qop[rb], kop), kt, thr0 + 32 * rb,
+                                            scale_log2, lane);
+}
+
+// Step nb: P*V of the wave's last block.
+template <int D>
+__device__ __forceinline__ void last_step(WaveState<D> &w, const Smem<D> &sm, int nb, int lane)
+{
+    u32x4_t vop[D / 32][2];
+    read_v<D>(vop, v_block<D>(sm, nb - 1), 0, lane);
+#pragma unroll
+    for (int rb = 0; rb < Cfg<D>::kNRB; ++rb)
+        pv_mfma<D>(w.acc[rb], vop, w.pop[rb]);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
+{
+    using C = Cfg<D>;
+    constexpr int NRB = C::kNRB;
     // workgroup -> (sequence, KV head, query head in group, query tile): all
     // workgroups of one (sequence, KV head) land on one XCD (workgroups are
     // dispatched to XCDs round-robin), heaviest query tiles first
@@ -252,91 +475,139 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16(PrefillArgs a)
 
     const int q0 = a.cu_seqlens_q[b];
     const int q_len = a.cu_seqlens_q[b + 1] - q0;
-    const int row0 = qt * kBM;
+    const int row0 = qt * C::kBM;
     if (row0 >= q_len)
         return;  // uniform over the workgroup
     const int L = a.seq_lens[b];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int r32 = lane & 31, half = lane >> 5;
     const int shift = L - q_len;  // position of query row i is shift + i
 
-    RowState<D> rs;
-    const int row = row0 + 32 * wave + r32;
-    rs.pos = shift + row;
-    rs.m = kNegInf;
-    rs.lsum = 0.f;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-        rs.acc[db] = f32x16_t{};
-    if (row < q_len) {
-        const uint16_t *qrow = a.q + ((size_t)(q0 + row) * a.num_q_heads + h) * D;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            rs.qop[kk] = *(const u32x4_t *)(qrow + 16 * kk + 8 * half);
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            rs.qop[kk] = u32x4_t{0, 0, 0, 0};
-    }
+    // this wave's rows: row_w + 32 rb + r32
+    const int row_w = row0 + 32 * NRB * wave;
 
-    // keys needed by the workgroup and by this wave
-    const int last_row = min(row0 + kBM, q_len) - 1;
+    // keys needed by the workgroup (tiles) and by this wave (blocks)
+    const int last_row = min(row0 + C::kBM, q_len) - 1;
     const int kv_end = min(shift + last_row + 1, L);
-    const int wave_first = row0 + 32 * wave;
-    const int wave_last = min(wave_first + 31, q_len - 1);
-    const int wave_kv_end = wave_first < q_len ? min(shift + wave_last + 1, L) : 0;
-    const int wave_pos_first = shift + wave_first;
+    const int ntiles = (kv_end + C::kBN - 1) / C::kBN;
+    const int wave_last = min(row_w + 32 * NRB - 1, q_len - 1);
+    const int nb = row_w < q_len ? (min(shift + wave_last + 1, L) + kKB - 1) / kKB : 0;
+    const int wpf = shift + row_w;  // position of the wave's first row
 
-    __shared__ Tile<D> tiles[2];
+    __shared__ Smem<D> sm;
     const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
-    const int ntiles = (kv_end + kBN - 1) / kBN;
-    TileRegs<D> regs;
-    load_tile<D>(regs, a, bt, 0, L, g);
-    store_tile<D>(tiles[0], regs);
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-        const int kv0 = it * kBN;
-        if (it + 1 < ntiles)
-            load_tile<D>(regs, a, bt, kv0 + kBN, L, g);
-        if (kv0 < wave_kv_end) {
-            const Tile<D> &t = tiles[it & 1];
-            if (kv0 + kBN - 1 > wave_pos_first || kv0 + kBN > L)
-                compute_tile<D, true>(rs, t, kv0, L, a.scale_log2, lane);
-            else
-                compute_tile<D, false>(rs, t, kv0, L, a.scale_log2, lane);
-        }
-        if (it + 1 < ntiles)
-            store_tile<D>(tiles[(it + 1) & 1], regs);
-        __syncthreads();
-    }
+    const int last_page = (L - 1) >> 4;
+    const size_t head_off = (size_t)g * 16 * D;
 
-    const float sink2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
-    const float lsum = rs.lsum + __shfl_xor(rs.lsum, 32, 64);
-    const float M = fmaxf(rs.m, sink2);
-    float scale = 0.f;
-    if (M != kNegInf) {
-        const float f = rs.m == kNegInf ? 0.f : exp2_fast(rs.m - M);
-        const float den = lsum * f + (sink2 == kNegInf ? 0.f : exp2_fast(sink2 - M));
-        scale = den > 0.f ? f / den : 0.f;
-    }
-    if (row < q_len) {
-        uint16_t *orow = a.out + ((size_t)(q0 + row) * a.num_q_heads + h) * D;
+    // tiles 0 .. S-3 in flight before the loop; tile t + S - 2 is issued at
+    // the start of tile t, into the stage tile t - 2 used
+    const LoadLanes<D> ll = load_lanes<D>(wave, lane, L);
+#pragma unroll
+    for (int t = 0; t < kStages - 2; ++t)
+        if (t < ntiles)
+            load_tile<D>(sm, a, bt, t, L, last_page, head_off, wave, ll);
+
+    // Q while the first tiles load; one wait covers both (the compiler then
+    // knows the Q registers are ready and adds no waits inside the loops)
+    WaveState<D> w;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        const int row = row_w + 32 * rb + r32;
+        w.m[rb] = kNegInf;
+        w.lsum[rb] = 0.f;
+        w.pop[rb][0] = w.pop[rb][1] = u32x4_t{0, 0, 0, 0};
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
+            w.acc[rb][db] = f32x16_t{};
+        const uint16_t *qrow = a.q + ((size_t)(q0 + min(row, q_len - 1)) * a.num_q_heads + h) * D;
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const u32x2_t w = {pack_bf16(rs.acc[db][4 * r4] * scale,
-                                             rs.acc[db][4 * r4 + 1] * scale),
-                                   pack_bf16(rs.acc[db][4 * r4 + 2] * scale,
-                                             rs.acc[db][4 * r4 + 3] * scale)};
-                *(u32x2_t *)(orow + 32 * db + 8 * r4 + 4 * half) = w;
+        for (int kk = 0; kk < D / 16; ++kk)
+            w.qop[rb][kk] = row < q_len ? *(const u32x4_t *)(qrow + 16 * kk + 8 * half)
+                                        : u32x4_t{0, 0, 0, 0};
+    }
+
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+
+    // Step b (< nb): S^T and weights of block b, P*V of block b - 1; step nb:
+    // P*V of the last block.  Every step that starts a tile first waits for
+    // that tile and issues the one two ahead; waves with fewer blocks keep
+    // doing so after their last step.  The first step, the unmasked steps,
+    // the masked steps near the diagonal and the last step run in separate
+    // loops so that each loop body is one straight path.
+    const int nsteps = C::kBPT * ntiles + 1;
+    auto tile_start = [&](int step) {
+        if (step % C::kBPT == 0) {
+            const int t = step / C::kBPT;
+            if (t < ntiles) {
+                // tile t has landed (tile t + 1 may still be in flight), and
+                // every wave is past its last read of tile t - 2
+                wait_loads_and_sync(t + 1 >= ntiles);
+                if (t + kStages - 2 < ntiles)
+                    load_tile<D>(sm, a, bt, t + kStages - 2, L, last_page, head_off, wave, ll);
             }
+        }
+    };
+    // blocks from bm on hold keys past the wave's first row: causal mask
+    const int bm = (wpf + 1) / kKB;
+    const int thr = wpf + r32 - 4 * half;  // minus the block start
+    tile_start(0);
+    if (nb > 0) {
+        if (bm == 0)
+            first_step<D, true>(w, sm, thr, a.scale_log2, lane);
+        else
+            first_step<D, false>(w, sm, thr, a.scale_log2, lane);
+    }
+    int step = 1;
+    for (const int end = min(bm, nb); step < end; ++step) {
+        tile_start(step);
+        full_step<D, false>(w, sm, step, 0, a.scale_log2, lane);
+    }
+    for (; step < nb; ++step) {
+        tile_start(step);
+        full_step<D, true>(w, sm, step, thr - kKB * step, a.scale_log2, lane);
+    }
+    if (nb > 0) {
+        tile_start(nb);
+        last_step<D>(w, sm, nb, lane);
+        step = nb + 1;
+    }
+    for (; step < nsteps; ++step)
+        tile_start(step);
+
+    const float sink2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        const int row = row_w + 32 * rb + r32;
+        float lx, ly;
+        halves(w.lsum[rb], lx, ly);
+        const float lsum = lx + ly;
+        const float M = fmaxf(w.m[rb], sink2);
+        float scale = 0.f;
+        if (M != kNegInf) {
+            const float f = w.m[rb] == kNegInf ? 0.f : exp2_fast(w.m[rb] - M);
+            const float den = lsum * f + (sink2 == kNegInf ? 0.f : exp2_fast(sink2 - M));
+            scale = den > 0.f ? f / den : 0.f;
+        }
+        if (row < q_len) {
+            uint16_t *orow = a.out + ((size_t)(q0 + row) * a.num_q_heads + h) * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const f32x16_t &o = w.acc[rb][db];
+                    const u32x2_t v = {pack_bf16(o[4 * r4] * scale, o[4 * r4 + 1] * scale),
+                                       pack_bf16(o[4 * r4 + 2] * scale, o[4 * r4 + 3] * scale)};
+                    *(u32x2_t *)(orow + 32 * db + 8 * r4 + 4 * half) = v;
+                }
+        }
     }
 }
 
 template <int D>
 hipError_t launch_d(const PrefillLaunch &p)
 {
+    using C = Cfg<D>;
     PrefillArgs a;
     a.q = (const uint16_t *)p.q;
     a.k_cache = (const uint16_t *)p.k_cache;
@@ -351,7 +622,7 @@ hipError_t launch_d(const PrefillLaunch &p)
     a.num_kv_heads = p.num_kv_heads;
     a.group = p.num_q_heads / p.num_kv_heads;
     a.max_pages = p.max_pages_per_seq;
-    a.num_q_tiles = (p.max_q_len + kBM - 1) / kBM;
+    a.num_q_tiles = (p.max_q_len + C::kBM - 1) / C::kBM;
     const int groups = p.num_seqs * p.num_kv_heads;
     a.xcd_groups = groups / 8 * 8;
     a.scale_log2 = p.scale * kLog2e;
