@@ -28,11 +28,12 @@
 //
 // K/V reach LDS by direct global-to-LDS loads (no registers): tiles of BN
 // keys (64 at d = 64, 32 at d = 128; 16 KiB of K+V either way) rotate through
-// four LDS stages, issued two tiles ahead.  Each 1 KiB load instruction
-// covers whole key rows of one 16-token page; lanes fetch the 16-byte chunk
-// that belongs in their slot of the XOR-swizzled row, so the transposed and
-// column reads above are free of bank conflicts.  Rows past the sequence are
-// fetched as copies of its last row (finite), and the causal mask hides them.
+// S LDS stages (4 at d = 64, 5 at d = 128), issued two tiles ahead.  Each
+// 1 KiB load instruction covers whole key rows of one 16-token page; lanes
+// fetch the 16-byte chunk that belongs in their slot of the XOR-swizzled row,
+// so the transposed and column reads above are free of bank conflicts.  Rows
+// past the sequence are fetched as copies of its last row (finite), and the
+// causal mask hides them.
 //
 // Softmax reference.  A row's reference maximum m is set exactly from its
 // first block and then kept: weights 2^(s - m) may exceed 1, which bf16 and
@@ -42,10 +43,12 @@
 // raised, the accumulators rescaled and the block's weights recomputed.  The
 // final division uses the same m, so the result does not depend on it.
 //
-// Per step b a wave issues S^T of block b and P*V of block b-1 (16 matrix
-// instructions at d = 64) and computes the weights of block b; the weights
-// of block b-1 feed this step's P*V, so the exponentials overlap the matrix
-// stream of the same wave.
+// Pipeline.  Step b of a wave issues S^T of block b+1 and P*V of block b-1 on
+// the matrix cores (16 instructions at d = 64) while the vector ALU computes
+// the weights of block b from the S^T of the previous step.  No instruction
+// of a step waits for another of the same step, so one wave keeps both pipes
+// busy.  At the step that reads the first block of tile T, the wave waits for
+// tile T, meets the other waves and issues tile T+2.
 #include "common.h"
 #include "kernels.h"
 
@@ -55,7 +58,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kKB = 32;          // keys per block: one 32x32 S^T tile
-constexpr int kStages = 4;       // LDS stages; tiles are fetched kStages - 2 ahead
 constexpr int kLoadsPerTile = 4; // 1 KiB direct loads per wave per tile (2 K + 2 V)
 // A block whose weight sum exceeds this (per lane) triggers an exact rescale.
 constexpr float kWeightSumLimit = 18446744073709551616.0f;  // 2^64
@@ -68,6 +70,11 @@ struct Cfg {
     static constexpr int kBPT = kBN / kKB;              // blocks per tile
     static constexpr int kRowsPerLoad = 1024 / (2 * D); // key rows per 1 KiB load
     static constexpr int kTileElems = kBN * D;          // bf16 elements of K (or V) per tile
+    // LDS stages: a step reads K two blocks ahead of the V it reads, and tile
+    // T+2 is issued at the step that starts reading tile T, so the stage it
+    // overwrites must have been read for the last time before that step.
+    static constexpr int kStages = kBPT == 2 ? 4 : 5;
+    static constexpr int kLdsBytes = 2 * kStages * kTileElems * 2;
 };
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -107,12 +114,12 @@ __device__ __forceinline__ void halves(float v, float &x, float &y)
     y = __uint_as_float(r[1]);
 }
 
-// Wait until at most n of this wave's direct loads are still in flight (the
-// older ones have landed in LDS), then meet the other waves.  The loads are
+// Wait until this wave's direct loads of tile T have landed in LDS (those of
+// tile T+1, issued after them, may still be in flight: kLoadsPerTile = 4
+// loads), then meet the other waves.  The loads are
 // not tracked by the compiler's own wait insertion, hence the explicit wait.
 __device__ __forceinline__ void wait_loads_and_sync(bool all_landed)
 {
-    static_assert(kLoadsPerTile * (kStages - 3) == 4, "wait count");
     if (all_landed)
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else
@@ -161,10 +168,18 @@ struct Swz {
     }
 };
 
+// LDS: the K stages, then the V stages (dynamic shared memory, kLdsBytes).
 template <int D>
 struct Smem {
-    uint16_t k[kStages][Cfg<D>::kTileElems];
-    uint16_t v[kStages][Cfg<D>::kTileElems];
+    uint16_t *base;
+    __device__ __forceinline__ uint16_t *k(int stage) const
+    {
+        return base + stage * Cfg<D>::kTileElems;
+    }
+    __device__ __forceinline__ uint16_t *v(int stage) const
+    {
+        return base + (Cfg<D>::kStages + stage) * Cfg<D>::kTileElems;
+    }
 };
 
 // Per-lane parts of this wave's direct loads (constant over tiles).  The wave
@@ -174,31 +189,25 @@ struct Smem {
 // R*j + l / (d/8) of the swizzled tile.
 template <int D>
 struct LoadLanes {
-    int key[2];       // key of this lane's row within the tile, per chunk
-    int koff[2];      // element offset within the page-head slab: row and K chunk
-    int voff[2];      // the same for V
-    int tail_koff[2]; // offsets when the row is past the sequence: its last row
-    int tail_voff[2];
+    int key[2];   // key of this lane's row within the tile, per chunk
+    int kc[2];    // K chunk (elements) within the row
+    int vc[2];    // V chunk (elements) within the row
 };
 
 template <int D>
-__device__ __forceinline__ LoadLanes<D> load_lanes(int wave, int lane, int L)
+__device__ __forceinline__ LoadLanes<D> load_lanes(int wave, int lane)
 {
     using C = Cfg<D>;
     constexpr int kChunks = D / 8;  // 16-byte chunks per key row
     LoadLanes<D> ll;
-    const int last_row = (L - 1) & 15;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int j = wave + kWaves * i;
         const int key = C::kRowsPerLoad * j + lane / kChunks;
         const int slot = lane % kChunks;
-        const int kc = 8 * (slot ^ Swz<D>::ksw(key)), vc = 8 * (slot ^ (Swz<D>::vsw(key) >> 1));
         ll.key[i] = key;
-        ll.koff[i] = (key & 15) * D + kc;
-        ll.voff[i] = (key & 15) * D + vc;
-        ll.tail_koff[i] = last_row * D + kc;
-        ll.tail_voff[i] = last_row * D + vc;
+        ll.kc[i] = 8 * (slot ^ Swz<D>::ksw(key));
+        ll.vc[i] = 8 * (slot ^ (Swz<D>::vsw(key) >> 1));
     }
     return ll;
 }
@@ -219,26 +228,45 @@ __device__ __forceinline__ void dma16(const uint16_t *gbase, uint32_t voff, cons
                  : "memory");
 }
 
+// Page ids of this wave's two load chunks of tile t (chunk j = wave + 4i
+// starts at key t*BN + R*j).  Page indices past the sequence's last page are
+// clamped to it.  Read one tile before the loads that use them, so that the
+// scalar-load latency stays off the tile start.
+struct ChunkPages {
+    int p[2];
+};
+
+template <int D>
+__device__ __forceinline__ ChunkPages chunk_pages(const int32_t *__restrict__ bt, int t,
+                                                  int last_page, int wave)
+{
+    using C = Cfg<D>;
+    ChunkPages cp;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        cp.p[i] = load_scalar(
+            bt, min((t * C::kBN + C::kRowsPerLoad * (wave + kWaves * i)) >> 4, last_page));
+    return cp;
+}
+
 // Issue this wave's direct loads of tile t (keys t*BN ..) into stage t % S.
 // Rows past the sequence repeat its last row (finite; the causal mask hides
 // them); their page index is clamped to the last page, which holds that row.
 template <int D>
-__device__ __forceinline__ void load_tile(Smem<D> &sm, const PrefillArgs &a,
-                                          const int32_t *__restrict__ bt, int t, int L,
-                                          int last_page, size_t head_off, int wave,
+__device__ __forceinline__ void load_tile(const Smem<D> &sm, const PrefillArgs &a, const ChunkPages &cp,
+                                          int t, int L, size_t head_off, int wave,
                                           const LoadLanes<D> &ll)
 {
     using C = Cfg<D>;
     const int kv0 = t * C::kBN;
-    const int stage = t % kStages;
+    const int stage = t % C::kStages;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int j = wave + kWaves * i;
-        const int page = load_scalar(bt, min((kv0 + C::kRowsPerLoad * j) >> 4, last_page));
-        const size_t slab = (size_t)page * a.num_kv_heads * 16 * D + head_off;
-        const bool in = kv0 + ll.key[i] < L;
-        dma16(a.k_cache + slab, 2 * (in ? ll.koff[i] : ll.tail_koff[i]), &sm.k[stage][512 * j]);
-        dma16(a.v_cache + slab, 2 * (in ? ll.voff[i] : ll.tail_voff[i]), &sm.v[stage][512 * j]);
+        const size_t slab = (size_t)cp.p[i] * a.num_kv_heads * 16 * D + head_off;
+        const int row = kv0 + ll.key[i] < L ? (ll.key[i] & 15) : ((L - 1) & 15);
+        dma16(a.k_cache + slab, 2 * (row * D + ll.kc[i]), sm.k(stage) + 512 * j);
+        dma16(a.v_cache + slab, 2 * (row * D + ll.vc[i]), sm.v(stage) + 512 * j);
     }
 }
 
@@ -355,87 +383,82 @@ __device__ __forceinline__ float block_weights(const f32x16_t &s, float m, u32x4
 template <int D>
 __device__ __forceinline__ const uint16_t *k_block(const Smem<D> &sm, int j)
 {
-    return sm.k[(j / Cfg<D>::kBPT) % kStages] + kKB * (j % Cfg<D>::kBPT) * D;
+    using C = Cfg<D>;
+    return sm.k((j / C::kBPT) % C::kStages) + kKB * (j % C::kBPT) * D;
 }
 
 template <int D>
 __device__ __forceinline__ const uint16_t *v_block(const Smem<D> &sm, int j)
 {
-    return sm.v[(j / Cfg<D>::kBPT) % kStages] + kKB * (j % Cfg<D>::kBPT) * D;
+    using C = Cfg<D>;
+    return sm.v((j / C::kBPT) % C::kStages) + kKB * (j % C::kBPT) * D;
 }
 
-// Weights of block b for row block rb, relative to its reference maximum
-// (set from the block itself when kFirst).  If the weight sum comes too close
-// to overflow (rare), the reference is raised: the accumulators and the row
-// sum are rescaled (this step's P*V for rb, relative to the old reference,
-// was issued before) and S^T is recomputed from the K block, which is still
-// resident, to redo the weights.
-template <int D, bool kMasked, bool kFirst>
-__device__ __forceinline__ void row_block_weights(WaveState<D> &w, int rb, f32x16_t s,
-                                                  const uint16_t *kt, int thr, float scale_log2,
-                                                  int lane)
+// S^T of one block for every row block, kk-interleaved so that the row
+// blocks' dependent chains overlap in the matrix pipe.
+template <int D>
+__device__ __forceinline__ void qk_all(f32x16_t (&s)[Cfg<D>::kNRB], const WaveState<D> &w,
+                                       const u32x4_t (&kop)[D / 16])
 {
-    if (kMasked)
-        apply_mask(s, thr);
-    // the first block sets the reference exactly; key 0 is visible to every
-    // row, so it is finite from then on
-    if (kFirst)
-        w.m[rb] = block_max(s, scale_log2);
-    u32x4_t pnew[2];
-    float psum = block_weights(s, w.m[rb], pnew, scale_log2);
-    if (!kFirst && __any(!(psum <= kWeightSumLimit))) {
-        u32x4_t kop[D / 16];
-        read_k<D>(kop, kt, 0, lane);
-        f32x16_t sr = qk_mfma<D>(w.qop[rb], kop);
-        if (kMasked)
-            apply_mask(sr, thr);
-        const float m_new = fmaxf(w.m[rb], block_max(sr, scale_log2));
-        const float alpha = exp2_fast(w.m[rb] - m_new);
-        w.lsum[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-            w.acc[rb][db] *= alpha;
-        w.m[rb] = m_new;
-        psum = block_weights(sr, m_new, pnew, scale_log2);
-    }
-    w.lsum[rb] += psum;
-    w.pop[rb][0] = pnew[0];
-    w.pop[rb][1] = pnew[1];
-}
-
-// Step b (1 <= b < nb) of one wave: for each row block, S^T of block b, P*V of
-// block b-1 (whose weights w.pop holds) and the weights of block b.  The K and
-// V^T operands are read once for all row blocks; the weights of one row block
-// overlap the matrix instructions of the next.
-template <int D, bool kMasked>
-__device__ __forceinline__ void full_step(WaveState<D> &w, const Smem<D> &sm, int b, int thr0,
-                                          float scale_log2, int lane)
-{
-    constexpr int NRB = Cfg<D>::kNRB;
-    const uint16_t *kt = k_block<D>(sm, b);
-    u32x4_t kop[D / 16], vop[D / 32][2];
-    read_k<D>(kop, kt, 0, lane);
-    read_v<D>(vop, v_block<D>(sm, b - 1), 0, lane);
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-        const f32x16_t s = qk_mfma<D>(w.qop[rb], kop);
-        pv_mfma<D>(w.acc[rb], vop, w.pop[rb]);
-        row_block_weights<D, kMasked, false>(w, rb, s, kt, thr0 + 32 * rb, scale_log2, lane);
-    }
-}
-
-// Step 0: S^T of block 0 and its weights, which set the reference maxima.
-template <int D, bool kMasked>
-__device__ __forceinline__ void first_step(WaveState<D> &w, const Smem<D> &sm, int thr0,
-                                           float scale_log2, int lane)
-{
-    const uint16_t *kt = k_block<D>(sm, 0);
-    u32x4_t kop[D / 16];
-    read_k<D>(kop, kt, 0, lane);
 #pragma unroll
     for (int rb = 0; rb < Cfg<D>::kNRB; ++rb)
-        row_block_weights<D, kMasked, true>(w, rb, qk_mfma<D>(w.qop[rb], kop), kt, thr0 + 32 * rb,
-                                            scale_log2, lane);
+        s[rb] = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+        for (int rb = 0; rb < Cfg<D>::kNRB; ++rb)
+            s[rb] = mfma32x32x16(kop[kk], w.qop[rb][kk], s[rb]);
+}
+
+// Step b of one wave.  kQK: S^T of block b+1 into s_next.  kPV: P*V of block
+// b-1 with the weights in w.pop.  Always: the weights of block b from s_cur,
+// relative to the reference maxima (set from the block itself when kFirst,
+// masked when kMasked).  A weight sum too close to overflow (or not finite)
+// marks the lane in `bad`; such a wave is recomputed exactly after the loop
+// (exact_rows), so the loop itself has no rescale branch.
+template <int D, bool kQK, bool kPV, bool kMasked, bool kFirst>
+__device__ __forceinline__ void step(WaveState<D> &w, const Smem<D> &sm, int b,
+                                     f32x16_t (&s_cur)[Cfg<D>::kNRB], int thr0, float scale_log2,
+                                     int lane, bool &bad)
+{
+    constexpr int NRB = Cfg<D>::kNRB;
+    u32x4_t kop[D / 16], vop[D / 32][2];
+    if (kQK)
+        read_k<D>(kop, k_block<D>(sm, b + 1), 0, lane);
+    if (kPV)
+        read_v<D>(vop, v_block<D>(sm, b - 1), 0, lane);
+    f32x16_t s_next[NRB];
+    if (kQK)
+        qk_all<D>(s_next, w, kop);
+    if (kPV) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+            pv_mfma<D>(w.acc[rb], vop, w.pop[rb]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        if (kMasked)
+            apply_mask(s_cur[rb], thr0 + 32 * rb);
+        // the first block sets the reference exactly; key 0 is visible to
+        // every row, so it is finite from then on
+        if (kFirst)
+            w.m[rb] = block_max(s_cur[rb], scale_log2);
+        const float psum = block_weights(s_cur[rb], w.m[rb], w.pop[rb], scale_log2);
+        bad = bad || !(psum <= kWeightSumLimit);
+        w.lsum[rb] += psum;
+        if (kQK)
+            s_cur[rb] = s_next[rb];
+    }
+    if (kQK && kPV) {
+        // vector work first while the LDS reads land, then one matrix
+        // instruction per eight vector ones
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 8 * NRB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+    }
 }
 
 // Step nb: P*V of the wave's last block.
@@ -447,6 +470,71 @@ __device__ __forceinline__ void last_step(WaveState<D> &w, const Smem<D> &sm, in
 #pragma unroll
     for (int rb = 0; rb < Cfg<D>::kNRB; ++rb)
         pv_mfma<D>(w.acc[rb], vop, w.pop[rb]);
+}
+
+// Exact recompute of a wave's rows (rare: some weight sum came too close to
+// overflow against the reference taken from the first block).  Each block's
+// exact row maximum is taken first and the running state rescaled to it, as
+// in the plain online softmax.  K and V come straight from the paged cache
+// into this wave's own quarter of the LDS (the workgroup has met after its
+// pipelined loop, so nothing else reads it).
+template <int D>
+__device__ void exact_rows(WaveState<D> &w, uint16_t *lds_wave, const PrefillArgs &a,
+                           const int32_t *__restrict__ bt, int L, size_t head_off, int nb,
+                           int wpf, int thr, int lane)
+{
+    constexpr int NRB = Cfg<D>::kNRB;
+    constexpr int kChunks = D / 8;            // 16-byte chunks per key row
+    constexpr int kPer = kKB * kChunks / 64;  // chunks per lane per block
+    uint16_t *kt = lds_wave;
+    uint16_t *vt = lds_wave + kKB * D;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        w.m[rb] = kNegInf;
+        w.lsum[rb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            w.acc[rb][db] = f32x16_t{};
+    }
+    for (int blk = 0; blk < nb; ++blk) {
+        const int k0 = kKB * blk;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = lane + 64 * i;
+            const int key = c / kChunks, chunk = c % kChunks;
+            const int tok = min(k0 + key, L - 1);  // past the sequence: its last row
+            const int page = bt[tok >> 4];
+            const size_t off = (size_t)page * a.num_kv_heads * 16 * D + head_off +
+                               (size_t)(tok & 15) * D + 8 * chunk;
+            const u32x4_t kv = *(const u32x4_t *)(a.k_cache + off);
+            const u32x4_t vv = *(const u32x4_t *)(a.v_cache + off);
+            *(u32x4_t *)&kt[Swz<D>::k_at(key, chunk)] = kv;
+            *(u32x4_t *)&vt[Swz<D>::v_at(key, 2 * chunk)] = vv;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        u32x4_t kop[D / 16], vop[D / 32][2];
+        read_k<D>(kop, kt, 0, lane);
+        read_v<D>(vop, vt, 0, lane);
+        const bool masked = k0 + kKB - 1 > wpf;
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            f32x16_t s = qk_mfma<D>(w.qop[rb], kop);
+            if (masked)
+                apply_mask(s, thr - k0 + 32 * rb);
+            const float m_new = fmaxf(w.m[rb], block_max(s, a.scale_log2));
+            const float alpha = exp2_fast(w.m[rb] - m_new);  // 0 while m is -inf
+            w.lsum[rb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                w.acc[rb][db] *= alpha;
+            w.m[rb] = m_new;
+            w.lsum[rb] += block_weights(s, m_new, w.pop[rb], a.scale_log2);
+            pv_mfma<D>(w.acc[rb], vop, w.pop[rb]);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block's writes
+        __builtin_amdgcn_wave_barrier();
+    }
 }
 
 template <int D>
@@ -495,18 +583,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     const int nb = row_w < q_len ? (min(shift + wave_last + 1, L) + kKB - 1) / kKB : 0;
     const int wpf = shift + row_w;  // position of the wave's first row
 
-    __shared__ Smem<D> sm;
+    extern __shared__ __align__(16) uint16_t lds[];
+    const Smem<D> sm{lds};
     const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
     const int last_page = (L - 1) >> 4;
     const size_t head_off = (size_t)g * 16 * D;
 
-    // tiles 0 .. S-3 in flight before the loop; tile t + S - 2 is issued at
-    // the start of tile t, into the stage tile t - 2 used
-    const LoadLanes<D> ll = load_lanes<D>(wave, lane, L);
+    // tiles 0 and 1 in flight before the loop; tile T+2 is issued when the
+    // wave starts reading tile T
+    const LoadLanes<D> ll = load_lanes<D>(wave, lane);
 #pragma unroll
-    for (int t = 0; t < kStages - 2; ++t)
+    for (int t = 0; t < 2; ++t)
         if (t < ntiles)
-            load_tile<D>(sm, a, bt, t, L, last_page, head_off, wave, ll);
+            load_tile<D>(sm, a, chunk_pages<D>(bt, t, last_page, wave), t, L, head_off, wave, ll);
+    ChunkPages next_pages = chunk_pages<D>(bt, 2, last_page, wave);
 
     // Q while the first tiles load; one wait covers both (the compiler then
     // knows the Q registers are ready and adds no waits inside the loops)
@@ -529,51 +619,80 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
 
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
-    // Step b (< nb): S^T and weights of block b, P*V of block b - 1; step nb:
-    // P*V of the last block.  Every step that starts a tile first waits for
-    // that tile and issues the one two ahead; waves with fewer blocks keep
-    // doing so after their last step.  The first step, the unmasked steps,
-    // the masked steps near the diagonal and the last step run in separate
-    // loops so that each loop body is one straight path.
-    const int nsteps = C::kBPT * ntiles + 1;
+    // Step j reads K of block j+1 (tile (j+1)/BPT) and V of block j-1.  When
+    // block j+1 starts tile T, the wave first waits for tile T, meets the
+    // other waves and issues tile T+2 (step -1 does this for tile 0).  Waves
+    // with fewer blocks keep doing so after their last step.  The first
+    // step, the unmasked steps, the masked steps near the diagonal and the
+    // last two steps run in separate loops, so each loop body is one
+    // straight path.
     auto tile_start = [&](int step) {
-        if (step % C::kBPT == 0) {
-            const int t = step / C::kBPT;
+        if ((step + 1) % C::kBPT == 0) {
+            const int t = (step + 1) / C::kBPT;
             if (t < ntiles) {
-                // tile t has landed (tile t + 1 may still be in flight), and
-                // every wave is past its last read of tile t - 2
                 wait_loads_and_sync(t + 1 >= ntiles);
-                if (t + kStages - 2 < ntiles)
-                    load_tile<D>(sm, a, bt, t + kStages - 2, L, last_page, head_off, wave, ll);
+                if (t + 2 < ntiles) {
+                    load_tile<D>(sm, a, next_pages, t + 2, L, head_off, wave, ll);
+                    next_pages = chunk_pages<D>(bt, t + 3, last_page, wave);
+                }
             }
         }
     };
     // blocks from bm on hold keys past the wave's first row: causal mask
     const int bm = (wpf + 1) / kKB;
     const int thr = wpf + r32 - 4 * half;  // minus the block start
-    tile_start(0);
+    const float sl2 = a.scale_log2;
+    f32x16_t s_cur[NRB];  // S^T of the block whose weights are next
+    bool bad = false;     // a weight sum of this lane came too close to overflow
+    tile_start(-1);
     if (nb > 0) {
+        u32x4_t kop[D / 16];
+        read_k<D>(kop, k_block<D>(sm, 0), 0, lane);
+        qk_all<D>(s_cur, w, kop);
+    }
+    // step 0
+    tile_start(0);
+    if (nb > 1) {
         if (bm == 0)
-            first_step<D, true>(w, sm, thr, a.scale_log2, lane);
+            step<D, true, false, true, true>(w, sm, 0, s_cur, thr, sl2, lane, bad);
         else
-            first_step<D, false>(w, sm, thr, a.scale_log2, lane);
+            step<D, true, false, false, true>(w, sm, 0, s_cur, thr, sl2, lane, bad);
+    } else if (nb == 1) {
+        if (bm == 0)
+            step<D, false, false, true, true>(w, sm, 0, s_cur, thr, sl2, lane, bad);
+        else
+            step<D, false, false, false, true>(w, sm, 0, s_cur, thr, sl2, lane, bad);
     }
-    int step = 1;
-    for (const int end = min(bm, nb); step < end; ++step) {
-        tile_start(step);
-        full_step<D, false>(w, sm, step, 0, a.scale_log2, lane);
+    // steps 1 .. nb-2: all three stages
+    int j = 1;
+    for (const int end = min(bm, nb - 1); j < end; ++j) {
+        tile_start(j);
+        step<D, true, true, false, false>(w, sm, j, s_cur, 0, sl2, lane, bad);
     }
-    for (; step < nb; ++step) {
-        tile_start(step);
-        full_step<D, true>(w, sm, step, thr - kKB * step, a.scale_log2, lane);
+    for (; j < nb - 1; ++j) {
+        tile_start(j);
+        step<D, true, true, true, false>(w, sm, j, s_cur, thr - kKB * j, sl2, lane, bad);
     }
+    // step nb-1: weights of the last block, P*V of the one before
+    if (nb > 1) {
+        tile_start(nb - 1);
+        if (nb - 1 >= bm)
+            step<D, false, true, true, false>(w, sm, nb - 1, s_cur, thr - kKB * (nb - 1), sl2,
+                                              lane, bad);
+        else
+            step<D, false, true, false, false>(w, sm, nb - 1, s_cur, 0, sl2, lane, bad);
+    }
+    // step nb: P*V of the last block
     if (nb > 0) {
         tile_start(nb);
         last_step<D>(w, sm, nb, lane);
-        step = nb + 1;
     }
-    for (; step < nsteps; ++step)
-        tile_start(step);
+    for (j = max(nb + 1, 1); j <= C::kBPT * ntiles; ++j)
+        tile_start(j);
+    __syncthreads();  // every wave is past its last read of the stages
+    if (__any(bad))
+        exact_rows<D>(w, lds + wave * (C::kLdsBytes / 2 / kWaves), a, bt, L, head_off, nb, wpf, thr,
+                      lane);
 
     const float sink2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
 #pragma unroll
@@ -629,7 +748,13 @@ hipError_t launch_d(const PrefillLaunch &p)
     const long long wgs = (long long)groups * a.group * a.num_q_tiles;
     if (wgs > 0x7fffffffLL)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(prefill_bf16<D>, dim3((unsigned)wgs), dim3(kThreads), 0, p.stream, a);
+    // more than 64 KiB of LDS (d = 128) has to be allowed once per kernel
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void *)prefill_bf16<D>, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+    if (attr != hipSuccess)
+        return attr;
+    hipLaunchKernelGGL(prefill_bf16<D>, dim3((unsigned)wgs), dim3(kThreads), C::kLdsBytes,
+                       p.stream, a);
     return hipGetLastError();
 }
 

@@ -106,6 +106,31 @@ def test_null_sinks_equal_neginf_sinks():
                        run_prefill(replace(p, sinks=None)).view(torch.int16))
 
 
+def _scale_keys(b, first_token, factor):
+    """Multiply the stored K rows of tokens >= first_token of every sequence by
+    `factor` (the oracle reads the same stored values)."""
+    k = b.k_cache.clone()
+    for s in range(b.num_seqs):
+        for t in range(first_token, int(b.seq_lens[s])):
+            page = int(b.block_table[s, t // 16])
+            k[page, :, t % 16, :] = (k[page, :, t % 16, :].float() * factor).to(k.dtype)
+    return replace(b, k_cache=k)
+
+
+@pytest.mark.parametrize("d,L,Lq", [(64, 300, 300), (64, 700, 190), (128, 400, 400)])
+def test_prefill_large_late_logits(d, L, Lq):
+    """Keys after the first 64 get logits far above every early one (std ~100
+    in natural units), beyond what weights relative to the early maximum can
+    hold: the kernel must detect it and still match the exact softmax."""
+    b = wl.small_batch(100 + d + L, "bf16", [L], [Lq], 8, 2, d)
+    b = _scale_keys(b, 64, 100.0)
+    note(f"prefill large late logits d={d} L={L} Lq={Lq}")
+    compare(run_prefill(b), oracle_full(b), "bf16", f"prefill large late logits d={d}")
+    note(f"decode large late logits d={d} L={L}")
+    dec = replace(b, cu_seqlens_q=torch.tensor([0, 1], dtype=torch.int32), q=b.q[-1:].contiguous())
+    compare(run_decode(dec), oracle_full(dec), "bf16", f"decode large late logits d={d}")
+
+
 # -------------------------------------------------------- structural checks
 
 def _permuted(b, seed):
