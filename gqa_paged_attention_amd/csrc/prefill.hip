@@ -410,7 +410,8 @@ __device__ __forceinline__ void qk_all(f32x16_t (&s)[Cfg<D>::kNRB], const WaveSt
             s[rb] = mfma32x32x16(kop[kk], w.qop[rb][kk], s[rb]);
 }
 
-// Step b of one wave.  kQK: S^T of block b+1 into s_next.  kPV: P*V of block
+// Step b of one wave.  kQK: S^T of block b+1 into s_next (the caller swaps
+// the two S^T register sets between steps).  kPV: P*V of block
 // b-1 with the weights in w.pop.  Always: the weights of block b from s_cur,
 // relative to the reference maxima (set from the block itself when kFirst,
 // masked when kMasked).  A weight sum too close to overflow (or not finite)
@@ -418,7 +419,8 @@ __device__ __forceinline__ void qk_all(f32x16_t (&s)[Cfg<D>::kNRB], const WaveSt
 // (exact_rows), so the loop itself has no rescale branch.
 template <int D, bool kQK, bool kPV, bool kMasked, bool kFirst>
 __device__ __forceinline__ void step(WaveState<D> &w, const Smem<D> &sm, int b,
-                                     f32x16_t (&s_cur)[Cfg<D>::kNRB], int thr0, float scale_log2,
+                                     f32x16_t (&s_cur)[Cfg<D>::kNRB],
+                                     f32x16_t (&s_next)[Cfg<D>::kNRB], int thr0, float scale_log2,
                                      int lane, bool &bad)
 {
     constexpr int NRB = Cfg<D>::kNRB;
@@ -427,7 +429,6 @@ __device__ __forceinline__ void step(WaveState<D> &w, const Smem<D> &sm, int b,
         read_k<D>(kop, k_block<D>(sm, b + 1), 0, lane);
     if (kPV)
         read_v<D>(vop, v_block<D>(sm, b - 1), 0, lane);
-    f32x16_t s_next[NRB];
     if (kQK)
         qk_all<D>(s_next, w, kop);
     if (kPV) {
@@ -446,8 +447,6 @@ __device__ __forceinline__ void step(WaveState<D> &w, const Smem<D> &sm, int b,
         const float psum = block_weights(s_cur[rb], w.m[rb], w.pop[rb], scale_log2);
         bad = bad || !(psum <= kWeightSumLimit);
         w.lsum[rb] += psum;
-        if (kQK)
-            s_cur[rb] = s_next[rb];
     }
     if (kQK && kPV) {
         // vector work first while the LDS reads land, then one matrix
@@ -642,45 +641,69 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     const int bm = (wpf + 1) / kKB;
     const int thr = wpf + r32 - 4 * half;  // minus the block start
     const float sl2 = a.scale_log2;
-    f32x16_t s_cur[NRB];  // S^T of the block whose weights are next
-    bool bad = false;     // a weight sum of this lane came too close to overflow
+    // S^T of the block whose weights are next, and of the one after: two
+    // register sets that trade roles every step (the steady loop is unrolled
+    // twice so that no copy is needed)
+    f32x16_t sa[NRB], sb[NRB];
+    bool bad = false;  // a weight sum of this lane came too close to overflow
     tile_start(-1);
     if (nb > 0) {
         u32x4_t kop[D / 16];
         read_k<D>(kop, k_block<D>(sm, 0), 0, lane);
-        qk_all<D>(s_cur, w, kop);
+        qk_all<D>(sa, w, kop);
     }
     // step 0
     tile_start(0);
     if (nb > 1) {
         if (bm == 0)
-            step<D, true, false, true, true>(w, sm, 0, s_cur, thr, sl2, lane, bad);
+            step<D, true, false, true, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad);
         else
-            step<D, true, false, false, true>(w, sm, 0, s_cur, thr, sl2, lane, bad);
+            step<D, true, false, false, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad);
     } else if (nb == 1) {
         if (bm == 0)
-            step<D, false, false, true, true>(w, sm, 0, s_cur, thr, sl2, lane, bad);
+            step<D, false, false, true, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad);
         else
-            step<D, false, false, false, true>(w, sm, 0, s_cur, thr, sl2, lane, bad);
+            step<D, false, false, false, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad);
     }
-    // steps 1 .. nb-2: all three stages
+    // Steps 1 .. nb-2: all three stages, in pairs (sb then sa holds the
+    // current S^T), so that no register copy is needed; step 0 left S^T of
+    // block 1 in sb and every pair leaves the next one there.  An odd count
+    // starts with one single step that moves its next S^T into sb.  The
+    // pairs that reach the diagonal run the masked variant (a block with no
+    // invisible key is unchanged by it).
     int j = 1;
-    for (const int end = min(bm, nb - 1); j < end; ++j) {
-        tile_start(j);
-        step<D, true, true, false, false>(w, sm, j, s_cur, 0, sl2, lane, bad);
+    if (nb >= 3 && (nb & 1)) {
+        tile_start(1);
+        if (bm <= 1)
+            step<D, true, true, true, false>(w, sm, 1, sb, sa, thr - kKB, sl2, lane, bad);
+        else
+            step<D, true, true, false, false>(w, sm, 1, sb, sa, 0, sl2, lane, bad);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+            sb[rb] = sa[rb];
+        j = 2;
     }
-    for (; j < nb - 1; ++j) {
+    for (; j + 1 < min(bm, nb - 1); j += 2) {
         tile_start(j);
-        step<D, true, true, true, false>(w, sm, j, s_cur, thr - kKB * j, sl2, lane, bad);
+        step<D, true, true, false, false>(w, sm, j, sb, sa, 0, sl2, lane, bad);
+        tile_start(j + 1);
+        step<D, true, true, false, false>(w, sm, j + 1, sa, sb, 0, sl2, lane, bad);
     }
-    // step nb-1: weights of the last block, P*V of the one before
+    for (; j + 1 < nb - 1; j += 2) {
+        tile_start(j);
+        step<D, true, true, true, false>(w, sm, j, sb, sa, thr - kKB * j, sl2, lane, bad);
+        tile_start(j + 1);
+        step<D, true, true, true, false>(w, sm, j + 1, sa, sb, thr - kKB * (j + 1), sl2, lane,
+                                         bad);
+    }
+    // step nb-1: weights of the last block (S^T in sb), P*V of the one before
     if (nb > 1) {
         tile_start(nb - 1);
         if (nb - 1 >= bm)
-            step<D, false, true, true, false>(w, sm, nb - 1, s_cur, thr - kKB * (nb - 1), sl2,
+            step<D, false, true, true, false>(w, sm, nb - 1, sb, sb, thr - kKB * (nb - 1), sl2,
                                               lane, bad);
         else
-            step<D, false, true, false, false>(w, sm, nb - 1, s_cur, 0, sl2, lane, bad);
+            step<D, false, true, false, false>(w, sm, nb - 1, sb, sb, 0, sl2, lane, bad);
     }
     // step nb: P*V of the last block
     if (nb > 0) {
