@@ -449,15 +449,22 @@ struct MergeArgs {
     const int32_t *__restrict__ seq_lens;
     const float *__restrict__ sinks;
     void *__restrict__ out;
-    int num_seqs, num_q_heads, num_wgs;
+    int num_seqs, num_q_heads, num_kv_heads, num_wgs;
 };
 
-// One wave per (query head, sequence): combine the pieces of the sequence in
-// logical order and fold the sink.
+// One workgroup per (sequence, KV head), one wave per query head of the
+// group: combine the pieces of the sequence in logical order and fold the
+// sink.  The work is two dependent memory round trips: the sequence lengths
+// (which place the sequence's pieces), then every piece's (m, l) -- one
+// piece per lane -- together with the accumulators of up to kBatch pieces.
 template <int D, bool kBf16Out>
-__global__ __launch_bounds__(64) void decode_merge(MergeArgs a)
+__global__ __launch_bounds__(1024) void decode_merge(MergeArgs a)
 {
-    const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    constexpr int kPer = D / 64;   // output dims per lane
+    constexpr int kBatch = 4;      // pieces whose accumulators are loaded at once
+    const int b = blockIdx.x, lane = threadIdx.x & 63;
+    const int group = a.num_q_heads / a.num_kv_heads;
+    const int h = blockIdx.y * group + (threadIdx.x >> 6);
     const float sink2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
     const int L = a.seq_lens[b];
     const long long nblk = units_of(L);
@@ -465,31 +472,48 @@ __global__ __launch_bounds__(64) void decode_merge(MergeArgs a)
     int w_lo = 0, w_hi = -1;
     long long U = 0;
     if (nblk > 0) {
-        int bb = 0;
-        long long base = 0;
-        U = scan_units(a.seq_lens, a.num_seqs, lane, -1, &bb, &base);
-        // units of the sequences before b
-        long long before = 0;
-        for (int b0 = 0; b0 < b; b0 += 64) {
+        // all units, and the units of the sequences before b, in one pass
+        long long before = 0, total = 0;
+        for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
             const int bi = b0 + lane;
-            before += bi < b ? units_of(a.seq_lens[bi]) : 0;
+            const long long u = bi < a.num_seqs ? units_of(a.seq_lens[bi]) : 0;
+            total += u;
+            before += bi < b ? u : 0;
         }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
+        for (int off = 32; off > 0; off >>= 1) {
+            total += __shfl_xor(total, off, 64);
             before += __shfl_xor(before, off, 64);
+        }
+        U = total;
         w_lo = wave_of_unit(before, U, a.num_wgs);
         w_hi = wave_of_unit(before + nblk - 1, U, a.num_wgs);
     }
-
+    const int npieces = w_hi - w_lo + 1;
     // workgroups in [w_lo, w_hi] with an empty unit range (possible when
     // there are fewer units than workgroups) wrote nothing and are skipped
-    float M = sink2;
-    for (int w = w_lo + lane; w <= w_hi; w += 64)
-        if (wave_first_unit(w, U, a.num_wgs) < wave_first_unit(w + 1, U, a.num_wgs))
-            M = fmaxf(M, a.part_ml[((size_t)(b + w) * a.num_q_heads + h) * 2]);
-    M = wave_max(M);
+    auto live = [&](int w) {
+        return wave_first_unit(w, U, a.num_wgs) < wave_first_unit(w + 1, U, a.num_wgs);
+    };
+    auto row_of = [&](int w) { return (size_t)(b + w) * a.num_q_heads + h; };
 
-    constexpr int kPer = D / 64;
+    // (m, l) of piece w_lo + i + 64 k in lane i
+    float M = sink2;
+    float mp[2] = {kNegInf, kNegInf}, lp[2] = {0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int w = w_lo + lane + 64 * k;
+        if (w <= w_hi && live(w)) {
+            const float2 ml = *(const float2 *)(a.part_ml + row_of(w) * 2);
+            mp[k] = ml.x;
+            lp[k] = ml.y;
+        }
+    }
+    for (int w = w_lo + lane + 128; w <= w_hi; w += 64)  // more than 128 pieces: max only
+        if (live(w))
+            M = fmaxf(M, a.part_ml[row_of(w) * 2]);
+    M = wave_max(fmaxf(M, fmaxf(mp[0], mp[1])));
+
     float acc[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
@@ -497,16 +521,35 @@ __global__ __launch_bounds__(64) void decode_merge(MergeArgs a)
     float den = 0.f;
     if (M != kNegInf) {
         den = sink2 == kNegInf ? 0.f : exp2_fast(sink2 - M);
-        for (int w = w_lo; w <= w_hi; ++w) {
-            if (wave_first_unit(w, U, a.num_wgs) == wave_first_unit(w + 1, U, a.num_wgs))
-                continue;
-            const size_t r = (size_t)(b + w) * a.num_q_heads + h;
-            const float mp = a.part_ml[r * 2];
-            const float f = mp == kNegInf ? 0.f : exp2_fast(mp - M);
-            den += f * a.part_ml[r * 2 + 1];
+        for (int i0 = 0; i0 < npieces; i0 += kBatch) {
+            float part[kBatch][kPer];
 #pragma unroll
-            for (int k = 0; k < kPer; ++k)
-                acc[k] += f * a.part_acc[r * D + lane + 64 * k];
+            for (int j = 0; j < kBatch; ++j) {
+                const int w = w_lo + i0 + j;
+                const bool ok = i0 + j < npieces;
+#pragma unroll
+                for (int k = 0; k < kPer; ++k)
+                    part[j][k] = ok ? a.part_acc[row_of(w) * D + lane + 64 * k] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int i = i0 + j, w = w_lo + i;
+                if (i >= npieces || !live(w))
+                    continue;
+                float m, l;
+                if (i < 128) {
+                    m = __shfl(i < 64 ? mp[0] : mp[1], i & 63, 64);
+                    l = __shfl(i < 64 ? lp[0] : lp[1], i & 63, 64);
+                } else {
+                    m = a.part_ml[row_of(w) * 2];
+                    l = a.part_ml[row_of(w) * 2 + 1];
+                }
+                const float f = m == kNegInf ? 0.f : exp2_fast(m - M);
+                den += f * l;
+#pragma unroll
+                for (int k = 0; k < kPer; ++k)
+                    acc[k] += f * part[j][k];
+            }
         }
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
@@ -557,12 +600,14 @@ hipError_t launch_merge_d(const DecodeLaunch &p)
     m.out = p.out;
     m.num_seqs = p.num_seqs;
     m.num_q_heads = p.num_q_heads;
+    m.num_kv_heads = p.num_kv_heads;
     m.num_wgs = p.num_wgs;
-    const dim3 grid(p.num_q_heads, p.num_seqs);
+    const dim3 grid(p.num_seqs, p.num_kv_heads);
+    const dim3 block(64 * (p.num_q_heads / p.num_kv_heads));
     if (p.dtype == 1)
-        hipLaunchKernelGGL((decode_merge<D, true>), grid, dim3(64), 0, p.stream, m);
+        hipLaunchKernelGGL((decode_merge<D, true>), grid, block, 0, p.stream, m);
     else
-        hipLaunchKernelGGL((decode_merge<D, false>), grid, dim3(64), 0, p.stream, m);
+        hipLaunchKernelGGL((decode_merge<D, false>), grid, block, 0, p.stream, m);
     return hipGetLastError();
 }
 
