@@ -717,10 +717,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
         exact_rows<D>(w, lds + wave * (C::kLdsBytes / 2 / kWaves), a, bt, L, head_off, nb, wpf, thr,
                       lane);
 
+    // Epilogue: fold the sink into each row's normalisation, then write the
+    // wave's rows through its own part of the (now free) LDS so that every
+    // global store covers whole 16-byte chunks of contiguous output rows.
+    // The staging rows are XOR-swizzled by 16-byte chunk (both the 8-byte
+    // writes and the 16-byte reads are then free of bank conflicts).
+    constexpr int kC16 = D / 8;  // 16-byte chunks per row
+    uint16_t *stage = lds + wave * (C::kLdsBytes / 2 / kWaves);
+    auto st_at = [&](int r, int c16) { return r * D + 8 * (c16 ^ (r & (kC16 - 1))); };
     const float sink2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-        const int row = row_w + 32 * rb + r32;
         float lx, ly;
         halves(w.lsum[rb], lx, ly);
         const float lsum = lx + ly;
@@ -731,18 +738,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
             const float den = lsum * f + (sink2 == kNegInf ? 0.f : exp2_fast(sink2 - M));
             scale = den > 0.f ? f / den : 0.f;
         }
-        if (row < q_len) {
-            uint16_t *orow = a.out + ((size_t)(q0 + row) * a.num_q_heads + h) * D;
+        // lane l holds dims 32 db + 8 r4 + 4 (l/32) .. +3 of row 32 rb + l%32
+        const int r = 32 * rb + r32;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const f32x16_t &o = w.acc[rb][db];
-                    const u32x2_t v = {pack_bf16(o[4 * r4] * scale, o[4 * r4 + 1] * scale),
-                                       pack_bf16(o[4 * r4 + 2] * scale, o[4 * r4 + 3] * scale)};
-                    *(u32x2_t *)(orow + 32 * db + 8 * r4 + 4 * half) = v;
-                }
-        }
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x16_t &o = w.acc[rb][db];
+                const u32x2_t v = {pack_bf16(o[4 * r4] * scale, o[4 * r4 + 1] * scale),
+                                   pack_bf16(o[4 * r4 + 2] * scale, o[4 * r4 + 3] * scale)};
+                *(u32x2_t *)&stage[st_at(r, 4 * db + r4) + 4 * half] = v;
+            }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
+    __builtin_amdgcn_wave_barrier();
+    // 64 lanes copy 64 / kC16 rows per pass, kC16 lanes per row
+    constexpr int kRowsPerPass = 64 / kC16;
+#pragma unroll
+    for (int r0 = 0; r0 < 32 * NRB; r0 += kRowsPerPass) {
+        const int r = r0 + lane / kC16, c16 = lane % kC16;
+        const int row = row_w + r;
+        const u32x4_t v = *(const u32x4_t *)&stage[st_at(r, c16)];
+        if (row < q_len)
+            *(u32x4_t *)(a.out + ((size_t)(q0 + row) * a.num_q_heads + h) * D + 8 * c16) = v;
     }
 }
 
