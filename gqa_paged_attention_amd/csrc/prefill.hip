@@ -447,6 +447,11 @@ __device__ __forceinline__ void step(WaveState<D> &w, const Smem<D> &sm, int b,
         const float psum = block_weights(s_cur[rb], w.m[rb], w.pop[rb], scale_log2);
         bad = bad || !(psum <= kWeightSumLimit);
         w.lsum[rb] += psum;
+        // Keep the weights in this step: without a use here, the compiler
+        // moves their computation to the next use, past the branch of the
+        // next tile start, where it no longer overlaps this step's matrix
+        // instructions.
+        asm volatile("" ::"v"(w.pop[rb][0]), "v"(w.pop[rb][1]), "v"(w.lsum[rb]));
     }
     if (kQK && kPV) {
         // vector work first while the LDS reads land, then one matrix
