@@ -340,8 +340,7 @@ __device__ __forceinline__ void apply_mask(f32x16_t &s, int thr)
 {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + (r & 3) > thr)
-            s[r] = kNegInf;
+        s[r] = 8 * (r >> 2) + (r & 3) > thr ? kNegInf : s[r];
 }
 
 // Exact block maximum of the row, base-2 units.
