@@ -79,6 +79,11 @@ def prefill_flops(batch) -> int:
 class Timer:
     """Per-stage HIP-event timing of a list of launches on the current stream."""
 
+    # Warm-up runs at least this long as well as at least W steps: after the
+    # host-side work between legs (seconds of workload generation) the GPU
+    # needs some tens of milliseconds of load before its clocks settle.
+    MIN_WARMUP_S = 0.25
+
     def __init__(self, torch, flush_buf):
         self.torch = torch
         self.flush_buf = flush_buf
@@ -86,12 +91,15 @@ class Timer:
     def run(self, stages, steps, warmup, flush=True):
         torch = self.torch
         n = len(stages)
-        for _ in range(warmup):
+        t_w = time.perf_counter()
+        done = 0
+        while done < warmup or time.perf_counter() - t_w < self.MIN_WARMUP_S:
             if flush:
                 self.flush_buf.fill_(1)
             for _, fn in stages:
                 fn()
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            done += 1
         events = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
                   for _ in range(steps)]
         torch.cuda.synchronize()
