@@ -58,7 +58,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kKB = 32;          // keys per block: one 32x32 S^T tile
-constexpr int kLoadsPerTile = 4; // 1 KiB direct loads per wave per tile (2 K + 2 V)
 // A block whose weight sum exceeds this (per lane) triggers an exact rescale.
 constexpr float kWeightSumLimit = 18446744073709551616.0f;  // 2^64
 
@@ -70,6 +69,9 @@ struct Cfg {
     static constexpr int kBPT = kBN / kKB;              // blocks per tile
     static constexpr int kRowsPerLoad = 1024 / (2 * D); // key rows per 1 KiB load
     static constexpr int kTileElems = kBN * D;          // bf16 elements of K (or V) per tile
+    // 1 KiB direct loads of one tensor per tile, and per wave
+    static constexpr int kChunks = kTileElems * 2 / 1024;
+    static constexpr int kChunksPerWave = kChunks / kWaves;
     // LDS stages: a step reads K two blocks ahead of the V it reads, and tile
     // T+2 is issued at the step that starts reading tile T, so the stage it
     // overwrites must have been read for the last time before that step.
@@ -115,15 +117,19 @@ __device__ __forceinline__ void halves(float v, float &x, float &y)
 }
 
 // Wait until this wave's direct loads of tile T have landed in LDS (those of
-// tile T+1, issued after them, may still be in flight: kLoadsPerTile = 4
-// loads), then meet the other waves.  The loads are
-// not tracked by the compiler's own wait insertion, hence the explicit wait.
+// tile T+1, issued after them, may still be in flight: 2 kChunksPerWave
+// loads), then meet the other waves.  The loads are not tracked by the
+// compiler's own wait insertion, hence the explicit wait.
+template <int kLoadsPerTile>
 __device__ __forceinline__ void wait_loads_and_sync(bool all_landed)
 {
+    static_assert(kLoadsPerTile == 2 || kLoadsPerTile == 4, "loads per tile");
     if (all_landed)
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else
+    else if (kLoadsPerTile == 4)
         asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 struct PrefillArgs {
@@ -183,15 +189,16 @@ struct Smem {
 };
 
 // Per-lane parts of this wave's direct loads (constant over tiles).  The wave
-// loads 1 KiB chunks j = wave and wave + 4 of each K and V tile; chunk j holds
+// loads 1 KiB chunks j = wave + 4i (i < kChunksPerWave) of each K and V tile;
+// chunk j holds
 // key rows R*j .. R*j+R-1 (R = 1024 / (2 d)), all inside one 16-token page,
 // and lane l fetches the 16-byte chunk that belongs in slot l % (d/8) of row
 // R*j + l / (d/8) of the swizzled tile.
 template <int D>
 struct LoadLanes {
-    int key[2];   // key of this lane's row within the tile, per chunk
-    int kc[2];    // K chunk (elements) within the row
-    int vc[2];    // V chunk (elements) within the row
+    int key[Cfg<D>::kChunksPerWave];  // key of this lane's row within the tile, per chunk
+    int kc[Cfg<D>::kChunksPerWave];   // K chunk (elements) within the row
+    int vc[Cfg<D>::kChunksPerWave];   // V chunk (elements) within the row
 };
 
 template <int D>
@@ -201,7 +208,7 @@ __device__ __forceinline__ LoadLanes<D> load_lanes(int wave, int lane)
     constexpr int kChunks = D / 8;  // 16-byte chunks per key row
     LoadLanes<D> ll;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < C::kChunksPerWave; ++i) {
         const int j = wave + kWaves * i;
         const int key = C::kRowsPerLoad * j + lane / kChunks;
         const int slot = lane % kChunks;
@@ -228,8 +235,8 @@ __device__ __forceinline__ void dma16(const uint16_t *gbase, uint32_t voff, cons
                  : "memory");
 }
 
-// Page ids of this wave's two load chunks of tile t (chunk j = wave + 4i
-// starts at key t*BN + R*j).  Page indices past the sequence's last page are
+// Page ids of this wave's load chunks of tile t (chunk j = wave + 4i starts
+// at key t*BN + R*j).  Page indices past the sequence's last page are
 // clamped to it.  Read one tile before the loads that use them, so that the
 // scalar-load latency stays off the tile start.
 struct ChunkPages {
@@ -242,8 +249,9 @@ __device__ __forceinline__ ChunkPages chunk_pages(const int32_t *__restrict__ bt
 {
     using C = Cfg<D>;
     ChunkPages cp;
+    cp.p[1] = 0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::kChunksPerWave; ++i)
         cp.p[i] = load_scalar(
             bt, min((t * C::kBN + C::kRowsPerLoad * (wave + kWaves * i)) >> 4, last_page));
     return cp;
@@ -261,7 +269,7 @@ __device__ __forceinline__ void load_tile(const Smem<D> &sm, const PrefillArgs &
     const int kv0 = t * C::kBN;
     const int stage = t % C::kStages;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < C::kChunksPerWave; ++i) {
         const int j = wave + kWaves * i;
         const size_t slab = (size_t)cp.p[i] * a.num_kv_heads * 16 * D + head_off;
         const int row = kv0 + ll.key[i] < L ? (ll.key[i] & 15) : ((L - 1) & 15);
@@ -633,7 +641,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
         if ((step + 1) % C::kBPT == 0) {
             const int t = (step + 1) / C::kBPT;
             if (t < ntiles) {
-                wait_loads_and_sync(t + 1 >= ntiles);
+                wait_loads_and_sync<2 * C::kChunksPerWave>(t + 1 >= ntiles);
                 if (t + 2 < ntiles) {
                     load_tile<D>(sm, a, next_pages, t + 2, L, head_off, wave, ll);
                     next_pages = chunk_pages<D>(bt, t + 3, last_page, wave);
