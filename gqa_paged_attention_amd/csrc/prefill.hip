@@ -460,9 +460,10 @@ __device__ __forceinline__ void step(WaveState<D> &w, const Smem<D> &sm, int b,
         // instructions.
         asm volatile("" ::"v"(w.pop[rb][0]), "v"(w.pop[rb][1]), "v"(w.lsum[rb]));
     }
-    if (kQK && kPV) {
+    if (kQK && kPV && D == 64) {
         // vector work first while the LDS reads land, then one matrix
-        // instruction per eight vector ones
+        // instruction per eight vector ones (at d = 128, with twice the
+        // matrix work per weight, the compiler's own order does better)
         __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
 #pragma unroll
         for (int i = 0; i < 8 * NRB; ++i) {
