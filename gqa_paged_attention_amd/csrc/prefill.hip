@@ -38,9 +38,9 @@
 // Softmax reference.  A row's reference maximum m is set exactly from its
 // first block and then kept: weights 2^(s - m) may exceed 1, which bf16 and
 // the fp32 accumulators absorb as long as they stay far from overflow.  The
-// block's weight sum (needed anyway) detects the rare block that would come
-// too close (sum > 2^64); only then is the exact block maximum taken, m
-// raised, the accumulators rescaled and the block's weights recomputed.  The
+// running row sum (needed anyway) detects the rare row that comes too close
+// (sum > 2^64, or not finite); the wave then recomputes its rows after the
+// loop with the plain online softmax (exact block maxima, rescaling).  The
 // final division uses the same m, so the result does not depend on it.
 //
 // Pipeline.  Step b of a wave issues S^T of block b+1 and P*V of block b-1 on
@@ -58,7 +58,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kKB = 32;          // keys per block: one 32x32 S^T tile
-// A block whose weight sum exceeds this (per lane) triggers an exact rescale.
+// A running row sum (per lane) above this triggers the exact recompute.
 constexpr float kWeightSumLimit = 18446744073709551616.0f;  // 2^64
 
 template <int D>
@@ -365,12 +365,12 @@ __device__ __forceinline__ float block_max(const f32x16_t &s, float scale_log2)
 
 // Weights 2^(s*scale_log2 - m) of one S^T block as the P^T operands of its
 // two 16-key halves (pop[ks]: keys 16ks + {4h..4h+3, 8+4h..8+4h+3} of this
-// lane's row, the k order of the V^T operand); returns their sum (this lane).
+// lane's row, the k order of the V^T operand); returns sum plus their sum
+// (this lane).
 __device__ __forceinline__ float block_weights(const f32x16_t &s, float m, u32x4_t (&pop)[2],
-                                               float scale_log2)
+                                               float scale_log2, float sum)
 {
     const float neg_m = -m;
-    float sum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         uint32_t pw[4];
@@ -421,7 +421,7 @@ __device__ __forceinline__ void qk_all(f32x16_t (&s)[Cfg<D>::kNRB], const WaveSt
 // the two S^T register sets between steps).  kPV: P*V of block
 // b-1 with the weights in w.pop.  Always: the weights of block b from s_cur,
 // relative to the reference maxima (set from the block itself when kFirst,
-// masked when kMasked).  A weight sum too close to overflow (or not finite)
+// masked when kMasked).  A row sum too close to overflow (or not finite)
 // marks the lane in `bad`; such a wave is recomputed exactly after the loop
 // (exact_rows), so the loop itself has no rescale branch.
 template <int D, bool kQK, bool kPV, bool kMasked, bool kFirst>
@@ -451,9 +451,8 @@ __device__ __forceinline__ void step(WaveState<D> &w, const Smem<D> &sm, int b,
         // every row, so it is finite from then on
         if (kFirst)
             w.m[rb] = block_max(s_cur[rb], scale_log2);
-        const float psum = block_weights(s_cur[rb], w.m[rb], w.pop[rb], scale_log2);
-        bad = bad || !(psum <= kWeightSumLimit);
-        w.lsum[rb] += psum;
+        w.lsum[rb] = block_weights(s_cur[rb], w.m[rb], w.pop[rb], scale_log2, w.lsum[rb]);
+        bad = bad || !(w.lsum[rb] <= kWeightSumLimit);
         // Keep the weights in this step: without a use here, the compiler
         // moves their computation to the next use, past the branch of the
         // next tile start, where it no longer overlaps this step's matrix
@@ -484,7 +483,7 @@ __device__ __forceinline__ void last_step(WaveState<D> &w, const Smem<D> &sm, in
         pv_mfma<D>(w.acc[rb], vop, w.pop[rb]);
 }
 
-// Exact recompute of a wave's rows (rare: some weight sum came too close to
+// Exact recompute of a wave's rows (rare: some row sum came too close to
 // overflow against the reference taken from the first block).  Each block's
 // exact row maximum is taken first and the running state rescaled to it, as
 // in the plain online softmax.  K and V come straight from the paged cache
@@ -541,7 +540,7 @@ __device__ void exact_rows(WaveState<D> &w, uint16_t *lds_wave, const PrefillArg
             for (int db = 0; db < D / 32; ++db)
                 w.acc[rb][db] *= alpha;
             w.m[rb] = m_new;
-            w.lsum[rb] += block_weights(s, m_new, w.pop[rb], a.scale_log2);
+            w.lsum[rb] = block_weights(s, m_new, w.pop[rb], a.scale_log2, w.lsum[rb]);
             pv_mfma<D>(w.acc[rb], vop, w.pop[rb]);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block's writes
@@ -658,7 +657,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     // register sets that trade roles every step (the steady loop is unrolled
     // twice so that no copy is needed)
     f32x16_t sa[NRB], sb[NRB];
-    bool bad = false;  // a weight sum of this lane came too close to overflow
+    bool bad = false;  // a row sum of this lane came too close to overflow
     tile_start(-1);
     if (nb > 0) {
         u32x4_t kop[D / 16];
