@@ -19,8 +19,11 @@ def _tolist(t):
     return t.tolist() if hasattr(t, "tolist") else list(t)
 
 
-def brute_force(batch):
-    """Return nested lists out[total_q][Hq][d] for a small CPU PagedBatch."""
+def brute_force(batch, window: int = 0):
+    """Return nested lists out[total_q][Hq][d] for a small CPU PagedBatch.
+
+    With window > 0 the query at position p lists only the keys at positions
+    p - window + 1 .. p (the sliding window of the model notes, section 4.1)."""
     q = _tolist(batch.q.double())
     k_pool = _tolist(batch.k_cache.double())
     v_pool = _tolist(batch.v_cache.double())
@@ -42,7 +45,8 @@ def brute_force(batch):
             for h in range(Hq):
                 kv_head = h // per_kv
                 keys, values = [], []
-                for j in range(newest + 1):
+                oldest = max(0, newest + 1 - window) if window > 0 else 0
+                for j in range(oldest, newest + 1):
                     page = table[b][j // P]
                     keys.append(k_pool[page][kv_head][j % P])
                     values.append(v_pool[page][kv_head][j % P])

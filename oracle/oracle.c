@@ -24,10 +24,17 @@
  *   p      = L_b - Lq_b + r            (position of the query; bottom-right
  *                                       causal alignment, so a decode token
  *                                       sees every cached key)
- *   s_j    = scale * sum_c q[c] * K_b[j][c],   j = 0 .. p
+ *   j0     = 0, or max(0, p - W + 1) with a sliding window of W > 0
+ *   s_j    = scale * sum_c q[c] * K_b[j][c],   j = j0 .. p
  *   m      = max(max_j s_j, sink_h)
  *   den    = sum_j exp(s_j - m) + exp(sink_h - m)
  *   out    = sum_j exp(s_j - m) * V_b[j] / den
+ *
+ *   Sliding window: the model notes (section 4.1, attention pattern; section
+ *   11, a per-layer window passed with each call into the paged kernel) give
+ *   even layers a local window of W = 128 positions.  Read here as: the query
+ *   at position p sees the W most recent positions p - W + 1 .. p, itself
+ *   included; the sink stays available whatever the window.
  *
  *   K_b[j] is read through the page table in HND page layout ("Hosting Qwen
  *   on Blackwell": KV caches laid out head-major with the tokens of a head
@@ -96,6 +103,7 @@ static int owner_seq(const int32_t *cu_seqlens_q, int num_seqs, int64_t t)
  *   seq_lens     [num_seqs] visible KV length L_b (includes the new tokens)
  *   cu_seqlens_q [num_seqs + 1] query offsets (decode: 0, 1, 2, ...)
  *   sinks        [Hq] fp32, or NULL meaning every sink is -inf
+ *   window       sliding window W (keys p - W + 1 .. p), or 0 for none
  *   row_token    [n_rows] query token index t in [0, total_q)
  *   row_head     [n_rows] query head h in [0, Hq)
  *   out          [n_rows][d] fp64
@@ -108,11 +116,11 @@ int oracle_attention_rows(int dtype, int num_seqs, int num_q_heads, int num_kv_h
                           const void *q, const void *k_cache, const void *v_cache,
                           const int32_t *block_table, const int32_t *seq_lens,
                           const int32_t *cu_seqlens_q, const float *sinks, double scale,
-                          int64_t n_rows, const int64_t *row_token, const int32_t *row_head,
+                          int window, int64_t n_rows, const int64_t *row_token, const int32_t *row_head,
                           double *out, double *lse, int num_threads)
 {
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        page_size <= 0 || num_q_heads % num_kv_heads != 0)
+        page_size <= 0 || num_q_heads % num_kv_heads != 0 || window < 0)
         return 1;
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16)
         return 1;
@@ -148,6 +156,7 @@ int oracle_attention_rows(int dtype, int num_seqs, int num_q_heads, int num_kv_h
             const int i = (int)(t - cu_seqlens_q[b]);
             const int pos = seq_lens[b] - q_len + i;
             const int n_vis = pos + 1 < 0 ? 0 : pos + 1;
+            const int j0 = (window > 0 && n_vis - window > 0) ? n_vis - window : 0;
             const int g = h / group;
             const double sink = sinks ? (double)sinks[h] : -INFINITY;
 
@@ -156,7 +165,7 @@ int oracle_attention_rows(int dtype, int num_seqs, int num_q_heads, int num_kv_h
 
             /* pass 1: logits and their maximum, the sink included */
             double m = sink;
-            for (int j = 0; j < n_vis; ++j) {
+            for (int j = j0; j < n_vis; ++j) {
                 const size_t row = kv_row(block_table, max_pages_per_seq, b, j, g,
                                           num_kv_heads, page_size, head_dim);
                 double dot = 0.0;
@@ -172,7 +181,7 @@ int oracle_attention_rows(int dtype, int num_seqs, int num_q_heads, int num_kv_h
                 acc[c] = 0.0;
             double den = 0.0;
             if (m != -INFINITY) {
-                for (int j = 0; j < n_vis; ++j) {
+                for (int j = j0; j < n_vis; ++j) {
                     const size_t row = kv_row(block_table, max_pages_per_seq, b, j, g,
                                               num_kv_heads, page_size, head_dim);
                     double e = exp(scores[j] - m);

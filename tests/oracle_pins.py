@@ -1,7 +1,7 @@
 """Pins that tie the oracle to facts other than its own code.
 
-Each pin takes `attn(batch, with_lse=False)` -- a callable with the oracle's
-signature -- and raises AssertionError when the callable disagrees with what
+Each pin takes `attn(batch, with_lse=False, window=0)` -- a callable with the
+oracle's signature -- and raises AssertionError when the callable disagrees with what
 the pages or the mathematics fix.  test_oracle.py runs them on the oracle;
 test_oracle_mutants.py runs them on copies of oracle.c with planted mistakes
 and checks that every mistake is caught by at least one pin.
@@ -17,7 +17,14 @@ The facts used:
   * sink = LSE halves the output; a sink far above LSE drives it to 0;
   * a single visible key gives v_0 * sigmoid(s_0 - sink);
   * permuting physical pages leaves the result bit-identical;
-  * a prefill row equals a decode call truncated at that row's position.
+  * a prefill row equals a decode call truncated at that row's position;
+  * sliding window ("GPT OSS" model notes, section 4.1: a local window of W
+    positions on even layers; section 11: the window is passed per call):
+    a window at least as long as the sequence changes nothing; the brute
+    force with the same window; plain softmax attention under a band mask
+    (torch SDPA) times sigmoid(LSE - sink); W = 1 is the single-key closed
+    form on the query's own key; and a windowed decode equals an unwindowed
+    decode over a pool that holds only the last W tokens.
 """
 from __future__ import annotations
 
@@ -38,11 +45,12 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "han
 
 # ---------------------------------------------------------------- references
 
-def sdpa_reference(batch):
+def sdpa_reference(batch, window=0):
     """Plain softmax attention (no sink) and per-row LSE, via torch fp64 CPU.
 
     Uses the logical K/V rows kept by the generator, GQA through
-    enable_gqa=True, and an explicit bottom-right causal mask.
+    enable_gqa=True, and an explicit bottom-right causal mask (a band of the
+    last `window` positions when window > 0).
     Returns (out [total_q][Hq][d], lse [total_q][Hq]) as numpy fp64.
     """
     assert batch.k_logical is not None, "build the batch with keep_logical=True"
@@ -60,6 +68,8 @@ def sdpa_reference(batch):
         i = torch.arange(nq).unsqueeze(1)
         j = torch.arange(L).unsqueeze(0)
         mask = j <= (L - nq + i)                                               # nq, L
+        if window > 0:
+            mask = mask & (j > (L - nq + i) - window)
         o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=batch.scale,
                                            enable_gqa=True)
         G = batch.num_q_heads // batch.num_kv_heads
@@ -263,6 +273,71 @@ def pin_empty_rows(attn):
     assert np.all(attn(e) == 0.0), "empty visible set with no sink must give 0"
 
 
+# ------------------------------------------------------------ sliding window
+
+def pin_window_wide_is_full(attn):
+    b = medium_batch(101)
+    full = attn(b)
+    for w in (int(b.seq_lens.max()), int(b.seq_lens.max()) + 7, 10 ** 6):
+        assert np.array_equal(attn(b, window=w), full), f"window {w} >= L changed the result"
+
+
+def pin_window_brute(attn):
+    for b, w in zip(tiny_batches(), (1, 3, 7, 16, 5)):
+        ref = np.array(brute_force(b, window=w))
+        _close(attn(b, window=w), ref, 1e-12, 1e-13, f"brute force, window {w}")
+
+
+def pin_window_band_sdpa(attn):
+    for seed, w, mode in ((111, 5, "normal"), (112, 24, "normal"), (113, 9, "neginf")):
+        b = medium_batch(seed, sink_mode=mode)
+        ref, lse = sdpa_reference(b, window=w)
+        if mode == "normal":
+            sink = b.sinks.double().numpy()[None, :]
+            ref = ref * sigmoid(lse - sink)[..., None]
+        _close(attn(b, window=w), ref, 1e-11, 1e-13, f"band-masked SDPA, window {w}")
+
+
+def pin_window_one(attn):
+    # W = 1: every row sees only its own position's key
+    b = wl.small_batch(121, "f32", [30, 12], [6, 12], 4, 2, 16, sink_mode="normal",
+                       sink_std=1.5, keep_logical=True)
+    got = attn(b, window=1)
+    G = b.num_q_heads // b.num_kv_heads
+    cu, offs = b.cu_seqlens_q.tolist(), b.kv_offsets.tolist()
+    for s in range(b.num_seqs):
+        L, nq = int(b.seq_lens[s]), cu[s + 1] - cu[s]
+        for i in range(nq):
+            kp = b.k_logical[offs[s] + L - nq + i].double()
+            vp = b.v_logical[offs[s] + L - nq + i].double()
+            for h in range(b.num_q_heads):
+                sp = float(b.scale * (b.q[cu[s] + i, h].double() @ kp[h // G]))
+                wgt = 1.0 / (1.0 + math.exp(float(b.sinks[h]) - sp))
+                _close(got[cu[s] + i, h], (vp[h // G] * wgt).numpy(), 1e-12, 1e-14,
+                       "window 1")
+
+
+def pin_window_truncation(attn):
+    # a windowed decode equals an unwindowed decode whose pool holds only
+    # the last W tokens of each sequence
+    b = wl.small_batch(131, "bf16", [70, 9, 129, 33], [1, 1, 1, 1], 8, 2, 32,
+                       sink_mode="normal", keep_logical=True)
+    offs = b.kv_offsets.tolist()
+    for w in (1, 16, 40):
+        ks, vs, lens = [], [], []
+        for s in range(b.num_seqs):
+            L = int(b.seq_lens[s])
+            lo = max(0, L - w)
+            ks.append(b.k_logical[offs[s] + lo:offs[s] + L])
+            vs.append(b.v_logical[offs[s] + lo:offs[s] + L])
+            lens.append(L - lo)
+        t = wl.from_logical("bf16", b.q.float(), torch.cat(ks).float(), torch.cat(vs).float(),
+                            lens, [1] * b.num_seqs, b.sinks, b.scale, perm_seed=w,
+                            spare_pages=3)
+        _close(attn(b, window=w), attn(t), 1e-12, 1e-14, f"window {w} vs truncated pool")
+
+
 ALL_PINS = [pin_golden, pin_brute, pin_plain_is_sdpa, pin_closed_form, pin_large_and_half_sink,
             pin_single_key, pin_page_permutation, pin_prefill_row_is_decode, pin_gqa_groups,
-            pin_empty_rows]
+            pin_empty_rows, pin_window_wide_is_full, pin_window_brute, pin_window_band_sdpa,
+            pin_window_one, pin_window_truncation]

@@ -7,8 +7,8 @@ from gqa_paged_attention_amd import workloads as wl
 from tests import oracle_pins as pins
 
 
-def _attn(batch, with_lse=False):
-    return oracle.attention(batch, threads=4, with_lse=with_lse)
+def _attn(batch, with_lse=False, window=0):
+    return oracle.attention(batch, threads=4, with_lse=with_lse, window=window)
 
 
 @pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)

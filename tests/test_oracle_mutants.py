@@ -32,6 +32,11 @@ MUTANTS = {
                                         "double e = exp(scores[j]);"),
     "query row of the wrong head": ("((size_t)t * num_q_heads + h) * head_dim + c",
                                     "((size_t)t * num_q_heads + h / group) * head_dim + c"),
+    "window one key too wide": ("? n_vis - window : 0;", "? n_vis - window - 1 : 0;"),
+    "window ignored": ("const int j0 = (window > 0 &&", "const int j0 = 0 * (window > 0 &&"),
+    "window anchored at the chunk's first query": (
+        "const int j0 = (window > 0 && n_vis - window > 0) ? n_vis - window : 0;",
+        "const int j0 = (window > 0 && n_vis - i - window > 0) ? n_vis - i - window : 0;"),
 }
 
 
@@ -51,8 +56,8 @@ def test_mutant_is_caught(tmp_path, name):
     old, new = MUTANTS[name]
     lib = _build(tmp_path, name, old, new)
 
-    def attn(batch, with_lse=False):
-        return oracle.attention(batch, threads=4, with_lse=with_lse, lib=lib)
+    def attn(batch, with_lse=False, window=0):
+        return oracle.attention(batch, threads=4, with_lse=with_lse, lib=lib, window=window)
 
     failures = []
     for pin in pins.ALL_PINS:
