@@ -55,6 +55,10 @@ def library():
     lib.attn_sinks_decode_merge.restype = I
     lib.attn_sinks_prefill.argtypes = [I] * 11 + [P] * 7 + [F, P, P]
     lib.attn_sinks_prefill.restype = I
+    lib.attn_sinks_decode_window.argtypes = [I] * 9 + [P] * 6 + [F, I, P, P, Z, P]
+    lib.attn_sinks_decode_window.restype = I
+    lib.attn_sinks_prefill_window.argtypes = [I] * 11 + [P] * 7 + [F, I, P, P]
+    lib.attn_sinks_prefill_window.restype = I
     lib.attn_sinks_status_string.argtypes = [I]
     lib.attn_sinks_status_string.restype = ctypes.c_char_p
     lib.attn_sinks_version.argtypes = []
@@ -114,6 +118,23 @@ def attn_sinks_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     q, workspace a byte (uint8) tensor of at least
     attn_sinks_decode_workspace_bytes(...) bytes.
     """
+    _decode(None, q, k_cache, v_cache, block_table, seq_lens, sinks, scale, out, workspace,
+            max_seq_len, stream)
+
+
+def attn_sinks_decode_window(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             block_table: torch.Tensor, seq_lens: torch.Tensor,
+                             sinks: Optional[torch.Tensor], scale: float, window: int,
+                             out: torch.Tensor, workspace: Optional[torch.Tensor],
+                             max_seq_len: int, stream=None) -> None:
+    """Enqueue attn_sinks_decode_window: as attn_sinks_decode, each query
+    seeing only its sequence's last `window` keys (0: all of them)."""
+    _decode(int(window), q, k_cache, v_cache, block_table, seq_lens, sinks, scale, out,
+            workspace, max_seq_len, stream)
+
+
+def _decode(window, q, k_cache, v_cache, block_table, seq_lens, sinks, scale, out, workspace,
+            max_seq_len, stream):
     dt = _DTYPE_CODE.get(q.dtype)
     if dt is None:
         raise ValueError(f"unsupported dtype {q.dtype}")
@@ -130,11 +151,14 @@ def attn_sinks_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.numel() != B:
         raise ValueError("block_table / seq_lens do not match the batch")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    status = library().attn_sinks_decode(
-        dt, B, Hq, Hkv, d, P, num_pages, block_table.shape[1], int(max_seq_len),
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(sinks),
-        ctypes.c_float(scale), _ptr(out), _ptr(workspace), ctypes.c_size_t(ws_bytes),
-        _stream_handle(stream))
+    head = (dt, B, Hq, Hkv, d, P, num_pages, block_table.shape[1], int(max_seq_len),
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(sinks),
+            ctypes.c_float(scale))
+    tail = (_ptr(out), _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream))
+    if window is None:
+        status = library().attn_sinks_decode(*head, *tail)
+    else:
+        status = library().attn_sinks_decode_window(*head, window, *tail)
     _raise(status)
 
 
@@ -187,6 +211,23 @@ def attn_sinks_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
 
     q [total_q][Hq][d] ragged by cu_seqlens_q [B+1] int32; out like q.
     """
+    _prefill(None, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, sinks, scale, out,
+             max_q_len, max_seq_len, stream)
+
+
+def attn_sinks_prefill_window(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              block_table: torch.Tensor, seq_lens: torch.Tensor,
+                              cu_seqlens_q: torch.Tensor, sinks: Optional[torch.Tensor],
+                              scale: float, window: int, out: torch.Tensor, max_q_len: int,
+                              max_seq_len: int, stream=None) -> None:
+    """Enqueue attn_sinks_prefill_window: as attn_sinks_prefill, the row at
+    position p seeing keys p - window + 1 .. p (window 0: all up to p)."""
+    _prefill(int(window), q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, sinks,
+             scale, out, max_q_len, max_seq_len, stream)
+
+
+def _prefill(window, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, sinks, scale,
+             out, max_q_len, max_seq_len, stream):
     dt = _DTYPE_CODE.get(q.dtype)
     if dt is None:
         raise ValueError(f"unsupported dtype {q.dtype}")
@@ -203,19 +244,24 @@ def attn_sinks_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
         raise ValueError("q / k_cache / v_cache / out shapes disagree")
     if block_table.dim() != 2 or block_table.shape[0] != B or cu_seqlens_q.numel() != B + 1:
         raise ValueError("block_table / cu_seqlens_q do not match the batch")
-    status = library().attn_sinks_prefill(
-        dt, B, Hq, Hkv, d, P, num_pages, block_table.shape[1], T, int(max_q_len),
-        int(max_seq_len), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-        _ptr(seq_lens), _ptr(cu_seqlens_q), _ptr(sinks), ctypes.c_float(scale), _ptr(out),
-        _stream_handle(stream))
+    head = (dt, B, Hq, Hkv, d, P, num_pages, block_table.shape[1], T, int(max_q_len),
+            int(max_seq_len), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(seq_lens), _ptr(cu_seqlens_q), _ptr(sinks), ctypes.c_float(scale))
+    tail = (_ptr(out), _stream_handle(stream))
+    if window is None:
+        status = library().attn_sinks_prefill(*head, *tail)
+    else:
+        status = library().attn_sinks_prefill_window(*head, window, *tail)
     _raise(status)
 
 
 # ------------------------------------------------------------ conveniences
 
 def decode_batch(batch, out: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Run attn_sinks_decode on a workloads.PagedBatch already on the GPU."""
+                 workspace: Optional[torch.Tensor] = None, stream=None,
+                 window: Optional[int] = None) -> torch.Tensor:
+    """Run attn_sinks_decode (attn_sinks_decode_window when `window` is given)
+    on a workloads.PagedBatch already on the GPU."""
     if out is None:
         out = torch.empty_like(batch.q)
     if workspace is None:
@@ -223,16 +269,25 @@ def decode_batch(batch, out: Optional[torch.Tensor] = None,
                                                    batch.num_kv_heads, batch.head_dim,
                                                    batch.max_seq_len)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=batch.q.device)
-    attn_sinks_decode(batch.q, batch.k_cache, batch.v_cache, batch.block_table, batch.seq_lens,
-                      batch.sinks, batch.scale, out, workspace, batch.max_seq_len, stream)
+    args = (batch.q, batch.k_cache, batch.v_cache, batch.block_table, batch.seq_lens,
+            batch.sinks, batch.scale)
+    if window is None:
+        attn_sinks_decode(*args, out, workspace, batch.max_seq_len, stream)
+    else:
+        attn_sinks_decode_window(*args, window, out, workspace, batch.max_seq_len, stream)
     return out
 
 
-def prefill_batch(batch, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Run attn_sinks_prefill on a workloads.PagedBatch already on the GPU."""
+def prefill_batch(batch, out: Optional[torch.Tensor] = None, stream=None,
+                  window: Optional[int] = None) -> torch.Tensor:
+    """Run attn_sinks_prefill (attn_sinks_prefill_window when `window` is
+    given) on a workloads.PagedBatch already on the GPU."""
     if out is None:
         out = torch.empty_like(batch.q)
-    attn_sinks_prefill(batch.q, batch.k_cache, batch.v_cache, batch.block_table, batch.seq_lens,
-                       batch.cu_seqlens_q, batch.sinks, batch.scale, out, batch.max_q_len,
-                       batch.max_seq_len, stream)
+    args = (batch.q, batch.k_cache, batch.v_cache, batch.block_table, batch.seq_lens,
+            batch.cu_seqlens_q, batch.sinks, batch.scale)
+    if window is None:
+        attn_sinks_prefill(*args, out, batch.max_q_len, batch.max_seq_len, stream)
+    else:
+        attn_sinks_prefill_window(*args, window, out, batch.max_q_len, batch.max_seq_len, stream)
     return out

@@ -141,14 +141,14 @@ int prepare_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, i
                    int page_size, int num_pages, int max_pages_per_seq, int max_seq_len,
                    const void *q, const void *k_cache, const void *v_cache,
                    const int32_t *block_table, const int32_t *seq_lens, const float *sinks,
-                   float scale, void *out, void *workspace, size_t workspace_bytes,
+                   float scale, int window, void *out, void *workspace, size_t workspace_bytes,
                    void *stream, bool reads_kv, bool writes_out, attn::DecodeLaunch *p)
 {
     int rc = check_common(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                           num_pages, max_pages_per_seq, max_seq_len);
     if (rc != ATTN_OK)
         return rc;
-    if (!std::isfinite(scale))
+    if (!std::isfinite(scale) || window < 0)
         return ATTN_ERR_SHAPE;
     if (num_seqs == 0)
         return ATTN_OK;
@@ -180,6 +180,7 @@ int prepare_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, i
     p->max_pages_per_seq = max_pages_per_seq;
     p->num_wgs = shape.wgs;
     p->heads_per_wg = shape.heads_per_wg;
+    p->window = window;
     p->q = q;
     p->k_cache = k_cache;
     p->v_cache = v_cache;
@@ -217,18 +218,31 @@ int attn_sinks_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads
                       float scale, void *out, void *workspace, size_t workspace_bytes,
                       void *stream)
 {
+    return attn_sinks_decode_window(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                    page_size, num_pages, max_pages_per_seq, max_seq_len, q,
+                                    k_cache, v_cache, block_table, seq_lens, sinks, scale, 0, out,
+                                    workspace, workspace_bytes, stream);
+}
+
+int attn_sinks_decode_window(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                             int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                             int max_seq_len, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *block_table,
+                             const int32_t *seq_lens, const float *sinks, float scale, int window,
+                             void *out, void *workspace, size_t workspace_bytes, void *stream)
+{
     attn::DecodeLaunch p;
     int rc = prepare_decode(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                             num_pages, max_pages_per_seq, max_seq_len, q, k_cache, v_cache,
-                            block_table, seq_lens, sinks, scale, out, workspace, workspace_bytes,
-                            stream, true, true, &p);
+                            block_table, seq_lens, sinks, scale, window, out, workspace,
+                            workspace_bytes, stream, true, true, &p);
     if (rc != ATTN_OK || num_seqs == 0)
         return rc;
     if (dtype == ATTN_DTYPE_F32) {
         hipError_t e = attn::launch_rows_f32(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                              max_pages_per_seq, num_seqs, q, k_cache, v_cache,
-                                             block_table, seq_lens, nullptr, sinks, scale, out,
-                                             p.stream);
+                                             block_table, seq_lens, nullptr, sinks, scale, window,
+                                             out, p.stream);
         return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
     }
     if (attn::launch_decode_split_bf16(p) != hipSuccess)
@@ -248,7 +262,7 @@ int attn_sinks_decode_partials(int dtype, int num_seqs, int num_q_heads, int num
     attn::DecodeLaunch p;
     int rc = prepare_decode(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                             num_pages, max_pages_per_seq, max_seq_len, q, k_cache, v_cache,
-                            block_table, seq_lens, nullptr, scale, nullptr, workspace,
+                            block_table, seq_lens, nullptr, scale, 0, nullptr, workspace,
                             workspace_bytes, stream, true, false, &p);
     if (rc != ATTN_OK || num_seqs == 0)
         return rc;
@@ -265,7 +279,7 @@ int attn_sinks_decode_merge(int dtype, int num_seqs, int num_q_heads, int num_kv
     const int pages = (max_seq_len + kPageSize - 1) / kPageSize;
     int rc = prepare_decode(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, kPageSize,
                             pages > 0 ? pages : 1, pages, max_seq_len, nullptr, nullptr, nullptr,
-                            nullptr, seq_lens, sinks, 1.0f, out, const_cast<void *>(workspace),
+                            nullptr, seq_lens, sinks, 1.0f, 0, out, const_cast<void *>(workspace),
                             workspace_bytes, stream, false, true, &p);
     if (rc != ATTN_OK || num_seqs == 0)
         return rc;
@@ -279,13 +293,27 @@ int attn_sinks_prefill(int dtype, int num_seqs, int num_q_heads, int num_kv_head
                        const int32_t *cu_seqlens_q, const float *sinks, float scale, void *out,
                        void *stream)
 {
+    return attn_sinks_prefill_window(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                     page_size, num_pages, max_pages_per_seq, total_q, max_q_len,
+                                     max_seq_len, q, k_cache, v_cache, block_table, seq_lens,
+                                     cu_seqlens_q, sinks, scale, 0, out, stream);
+}
+
+int attn_sinks_prefill_window(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                              int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                              int total_q, int max_q_len, int max_seq_len, const void *q,
+                              const void *k_cache, const void *v_cache,
+                              const int32_t *block_table, const int32_t *seq_lens,
+                              const int32_t *cu_seqlens_q, const float *sinks, float scale,
+                              int window, void *out, void *stream)
+{
     int rc = check_common(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                           num_pages, max_pages_per_seq, max_seq_len);
     if (rc != ATTN_OK)
         return rc;
     if (total_q < 0 || max_q_len < 0 || max_q_len > max_seq_len || max_q_len > total_q)
         return ATTN_ERR_SHAPE;
-    if (!std::isfinite(scale))
+    if (!std::isfinite(scale) || window < 0)
         return ATTN_ERR_SHAPE;
     if (num_seqs == 0 || total_q == 0)
         return ATTN_OK;
@@ -305,7 +333,7 @@ int attn_sinks_prefill(int dtype, int num_seqs, int num_q_heads, int num_kv_head
         hipError_t e = attn::launch_rows_f32(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                              max_pages_per_seq, total_q, q, k_cache, v_cache,
                                              block_table, seq_lens, cu_seqlens_q, sinks, scale,
-                                             out, s);
+                                             window, out, s);
         return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
     }
     attn::PrefillLaunch p;
@@ -317,6 +345,8 @@ int attn_sinks_prefill(int dtype, int num_seqs, int num_q_heads, int num_kv_head
     p.max_pages_per_seq = max_pages_per_seq;
     p.total_q = total_q;
     p.max_q_len = max_q_len;
+    p.max_seq_len = max_seq_len;
+    p.window = window;
     p.q = q;
     p.k_cache = k_cache;
     p.v_cache = v_cache;

@@ -52,14 +52,30 @@ struct SplitArgs {
     int num_seqs, num_q_heads, num_kv_heads, group, max_pages;
     int num_wgs;        // workgroups per head group
     int heads_per_wg;   // KV heads (waves) per workgroup
+    int window;         // sliding window W (0: none)
     float scale_log2;
 };
 
 constexpr int kUnitTokens = 32;
 
-__device__ __forceinline__ long long units_of(int L)
+// Oldest key a decode token at position L - 1 sees: 0, or L - W under a
+// sliding window of W ("GPT OSS" model notes, section 4.1: even layers attend
+// within a local window; section 11: the window is passed per call).
+__device__ __forceinline__ int oldest_key(int L, int window)
 {
-    return (L + kUnitTokens - 1) / kUnitTokens;
+    return (window > 0 && L > window) ? L - window : 0;
+}
+
+// The units of a sequence are the 32-token blocks from the one holding its
+// oldest visible key to its last: units_of of them, the first being block
+// first_unit.
+__device__ __forceinline__ int first_unit(int L, int window)
+{
+    return oldest_key(L, window) / kUnitTokens;
+}
+__device__ __forceinline__ long long units_of(int L, int window)
+{
+    return (L + kUnitTokens - 1) / kUnitTokens - first_unit(L, window);
 }
 
 // First unit of workgroup w, and the workgroup that processes unit u (the
@@ -76,14 +92,14 @@ __device__ __forceinline__ int wave_of_unit(long long u, long long U, int nw)
 // Wave-wide scan over the sequences.  Returns U, the total unit count; when
 // `target` >= 0 also returns the sequence that holds unit `target` and the
 // index of that sequence's first unit.
-__device__ long long scan_units(const int32_t *__restrict__ seq_lens, int num_seqs, int lane,
-                                long long target, int *b_out, long long *base_out)
+__device__ long long scan_units(const int32_t *__restrict__ seq_lens, int num_seqs, int window,
+                                int lane, long long target, int *b_out, long long *base_out)
 {
     long long carry = 0;
     bool found = false;
     for (int b0 = 0; b0 < num_seqs; b0 += 64) {
         const int b = b0 + lane;
-        const long long nb = b < num_seqs ? units_of(seq_lens[b]) : 0;
+        const long long nb = b < num_seqs ? units_of(seq_lens[b], window) : 0;
         long long incl = nb;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -212,8 +228,9 @@ struct WaveState {
 
 template <int D, bool kMasked>
 __device__ __forceinline__ void compute_block(WaveState<D> &st, Block<D> &blk,
-                                              const u32x4_t (&qop)[D / 32], int t0, int t_end,
-                                              float scale_log2, int lg, u32x4_t *klds)
+                                              const u32x4_t (&qop)[D / 32], int t0, int t_lo,
+                                              int t_end, float scale_log2, int lg,
+                                              u32x4_t *klds)
 {
     using VRow = typename VRowT<D>::type;
     constexpr int kChunks = D / 8;  // 16-byte chunks per K row
@@ -250,15 +267,18 @@ __device__ __forceinline__ void compute_block(WaveState<D> &st, Block<D> &blk,
         x[4 + i] = s1[i] * scale_log2;
     }
     if (kMasked) {
-        // tail block: mask scores and zero the V rows of tokens outside the
-        // range (they may hold NaN, and 0 * NaN would poison every head)
+        // first or last block of a piece: mask scores and zero the V rows of
+        // tokens outside [t_lo, t_end) (past the end they may hold NaN, and
+        // 0 * NaN would poison every head); the block holds at least one
+        // token of the range, so its maximum below is finite
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (t0 + 4 * lg + i >= t_end) {
+            const int ta = t0 + 4 * lg + i, tb = ta + 16;
+            if (ta >= t_end || ta < t_lo) {
                 x[i] = kNegInf;
                 blk.v[i] = VRow{};
             }
-            if (t0 + 16 + 4 * lg + i >= t_end) {
+            if (tb >= t_end || tb < t_lo) {
                 x[4 + i] = kNegInf;
                 blk.v[4 + i] = VRow{};
             }
@@ -297,15 +317,17 @@ __device__ __forceinline__ void compute_block(WaveState<D> &st, Block<D> &blk,
     }
 }
 
-// One piece: tokens [t_begin, t_end) of segment (b, g); the result goes to `slot`.
+// One piece: the tokens of [t_begin, t_end) (t_begin a multiple of 32) from
+// t_lo on, of segment (b, g); the result goes to `slot`.
 template <int D>
 __device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int t_begin,
-                                          int t_end, long long slot, int n, int lg,
+                                          int t_lo, int t_end, long long slot, int n, int lg,
                                           u32x4_t *klds)
 {
     b = uniform(b);
     g = uniform(g);
     t_begin = uniform(t_begin);
+    t_lo = uniform(t_lo);
     t_end = uniform(t_end);
     // Q^T operand: column n = query head g*G + n, dims kk*32 + lg*8 .. +7
     u32x4_t qop[D / 32];
@@ -327,12 +349,20 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int 
         st.acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
+    if (t_begin < t_lo) {
+        // the block that holds the oldest key of a sliding window
+        Block<D> head;
+        load_block<D, false>(head, a.k_cache, a.v_cache, bt, t_begin, t_end, g, a.num_kv_heads,
+                             n, lg);
+        compute_block<D, true>(st, head, qop, t_begin, t_lo, t_end, a.scale_log2, lg, klds);
+        t_begin += kUnitTokens;
+    }
     // Full blocks stream through a ring of register buffers with loads issued
     // ahead of the matrix work (two blocks ahead at d = 64, one at d = 128,
     // where a block is 16 KiB per wave).  Prefetches past the last full block
     // re-read that block (a cache hit), so the loop body has no branches
     // around loads.  A partial last block is handled after the loop.
-    const int nfull = (t_end - t_begin) / kUnitTokens;
+    const int nfull = t_end > t_begin ? (t_end - t_begin) / kUnitTokens : 0;
     const int t_last = t_begin + kUnitTokens * (nfull - 1);
     auto at = [&](int ib) { return min(t_begin + kUnitTokens * ib, t_last); };
     if (nfull > 0) {
@@ -346,17 +376,17 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int 
                 const int t0 = t_begin + kUnitTokens * ib;
                 load_block<D, true>(b2, a.k_cache, a.v_cache, bt, at(ib + 2), t_end, g,
                                     a.num_kv_heads, n, lg);
-                compute_block<D, false>(st, b0, qop, t0, t_end, a.scale_log2, lg, klds);
+                compute_block<D, false>(st, b0, qop, t0, t_lo, t_end, a.scale_log2, lg, klds);
                 if (ib + 1 >= nfull)
                     break;
                 load_block<D, true>(b0, a.k_cache, a.v_cache, bt, at(ib + 3), t_end, g,
                                     a.num_kv_heads, n, lg);
-                compute_block<D, false>(st, b1, qop, t0 + 32, t_end, a.scale_log2, lg, klds);
+                compute_block<D, false>(st, b1, qop, t0 + 32, t_lo, t_end, a.scale_log2, lg, klds);
                 if (ib + 2 >= nfull)
                     break;
                 load_block<D, true>(b1, a.k_cache, a.v_cache, bt, at(ib + 4), t_end, g,
                                     a.num_kv_heads, n, lg);
-                compute_block<D, false>(st, b2, qop, t0 + 64, t_end, a.scale_log2, lg, klds);
+                compute_block<D, false>(st, b2, qop, t0 + 64, t_lo, t_end, a.scale_log2, lg, klds);
             }
         } else {
             Block<D> b0, b1;
@@ -366,12 +396,12 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int 
                 const int t0 = t_begin + kUnitTokens * ib;
                 load_block<D, true>(b1, a.k_cache, a.v_cache, bt, at(ib + 1), t_end, g,
                                     a.num_kv_heads, n, lg);
-                compute_block<D, false>(st, b0, qop, t0, t_end, a.scale_log2, lg, klds);
+                compute_block<D, false>(st, b0, qop, t0, t_lo, t_end, a.scale_log2, lg, klds);
                 if (ib + 1 >= nfull)
                     break;
                 load_block<D, true>(b0, a.k_cache, a.v_cache, bt, at(ib + 2), t_end, g,
                                     a.num_kv_heads, n, lg);
-                compute_block<D, false>(st, b1, qop, t0 + 32, t_end, a.scale_log2, lg, klds);
+                compute_block<D, false>(st, b1, qop, t0 + 32, t_lo, t_end, a.scale_log2, lg, klds);
             }
         }
     }
@@ -380,7 +410,7 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int 
         const int t0 = t_begin + kUnitTokens * nfull;
         load_block<D, false>(bt_tail, a.k_cache, a.v_cache, bt, t0, t_end, g, a.num_kv_heads, n,
                              lg);
-        compute_block<D, true>(st, bt_tail, qop, t0, t_end, a.scale_log2, lg, klds);
+        compute_block<D, true>(st, bt_tail, qop, t0, t_lo, t_end, a.scale_log2, lg, klds);
     }
     const float lsum = group4_sum(st.lsum);
     if (n < a.group) {
@@ -414,24 +444,27 @@ __global__ __launch_bounds__(512) void decode_split_bf16(SplitArgs a)
     u32x4_t *klds = s_k + (threadIdx.x >> 6) * (2 * 16 * (D / 8));
     int b = 0;
     long long base = 0;
-    const long long U = scan_units(a.seq_lens, a.num_seqs, lane, -1, &b, &base);
+    const long long U = scan_units(a.seq_lens, a.num_seqs, a.window, lane, -1, &b, &base);
     const long long u_begin = wave_first_unit(w, U, a.num_wgs);
     const long long u_end = wave_first_unit(w + 1, U, a.num_wgs);
     if (u_begin >= u_end)
         return;  // no unit for this workgroup
-    scan_units(a.seq_lens, a.num_seqs, lane, u_begin, &b, &base);
+    scan_units(a.seq_lens, a.num_seqs, a.window, lane, u_begin, &b, &base);
     b = uniform(b);
     base = uniform64(base);
     long long u = uniform64(u_begin);
     const long long u_stop = uniform64(u_end);
     while (u < u_stop) {
-        // sequence b holds units [base, base + nblk)
+        // sequence b holds units [base, base + nblk): its 32-token blocks
+        // from block first_unit on
         const int L = load_scalar(a.seq_lens, b);
-        const long long nblk = units_of(L);
+        const long long nblk = units_of(L, a.window);
+        const int fu = first_unit(L, a.window);
         const long long piece_end = min(u_stop, base + nblk);
-        const int t_begin = (int)(u - base) * kUnitTokens;
-        const int t_end = min((int)(piece_end - base) * kUnitTokens, L);
-        run_piece<D>(a, b, g, t_begin, t_end, (long long)b + w, n, lg, klds);
+        const int t_begin = ((int)(u - base) + fu) * kUnitTokens;
+        const int t_end = min(((int)(piece_end - base) + fu) * kUnitTokens, L);
+        run_piece<D>(a, b, g, t_begin, oldest_key(L, a.window), t_end, (long long)b + w, n, lg,
+                     klds);
         u = piece_end;
         if (u < u_stop) {
             // next sequence with at least one unit
@@ -450,6 +483,7 @@ struct MergeArgs {
     const float *__restrict__ sinks;
     void *__restrict__ out;
     int num_seqs, num_q_heads, num_kv_heads, num_wgs;
+    int window;  // sliding window W (0: none); places the pieces as the split pass does
 };
 
 // One workgroup per (sequence, KV head), one wave per query head of the
@@ -467,7 +501,7 @@ __global__ __launch_bounds__(1024) void decode_merge(MergeArgs a)
     const int h = blockIdx.y * group + (threadIdx.x >> 6);
     const float sink2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
     const int L = a.seq_lens[b];
-    const long long nblk = units_of(L);
+    const long long nblk = units_of(L, a.window);
 
     int w_lo = 0, w_hi = -1;
     long long U = 0;
@@ -476,7 +510,7 @@ __global__ __launch_bounds__(1024) void decode_merge(MergeArgs a)
         long long before = 0, total = 0;
         for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
             const int bi = b0 + lane;
-            const long long u = bi < a.num_seqs ? units_of(a.seq_lens[bi]) : 0;
+            const long long u = bi < a.num_seqs ? units_of(a.seq_lens[bi], a.window) : 0;
             total += u;
             before += bi < b ? u : 0;
         }
@@ -582,6 +616,7 @@ hipError_t launch_split_d(const DecodeLaunch &p)
     a.max_pages = p.max_pages_per_seq;
     a.num_wgs = p.num_wgs;
     a.heads_per_wg = p.heads_per_wg;
+    a.window = p.window;
     a.scale_log2 = p.scale * kLog2e;
     const dim3 grid(p.num_wgs, (p.num_kv_heads + p.heads_per_wg - 1) / p.heads_per_wg);
     const size_t lds = (size_t)p.heads_per_wg * 2 * 16 * (D / 8) * sizeof(u32x4_t);
@@ -602,6 +637,7 @@ hipError_t launch_merge_d(const DecodeLaunch &p)
     m.num_q_heads = p.num_q_heads;
     m.num_kv_heads = p.num_kv_heads;
     m.num_wgs = p.num_wgs;
+    m.window = p.window;
     const dim3 grid(p.num_seqs, p.num_kv_heads);
     const dim3 block(64 * (p.num_q_heads / p.num_kv_heads));
     if (p.dtype == 1)

@@ -12,6 +12,7 @@ struct DecodeLaunch {
     int max_pages_per_seq;
     int num_wgs;        // split-pass workgroups per KV-head group
     int heads_per_wg;   // KV heads (one wave each) per split-pass workgroup
+    int window;         // sliding window W (keys L - W .. L - 1), 0: none
     const void *q, *k_cache, *v_cache;
     const int32_t *block_table, *seq_lens;
     const float *sinks;
@@ -25,7 +26,8 @@ struct DecodeLaunch {
 struct PrefillLaunch {
     int dtype;
     int num_seqs, num_q_heads, num_kv_heads, head_dim;
-    int max_pages_per_seq, total_q, max_q_len;
+    int max_pages_per_seq, total_q, max_q_len, max_seq_len;
+    int window;         // sliding window W (keys p - W + 1 .. p), 0: none
     const void *q, *k_cache, *v_cache;
     const int32_t *block_table, *seq_lens, *cu_seqlens_q;
     const float *sinks;
@@ -52,6 +54,7 @@ hipError_t launch_rows_f32(int num_seqs, int num_q_heads, int num_kv_heads, int 
                            int max_pages_per_seq, int total_q, const void *q,
                            const void *k_cache, const void *v_cache, const int32_t *block_table,
                            const int32_t *seq_lens, const int32_t *cu_seqlens_q,
-                           const float *sinks, float scale, void *out, hipStream_t stream);
+                           const float *sinks, float scale, int window, void *out,
+                           hipStream_t stream);
 
 }  // namespace attn

@@ -143,6 +143,7 @@ struct PrefillArgs {
     uint16_t *__restrict__ out;
     int num_seqs, num_q_heads, num_kv_heads, group, max_pages, num_q_tiles;
     int xcd_groups;  // (sequence, KV head) groups laid out XCD by XCD
+    int window;      // sliding window W (keys p - W + 1 .. p), 0: none
     float scale_log2;
 };
 
@@ -351,6 +352,17 @@ __device__ __forceinline__ void apply_mask(f32x16_t &s, int thr)
         s[r] = 8 * (r >> 2) + (r & 3) > thr ? kNegInf : s[r];
 }
 
+// Sliding window: keys with offset > thr or <= thr - W are invisible (the
+// window holds the W positions up to the row's own).
+__device__ __forceinline__ void apply_band(f32x16_t &s, int thr, int window)
+{
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int e = 8 * (r >> 2) + (r & 3);
+        s[r] = (e > thr || e <= thr - window) ? kNegInf : s[r];
+    }
+}
+
 // Exact block maximum of the row, base-2 units.
 __device__ __forceinline__ float block_max(const f32x16_t &s, float scale_log2)
 {
@@ -483,20 +495,96 @@ __device__ __forceinline__ void last_step(WaveState<D> &w, const Smem<D> &sm, in
         pv_mfma<D>(w.acc[rb], vop, w.pop[rb]);
 }
 
+// One 32-key block of K and V fetched straight from the paged cache: kPer
+// 16-byte chunks of each per lane (key c / (d/8), chunk c % (d/8) for c =
+// lane + 64 i).  Keys past the sequence repeat its last key (finite; masked).
+template <int D>
+struct RawBlock {
+    static constexpr int kPer = kKB * (D / 8) / 64;
+    u32x4_t k[kPer], v[kPer];
+};
+
+template <int D>
+__device__ __forceinline__ void fetch_block(RawBlock<D> &rb, const PrefillArgs &a,
+                                            const int32_t *__restrict__ bt, int L,
+                                            size_t head_off, int k0, int lane)
+{
+    constexpr int kChunks = D / 8;
+#pragma unroll
+    for (int i = 0; i < RawBlock<D>::kPer; ++i) {
+        const int c = lane + 64 * i;
+        const int key = c / kChunks, chunk = c % kChunks;
+        const int tok = min(k0 + key, L - 1);
+        const int page = bt[tok >> 4];
+        const size_t off = (size_t)page * a.num_kv_heads * 16 * D + head_off +
+                           (size_t)(tok & 15) * D + 8 * chunk;
+        rb.k[i] = *(const u32x4_t *)(a.k_cache + off);
+        rb.v[i] = *(const u32x4_t *)(a.v_cache + off);
+    }
+}
+
+// Into a wave's own K and V tiles (32 keys each, the layouts of the pipelined
+// loop), then wait until the wave's writes are done.
+template <int D>
+__device__ __forceinline__ void stash_block(const RawBlock<D> &rb, uint16_t *kt, uint16_t *vt,
+                                            int lane)
+{
+    constexpr int kChunks = D / 8;
+#pragma unroll
+    for (int i = 0; i < RawBlock<D>::kPer; ++i) {
+        const int c = lane + 64 * i;
+        const int key = c / kChunks, chunk = c % kChunks;
+        *(u32x4_t *)&kt[Swz<D>::k_at(key, chunk)] = rb.k[i];
+        *(u32x4_t *)&vt[Swz<D>::v_at(key, 2 * chunk)] = rb.v[i];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Plain online softmax over one block held in the wave's tiles: exact row
+// maximum, running state rescaled to it, weights, P*V.  kBand: sliding-window
+// mask (both sides) instead of the causal one.  A row that has seen no
+// visible key yet keeps m = -inf and adds nothing (its weights are 0).
+template <int D, bool kBand>
+__device__ __forceinline__ void exact_block(WaveState<D> &w, const uint16_t *kt,
+                                            const uint16_t *vt, bool masked, int thr,
+                                            int window, float scale_log2, int lane)
+{
+    u32x4_t kop[D / 16], vop[D / 32][2];
+    read_k<D>(kop, kt, 0, lane);
+    read_v<D>(vop, vt, 0, lane);
+#pragma unroll
+    for (int rb = 0; rb < Cfg<D>::kNRB; ++rb) {
+        f32x16_t s = qk_mfma<D>(w.qop[rb], kop);
+        if (kBand)
+            apply_band(s, thr + 32 * rb, window);
+        else if (masked)
+            apply_mask(s, thr + 32 * rb);
+        const float m_new = fmaxf(w.m[rb], block_max(s, scale_log2));
+        const float m_ref = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = exp2_fast(w.m[rb] - m_ref);  // 0 while m is -inf
+        w.lsum[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            w.acc[rb][db] *= alpha;
+        w.m[rb] = m_new;
+        w.lsum[rb] = block_weights(s, m_ref, w.pop[rb], scale_log2, w.lsum[rb]);
+        pv_mfma<D>(w.acc[rb], vop, w.pop[rb]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block's writes
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Exact recompute of a wave's rows (rare: some row sum came too close to
-// overflow against the reference taken from the first block).  Each block's
-// exact row maximum is taken first and the running state rescaled to it, as
-// in the plain online softmax.  K and V come straight from the paged cache
-// into this wave's own quarter of the LDS (the workgroup has met after its
-// pipelined loop, so nothing else reads it).
+// overflow against the reference taken from the first block).  K and V come
+// straight from the paged cache into this wave's own part of the LDS (the
+// workgroup has met after its pipelined loop, so nothing else reads it).
 template <int D>
 __device__ void exact_rows(WaveState<D> &w, uint16_t *lds_wave, const PrefillArgs &a,
                            const int32_t *__restrict__ bt, int L, size_t head_off, int nb,
                            int wpf, int thr, int lane)
 {
     constexpr int NRB = Cfg<D>::kNRB;
-    constexpr int kChunks = D / 8;            // 16-byte chunks per key row
-    constexpr int kPer = kKB * kChunks / 64;  // chunks per lane per block
     uint16_t *kt = lds_wave;
     uint16_t *vt = lds_wave + kKB * D;
 #pragma unroll
@@ -509,53 +597,22 @@ __device__ void exact_rows(WaveState<D> &w, uint16_t *lds_wave, const PrefillArg
     }
     for (int blk = 0; blk < nb; ++blk) {
         const int k0 = kKB * blk;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int c = lane + 64 * i;
-            const int key = c / kChunks, chunk = c % kChunks;
-            const int tok = min(k0 + key, L - 1);  // past the sequence: its last row
-            const int page = bt[tok >> 4];
-            const size_t off = (size_t)page * a.num_kv_heads * 16 * D + head_off +
-                               (size_t)(tok & 15) * D + 8 * chunk;
-            const u32x4_t kv = *(const u32x4_t *)(a.k_cache + off);
-            const u32x4_t vv = *(const u32x4_t *)(a.v_cache + off);
-            *(u32x4_t *)&kt[Swz<D>::k_at(key, chunk)] = kv;
-            *(u32x4_t *)&vt[Swz<D>::v_at(key, 2 * chunk)] = vv;
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-        __builtin_amdgcn_wave_barrier();
-        u32x4_t kop[D / 16], vop[D / 32][2];
-        read_k<D>(kop, kt, 0, lane);
-        read_v<D>(vop, vt, 0, lane);
-        const bool masked = k0 + kKB - 1 > wpf;
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            f32x16_t s = qk_mfma<D>(w.qop[rb], kop);
-            if (masked)
-                apply_mask(s, thr - k0 + 32 * rb);
-            const float m_new = fmaxf(w.m[rb], block_max(s, a.scale_log2));
-            const float alpha = exp2_fast(w.m[rb] - m_new);  // 0 while m is -inf
-            w.lsum[rb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-                w.acc[rb][db] *= alpha;
-            w.m[rb] = m_new;
-            w.lsum[rb] = block_weights(s, m_new, w.pop[rb], a.scale_log2, w.lsum[rb]);
-            pv_mfma<D>(w.acc[rb], vop, w.pop[rb]);
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block's writes
-        __builtin_amdgcn_wave_barrier();
+        RawBlock<D> raw;
+        fetch_block<D>(raw, a, bt, L, head_off, k0, lane);
+        stash_block<D>(raw, kt, vt, lane);
+        exact_block<D, false>(w, kt, vt, k0 + kKB - 1 > wpf, thr - k0, 0, a.scale_log2, lane);
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
+// Workgroup -> (sequence, KV head, query head, query tile): all workgroups of
+// one (sequence, KV head) land on one XCD (workgroups are dispatched to XCDs
+// round-robin), heaviest query tiles first.
+struct TileCoords {
+    int b, g, h, qt;
+};
+
+__device__ __forceinline__ TileCoords tile_of(const PrefillArgs &a)
 {
-    using C = Cfg<D>;
-    constexpr int NRB = C::kNRB;
-    // workgroup -> (sequence, KV head, query head in group, query tile): all
-    // workgroups of one (sequence, KV head) land on one XCD (workgroups are
-    // dispatched to XCDs round-robin), heaviest query tiles first
     const int per_group = a.group * a.num_q_tiles;
     const int id = blockIdx.x;
     int grp, r;
@@ -568,9 +625,98 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
         grp = a.xcd_groups + (id - main_ids) / per_group;
         r = (id - main_ids) % per_group;
     }
-    const int b = grp / a.num_kv_heads, g = grp % a.num_kv_heads;
-    const int qt = a.num_q_tiles - 1 - r / a.group;
-    const int h = g * a.group + r % a.group;
+    TileCoords tc;
+    tc.b = grp / a.num_kv_heads;
+    tc.g = grp % a.num_kv_heads;
+    tc.qt = a.num_q_tiles - 1 - r / a.group;
+    tc.h = tc.g * a.group + r % a.group;
+    return tc;
+}
+
+// Q^T operands of the wave's rows (rows past the chunk read its last row and
+// are never stored); the running state starts empty.
+template <int D>
+__device__ __forceinline__ void init_rows(WaveState<D> &w, const PrefillArgs &a, int q0, int q_len,
+                                          int row_w, int h, int lane)
+{
+    const int r32 = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int rb = 0; rb < Cfg<D>::kNRB; ++rb) {
+        const int row = row_w + 32 * rb + r32;
+        w.m[rb] = kNegInf;
+        w.lsum[rb] = 0.f;
+        w.pop[rb][0] = w.pop[rb][1] = u32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            w.acc[rb][db] = f32x16_t{};
+        const uint16_t *qrow = a.q + ((size_t)(q0 + min(row, q_len - 1)) * a.num_q_heads + h) * D;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            w.qop[rb][kk] = row < q_len ? *(const u32x4_t *)(qrow + 16 * kk + 8 * half)
+                                        : u32x4_t{0, 0, 0, 0};
+    }
+}
+
+// Epilogue: fold the sink into each row's normalisation, then write the
+// wave's rows through its own LDS staging area (32 NRB rows of d bf16) so
+// that every global store covers whole 16-byte chunks of contiguous output
+// rows.  The staging rows are XOR-swizzled by 16-byte chunk (both the 8-byte
+// writes and the 16-byte reads are then free of bank conflicts).
+template <int D>
+__device__ __forceinline__ void store_rows(const WaveState<D> &w, uint16_t *stage,
+                                           const PrefillArgs &a, int q0, int q_len, int row_w,
+                                           int h, int lane)
+{
+    constexpr int NRB = Cfg<D>::kNRB;
+    constexpr int kC16 = D / 8;  // 16-byte chunks per row
+    const int r32 = lane & 31, half = lane >> 5;
+    auto st_at = [&](int r, int c16) { return r * D + 8 * (c16 ^ (r & (kC16 - 1))); };
+    const float sink2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        float lx, ly;
+        halves(w.lsum[rb], lx, ly);
+        const float lsum = lx + ly;
+        const float M = fmaxf(w.m[rb], sink2);
+        float scale = 0.f;
+        if (M != kNegInf) {
+            const float f = w.m[rb] == kNegInf ? 0.f : exp2_fast(w.m[rb] - M);
+            const float den = lsum * f + (sink2 == kNegInf ? 0.f : exp2_fast(sink2 - M));
+            scale = den > 0.f ? f / den : 0.f;
+        }
+        // lane l holds dims 32 db + 8 r4 + 4 (l/32) .. +3 of row 32 rb + l%32
+        const int r = 32 * rb + r32;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x16_t &o = w.acc[rb][db];
+                const u32x2_t v = {pack_bf16(o[4 * r4] * scale, o[4 * r4 + 1] * scale),
+                                   pack_bf16(o[4 * r4 + 2] * scale, o[4 * r4 + 3] * scale)};
+                *(u32x2_t *)&stage[st_at(r, 4 * db + r4) + 4 * half] = v;
+            }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
+    __builtin_amdgcn_wave_barrier();
+    // 64 lanes copy 64 / kC16 rows per pass, kC16 lanes per row
+    constexpr int kRowsPerPass = 64 / kC16;
+#pragma unroll
+    for (int r0 = 0; r0 < 32 * NRB; r0 += kRowsPerPass) {
+        const int r = r0 + lane / kC16, c16 = lane % kC16;
+        const int row = row_w + r;
+        const u32x4_t v = *(const u32x4_t *)&stage[st_at(r, c16)];
+        if (row < q_len)
+            *(u32x4_t *)(a.out + ((size_t)(q0 + row) * a.num_q_heads + h) * D + 8 * c16) = v;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
+{
+    using C = Cfg<D>;
+    constexpr int NRB = C::kNRB;
+    const TileCoords tc = tile_of(a);
+    const int b = tc.b, g = tc.g, h = tc.h, qt = tc.qt;
 
     const int q0 = a.cu_seqlens_q[b];
     const int q_len = a.cu_seqlens_q[b + 1] - q0;
@@ -612,21 +758,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     // Q while the first tiles load; one wait covers both (the compiler then
     // knows the Q registers are ready and adds no waits inside the loops)
     WaveState<D> w;
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-        const int row = row_w + 32 * rb + r32;
-        w.m[rb] = kNegInf;
-        w.lsum[rb] = 0.f;
-        w.pop[rb][0] = w.pop[rb][1] = u32x4_t{0, 0, 0, 0};
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-            w.acc[rb][db] = f32x16_t{};
-        const uint16_t *qrow = a.q + ((size_t)(q0 + min(row, q_len - 1)) * a.num_q_heads + h) * D;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            w.qop[rb][kk] = row < q_len ? *(const u32x4_t *)(qrow + 16 * kk + 8 * half)
-                                        : u32x4_t{0, 0, 0, 0};
-    }
+    init_rows<D>(w, a, q0, q_len, row_w, h, lane);
 
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
@@ -729,52 +861,75 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
         exact_rows<D>(w, lds + wave * (C::kLdsBytes / 2 / kWaves), a, bt, L, head_off, nb, wpf, thr,
                       lane);
 
-    // Epilogue: fold the sink into each row's normalisation, then write the
-    // wave's rows through its own part of the (now free) LDS so that every
-    // global store covers whole 16-byte chunks of contiguous output rows.
-    // The staging rows are XOR-swizzled by 16-byte chunk (both the 8-byte
-    // writes and the 16-byte reads are then free of bank conflicts).
-    constexpr int kC16 = D / 8;  // 16-byte chunks per row
-    uint16_t *stage = lds + wave * (C::kLdsBytes / 2 / kWaves);
-    auto st_at = [&](int r, int c16) { return r * D + 8 * (c16 ^ (r & (kC16 - 1))); };
-    const float sink2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-        float lx, ly;
-        halves(w.lsum[rb], lx, ly);
-        const float lsum = lx + ly;
-        const float M = fmaxf(w.m[rb], sink2);
-        float scale = 0.f;
-        if (M != kNegInf) {
-            const float f = w.m[rb] == kNegInf ? 0.f : exp2_fast(w.m[rb] - M);
-            const float den = lsum * f + (sink2 == kNegInf ? 0.f : exp2_fast(sink2 - M));
-            scale = den > 0.f ? f / den : 0.f;
-        }
-        // lane l holds dims 32 db + 8 r4 + 4 (l/32) .. +3 of row 32 rb + l%32
-        const int r = 32 * rb + r32;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const f32x16_t &o = w.acc[rb][db];
-                const u32x2_t v = {pack_bf16(o[4 * r4] * scale, o[4 * r4 + 1] * scale),
-                                   pack_bf16(o[4 * r4 + 2] * scale, o[4 * r4 + 3] * scale)};
-                *(u32x2_t *)&stage[st_at(r, 4 * db + r4) + 4 * half] = v;
-            }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
-    __builtin_amdgcn_wave_barrier();
-    // 64 lanes copy 64 / kC16 rows per pass, kC16 lanes per row
-    constexpr int kRowsPerPass = 64 / kC16;
-#pragma unroll
-    for (int r0 = 0; r0 < 32 * NRB; r0 += kRowsPerPass) {
-        const int r = r0 + lane / kC16, c16 = lane % kC16;
-        const int row = row_w + r;
-        const u32x4_t v = *(const u32x4_t *)&stage[st_at(r, c16)];
-        if (row < q_len)
-            *(u32x4_t *)(a.out + ((size_t)(q0 + row) * a.num_q_heads + h) * D + 8 * c16) = v;
-    }
+    // Epilogue through this wave's part of the (now free) LDS.
+    store_rows<D>(w, lds + wave * (C::kLdsBytes / 2 / kWaves), a, q0, q_len, row_w, h, lane);
 }
+
+// Sliding-window prefill ("GPT OSS" model notes, section 4.1: even layers
+// attend within a local window of W positions; section 11: the window comes
+// with each call).  A row at position p sees keys p - W + 1 .. p, so a wave
+// needs only the blocks from its first row's oldest key to its last row:
+// few for the windows the notes name (W = 128: at most 7 per wave at d = 64).
+// Each wave streams its own blocks from the paged cache into its own LDS
+// tiles, the next block in registers while the current one is computed, and
+// runs the plain online softmax on each (a row's first blocks may hold none
+// of its keys, so no reference is fixed in advance).  The four waves of a
+// workgroup never wait for one another.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void prefill_window_bf16(PrefillArgs a)
+{
+    using C = Cfg<D>;
+    constexpr int NRB = C::kNRB;
+    const TileCoords tc = tile_of(a);
+    const int q0 = a.cu_seqlens_q[tc.b];
+    const int q_len = a.cu_seqlens_q[tc.b + 1] - q0;
+    const int row0 = tc.qt * C::kBM;
+    if (row0 >= q_len)
+        return;  // uniform over the workgroup
+    const int L = a.seq_lens[tc.b];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int r32 = lane & 31, half = lane >> 5;
+    const int shift = L - q_len;  // position of query row i is shift + i
+    const int row_w = row0 + 32 * NRB * wave;
+    const int wpf = shift + row_w;  // position of the wave's first row
+    const int wave_last = min(row_w + 32 * NRB - 1, q_len - 1);
+    const int nb = row_w < q_len ? (min(shift + wave_last + 1, L) + kKB - 1) / kKB : 0;
+    const int b_lo = max(wpf - a.window + 1, 0) / kKB;
+
+    extern __shared__ __align__(16) uint16_t lds[];
+    uint16_t *kt = lds + wave * (2 * kKB * D);
+    uint16_t *vt = kt + kKB * D;
+    const int32_t *bt = a.block_table + (size_t)tc.b * a.max_pages;
+    const size_t head_off = (size_t)tc.g * 16 * D;
+
+    WaveState<D> w;
+    init_rows<D>(w, a, q0, q_len, row_w, tc.h, lane);
+    const int thr = wpf + r32 - 4 * half;  // minus the block start
+    // one register block: stored to LDS, then refilled with the next block,
+    // whose loads are in flight while the current one is computed
+    // (d = 64; at d = 128 the registers are needed by the block itself, and
+    // each block is fetched when its turn comes)
+    constexpr bool kAhead = D == 64;
+    RawBlock<D> raw;
+    if (kAhead && b_lo < nb)
+        fetch_block<D>(raw, a, bt, L, head_off, kKB * b_lo, lane);
+    for (int blk = b_lo; blk < nb; ++blk) {
+        const int k0 = kKB * blk;
+        if (!kAhead)
+            fetch_block<D>(raw, a, bt, L, head_off, k0, lane);
+        stash_block<D>(raw, kt, vt, lane);
+        if (kAhead && blk + 1 < nb)
+            fetch_block<D>(raw, a, bt, L, head_off, k0 + kKB, lane);
+        exact_block<D, true>(w, kt, vt, true, thr - k0, a.window, a.scale_log2, lane);
+    }
+    // the staging area of the epilogue is the wave's own K tile and more:
+    // 32 NRB rows of d bf16 fit in its 2 * 32 * d elements
+    store_rows<D>(w, kt, a, q0, q_len, row_w, tc.h, lane);
+}
+
+template <int D>
+constexpr int kWindowLdsBytes = kWaves * 2 * kKB * D * 2;
 
 template <int D>
 hipError_t launch_d(const PrefillLaunch &p)
@@ -797,10 +952,23 @@ hipError_t launch_d(const PrefillLaunch &p)
     a.num_q_tiles = (p.max_q_len + C::kBM - 1) / C::kBM;
     const int groups = p.num_seqs * p.num_kv_heads;
     a.xcd_groups = groups / 8 * 8;
+    a.window = p.window;
     a.scale_log2 = p.scale * kLog2e;
     const long long wgs = (long long)groups * a.group * a.num_q_tiles;
     if (wgs > 0x7fffffffLL)
         return hipErrorInvalidValue;
+    if (p.window > 0 && p.window < p.max_seq_len) {
+        // a window that leaves out some key of some row (otherwise the
+        // causal kernel below computes exactly the same rows)
+        static const hipError_t wattr = hipFuncSetAttribute(
+            (const void *)prefill_window_bf16<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+            kWindowLdsBytes<D>);
+        if (wattr != hipSuccess)
+            return wattr;
+        hipLaunchKernelGGL(prefill_window_bf16<D>, dim3((unsigned)wgs), dim3(kThreads),
+                           kWindowLdsBytes<D>, p.stream, a);
+        return hipGetLastError();
+    }
     // more than 64 KiB of LDS (d = 128) has to be allowed once per kernel
     static const hipError_t attr = hipFuncSetAttribute(
         (const void *)prefill_bf16<D>, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);

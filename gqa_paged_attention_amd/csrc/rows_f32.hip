@@ -26,6 +26,7 @@ struct RowsArgs {
     const float *__restrict__ sinks;
     float *__restrict__ out;
     int num_seqs, num_q_heads, num_kv_heads, group, max_pages;
+    int window;  // sliding window W: keys p - W + 1 .. p (0: none)
     float scale_log2;
 };
 
@@ -49,6 +50,8 @@ __global__ __launch_bounds__(64) void rows_f32(RowsArgs a)
     }
     const int L = a.seq_lens[b];
     const int n_vis = max(L - q_len + i + 1, 0);
+    // oldest visible key ("GPT OSS" model notes, section 4.1: local window)
+    const int k_lo = (a.window > 0 && n_vis > a.window) ? n_vis - a.window : 0;
     const int g = h / a.group;
 
     __shared__ float sq[D];
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(64) void rows_f32(RowsArgs a)
         acc[j] = 0.f;
     float m = kNegInf, l = 0.f;
 
-    for (int kb = 0; kb < n_vis; kb += 64) {
+    for (int kb = k_lo; kb < n_vis; kb += 64) {
         const int key = kb + lane;
         float x = kNegInf;
         if (key < n_vis) {
@@ -124,7 +127,8 @@ hipError_t launch_rows_f32(int num_seqs, int num_q_heads, int num_kv_heads, int 
                            int max_pages_per_seq, int total_q, const void *q,
                            const void *k_cache, const void *v_cache, const int32_t *block_table,
                            const int32_t *seq_lens, const int32_t *cu_seqlens_q,
-                           const float *sinks, float scale, void *out, hipStream_t stream)
+                           const float *sinks, float scale, int window, void *out,
+                           hipStream_t stream)
 {
     if (total_q == 0 || num_seqs == 0)
         return hipSuccess;
@@ -142,6 +146,7 @@ hipError_t launch_rows_f32(int num_seqs, int num_q_heads, int num_kv_heads, int 
     a.num_kv_heads = num_kv_heads;
     a.group = num_q_heads / num_kv_heads;
     a.max_pages = max_pages_per_seq;
+    a.window = window;
     a.scale_log2 = scale * kLog2e;
     return head_dim == 64 ? launch_d<64>(a, total_q, stream) : launch_d<128>(a, total_q, stream);
 }

@@ -194,6 +194,43 @@ int attn_sinks_prefill(int dtype, int num_seqs, int num_q_heads, int num_kv_head
                        const int32_t *cu_seqlens_q, const float *sinks, float scale, void *out,
                        void *stream);
 
+/*
+ * Sliding-window variants.  The "GPT OSS" model notes give the model's even
+ * layers a local attention window (section 4.1: SWA, window 128 by default)
+ * and pass the per-layer window with each call into the paged kernel
+ * (section 11).  With window = W > 0 the query at position p sees only the
+ * keys at positions p - W + 1 .. p (its own included); the sink stays in
+ * every row's softmax whatever the window:
+ *
+ *     s_j = scale * <q_i,h , K_b,g[j]>          j = max(0, p - W + 1) .. p
+ *
+ * and the rest of the definition above is unchanged.  window = 0 means no
+ * window: these calls then run exactly the code of attn_sinks_decode and
+ * attn_sinks_prefill and return bit-identical results.  A window of at least
+ * max_seq_len also leaves every row whole and gives the same bits.  window <
+ * 0 returns ATTN_ERR_SHAPE.  All other arguments, the workspace of the decode
+ * (size from attn_sinks_decode_workspace_bytes, which covers every window),
+ * ownership, checks and errors are as for the unwindowed calls.
+ *
+ * Decode reads only the blocks of each sequence that hold its last W keys.
+ * Prefill with 0 < W < max_seq_len runs a kernel of its own in which each
+ * wave streams the few blocks its rows need straight from the paged cache.
+ */
+int attn_sinks_decode_window(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                             int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                             int max_seq_len, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *block_table,
+                             const int32_t *seq_lens, const float *sinks, float scale, int window,
+                             void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+int attn_sinks_prefill_window(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                              int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                              int total_q, int max_q_len, int max_seq_len, const void *q,
+                              const void *k_cache, const void *v_cache,
+                              const int32_t *block_table, const int32_t *seq_lens,
+                              const int32_t *cu_seqlens_q, const float *sinks, float scale,
+                              int window, void *out, void *stream);
+
 /* Static English text for a status code (never NULL). */
 const char *attn_sinks_status_string(int status);
 

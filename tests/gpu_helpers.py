@@ -29,7 +29,9 @@ def require_gpu():
     ga.library()  # raises if the HIP library is missing
 
 
-def run_decode(batch_cpu, max_seq_len=None, sync=True):
+def run_decode(batch_cpu, max_seq_len=None, sync=True, window=None):
+    """attn_sinks_decode through the C ABI (attn_sinks_decode_window when
+    `window` is given); returns the output on the CPU."""
     require_gpu()
     g = batch_cpu.to("cuda")
     out = torch.empty_like(g.q)
@@ -37,19 +39,29 @@ def run_decode(batch_cpu, max_seq_len=None, sync=True):
     nbytes = ga.attn_sinks_decode_workspace_bytes(g.num_seqs, g.num_q_heads, g.num_kv_heads,
                                                   g.head_dim, msl)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
-    ga.attn_sinks_decode(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.sinks, g.scale,
-                         out, ws, msl)
+    args = (g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.sinks, g.scale)
+    if window is None:
+        ga.attn_sinks_decode(*args, out, ws, msl)
+    else:
+        ga.attn_sinks_decode_window(*args, window, out, ws, msl)
     if sync:
         torch.cuda.synchronize()
     return out.cpu()
 
 
-def run_prefill(batch_cpu, sync=True):
+def run_prefill(batch_cpu, sync=True, window=None):
+    """attn_sinks_prefill through the C ABI (attn_sinks_prefill_window when
+    `window` is given); returns the output on the CPU."""
     require_gpu()
     g = batch_cpu.to("cuda")
     out = torch.empty_like(g.q)
-    ga.attn_sinks_prefill(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.cu_seqlens_q,
-                          g.sinks, g.scale, out, batch_cpu.max_q_len, batch_cpu.max_seq_len)
+    args = (g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.cu_seqlens_q, g.sinks,
+            g.scale)
+    if window is None:
+        ga.attn_sinks_prefill(*args, out, batch_cpu.max_q_len, batch_cpu.max_seq_len)
+    else:
+        ga.attn_sinks_prefill_window(*args, window, out, batch_cpu.max_q_len,
+                                     batch_cpu.max_seq_len)
     if sync:
         torch.cuda.synchronize()
     return out.cpu()
@@ -81,8 +93,8 @@ def compare(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str) -> dict:
     return stats
 
 
-def oracle_full(batch_cpu):
-    return oracle.attention(batch_cpu, threads=ORACLE_THREADS)
+def oracle_full(batch_cpu, window=0):
+    return oracle.attention(batch_cpu, threads=ORACLE_THREADS, window=window)
 
 
 def sample_rows(batch_cpu, n_rows: int, seed: int):
@@ -102,8 +114,9 @@ def sample_rows(batch_cpu, n_rows: int, seed: int):
     return toks, heads.astype(np.int32)
 
 
-def check_sampled(got: torch.Tensor, batch_cpu, n_rows: int, seed: int, what: str) -> dict:
+def check_sampled(got: torch.Tensor, batch_cpu, n_rows: int, seed: int, what: str,
+                  window: int = 0) -> dict:
     toks, heads = sample_rows(batch_cpu, n_rows, seed)
-    ref = oracle.attention_rows(batch_cpu, toks, heads, threads=ORACLE_THREADS)
+    ref = oracle.attention_rows(batch_cpu, toks, heads, threads=ORACLE_THREADS, window=window)
     return compare(got[torch.as_tensor(toks), torch.as_tensor(heads.astype(np.int64))], ref,
                    batch_cpu.dtype, what)

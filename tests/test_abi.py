@@ -160,3 +160,39 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ga, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         ga.library()
+
+
+def _decode_window(lib, window, **kw):
+    args = dict(dtype=1, B=2, Hq=8, Hkv=2, d=64, P=16, pages=8, max_pages=4, max_len=64,
+                q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, sinks=None, scale=0.125, out=FAKE,
+                ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    return lib.attn_sinks_decode_window(
+        args["dtype"], args["B"], args["Hq"], args["Hkv"], args["d"], args["P"], args["pages"],
+        args["max_pages"], args["max_len"], args["q"], args["k"], args["v"], args["bt"],
+        args["sl"], args["sinks"], ctypes.c_float(args["scale"]), window, args["out"],
+        args["ws"], ctypes.c_size_t(args["ws_bytes"]), None)
+
+
+def _prefill_window(lib, window, **kw):
+    args = dict(dtype=1, B=2, Hq=8, Hkv=2, d=64, P=16, pages=8, max_pages=4, total_q=40,
+                max_q=32, max_len=64, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, cu=FAKE,
+                sinks=None, scale=0.125, out=FAKE)
+    args.update(kw)
+    return lib.attn_sinks_prefill_window(
+        args["dtype"], args["B"], args["Hq"], args["Hkv"], args["d"], args["P"], args["pages"],
+        args["max_pages"], args["total_q"], args["max_q"], args["max_len"], args["q"],
+        args["k"], args["v"], args["bt"], args["sl"], args["cu"], args["sinks"],
+        ctypes.c_float(args["scale"]), window, args["out"], None)
+
+
+@pytest.mark.parametrize("call", [_decode_window, _prefill_window], ids=["decode", "prefill"])
+def test_window_entry_points_check_like_the_plain_ones(lib, call):
+    assert call(lib, -1) == ERR_SHAPE
+    assert call(lib, -1000) == ERR_SHAPE
+    assert call(lib, 128, dtype=2) == ERR_UNSUPPORTED
+    assert call(lib, 128, q=None) == ERR_NULL
+    assert call(lib, 128, out=FAKE + 8) == ERR_ALIGN
+    assert call(lib, 128, scale=float("nan")) == ERR_SHAPE
+    assert call(lib, 0, B=0) == OK
+    assert call(lib, 128, B=0) == OK

@@ -1,0 +1,104 @@
+"""GPU parity of the sliding-window entry points against the windowed oracle.
+
+The window follows the "GPT OSS" model notes (section 4.1: even layers
+attend within a local window, 128 by default; section 11: the window is
+passed per call): the query at position p sees keys p - W + 1 .. p and the
+sink.  Cases cover windows shorter than, equal to and longer than the
+32-token decode blocks and 16-token pages, windows that start mid-page,
+sequences shorter than the window, chunks over cached prefixes, both head
+dims and fp32, plus the full-size gpt-oss shapes at W = 128.
+"""
+import zlib
+
+import pytest
+import torch
+
+from gqa_paged_attention_amd import workloads as wl
+from tests.gpu_helpers import check_sampled, compare, note, oracle_full, run_decode, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+WINDOWS = [1, 5, 16, 31, 32, 33, 100, 128, 1000]
+
+DECODE_CASES = [
+    # id, dtype, seq_lens, Hq, Hkv, d, sink_mode
+    ("d64_g8", "bf16", [1, 15, 16, 17, 33, 100, 129, 1000, 2049], 16, 2, 64, "normal"),
+    ("d128_g16", "bf16", [1, 31, 32, 200, 2049], 32, 2, 128, "normal"),
+    ("d64_g1_nosink", "bf16", [7, 300, 64, 4097], 4, 4, 64, "none"),
+    ("f32_d64", "f32", [1, 17, 300], 8, 2, 64, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_window(case):
+    name, dt, L, Hq, Hkv, d, sm = case
+    b = wl.small_batch(zlib.crc32(name.encode()) % 1000 + 3, dt, L, [1] * len(L), Hq, Hkv, d,
+                       sink_mode=sm)
+    for w in WINDOWS:
+        note(f"decode window {w} {name}: L={L} Hq={Hq} Hkv={Hkv} d={d} {dt}")
+        compare(run_decode(b, window=w), oracle_full(b, window=w), dt,
+                f"decode {name} window {w}")
+
+
+PREFILL_CASES = [
+    # id, dtype, seq_lens, q_lens, Hq, Hkv, d, sink_mode
+    ("d64_full_causal", "bf16", [1, 17, 130, 300, 600], [1, 17, 130, 300, 600], 16, 2, 64,
+     "normal"),
+    ("d64_chunks_over_prefix", "bf16", [500, 1000, 64], [100, 257, 1], 16, 2, 64, "normal"),
+    ("d128_full", "bf16", [200, 333], [200, 333], 8, 2, 128, "normal"),
+    ("d128_chunk", "bf16", [700], [129], 16, 1, 128, "none"),
+    ("f32_d64", "f32", [40, 150], [40, 100], 8, 2, 64, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_window(case):
+    name, dt, L, Lq, Hq, Hkv, d, sm = case
+    b = wl.small_batch(zlib.crc32(name.encode()) % 1000 + 11, dt, L, Lq, Hq, Hkv, d,
+                       sink_mode=sm)
+    for w in (1, 17, 32, 64, 128, 300):
+        note(f"prefill window {w} {name}: L={L} Lq={Lq} Hq={Hq} Hkv={Hkv} d={d} {dt}")
+        compare(run_prefill(b, window=w), oracle_full(b, window=w), dt,
+                f"prefill {name} window {w}")
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_no_window_and_wide_window_are_the_plain_calls(dt):
+    """window 0, and any window of at least max_seq_len, give the bits of the
+    unwindowed entry points."""
+    d = wl.small_batch(201, dt, [900, 33, 2049], [1, 1, 1], 16, 2, 64, sink_mode="normal")
+    note(f"decode window 0 / wide vs plain {dt}")
+    plain = run_decode(d)
+    for w in (0, d.max_seq_len, d.max_seq_len + 5):
+        assert torch.equal(_bits(run_decode(d, window=w)), _bits(plain)), f"decode window {w}"
+    p = wl.small_batch(202, dt, [300, 500], [300, 200], 8, 2, 64, sink_mode="normal")
+    note(f"prefill window 0 / wide vs plain {dt}")
+    plain = run_prefill(p)
+    for w in (0, p.max_seq_len, 10 ** 6):
+        assert torch.equal(_bits(run_prefill(p, window=w)), _bits(plain)), f"prefill window {w}"
+
+
+def test_window_runs_are_deterministic():
+    d = wl.small_batch(203, "bf16", [3000, 129, 77], [1, 1, 1], 16, 2, 64, sink_mode="normal")
+    p = wl.small_batch(204, "bf16", [700, 300], [700, 100], 16, 2, 64, sink_mode="normal")
+    note("window determinism")
+    assert torch.equal(_bits(run_decode(d, window=128)), _bits(run_decode(d, window=128)))
+    assert torch.equal(_bits(run_prefill(p, window=128)), _bits(run_prefill(p, window=128)))
+
+
+def test_full_gptoss_decode_window128():
+    b = wl.gptoss_decode(0)
+    note("full gpt-oss decode, window 128 (every row)")
+    compare(run_decode(b, window=128), oracle_full(b, window=128), "bf16",
+            "gpt-oss decode window 128")
+
+
+def test_full_gptoss_prefill_window128():
+    b = wl.gptoss_prefill(0)
+    note("full gpt-oss prefill, window 128 (sampled rows)")
+    check_sampled(run_prefill(b, window=128), b, 3000, 5, "gpt-oss prefill window 128",
+                  window=128)
