@@ -74,6 +74,35 @@ def prefill_flops(batch) -> int:
     return 4 * batch.head_dim * batch.num_q_heads * pairs
 
 
+def window_decode_bytes(batch, window: int) -> int:
+    """Bytes a sliding-window decode pass must move: K and V of the last
+    `window` keys of every sequence, q, out, the table entries of the pages
+    holding them, seq_lens and sinks."""
+    elem = 4 if batch.dtype == "f32" else 2
+    L = batch.seq_lens.to("cpu").long()
+    lo = (L - window).clamp(min=0)
+    kv = int((L - lo).sum()) * batch.num_kv_heads * batch.head_dim * 2 * elem
+    qo = 2 * batch.num_seqs * batch.num_q_heads * batch.head_dim * elem
+    table = int(((L - 1) // 16 - lo // 16 + 1).clamp(min=0).sum()) * 4
+    return kv + qo + table + 4 * batch.num_seqs + 4 * batch.num_q_heads
+
+
+def window_prefill_work(batch, window: int):
+    """(flops, bytes) of a sliding-window prefill: 4 d Hq per visible
+    (query, key) pair; q and out once, and K and V of every key some row of
+    the chunk sees, once."""
+    elem = 4 if batch.dtype == "f32" else 2
+    flops = kv = 0
+    L = batch.seq_lens.tolist()
+    Lq = batch.q_lens.tolist()
+    for l, lq in zip(L, Lq):
+        flops += sum(min(p + 1, window) for p in range(l - lq, l))
+        kv += l - max(l - lq - window + 1, 0)
+    flops *= 4 * batch.head_dim * batch.num_q_heads
+    qo = 2 * batch.total_q * batch.num_q_heads * batch.head_dim * elem
+    return flops, qo + kv * batch.num_kv_heads * batch.head_dim * 2 * elem
+
+
 # ------------------------------------------------------------------ timing
 
 class Timer:
@@ -178,6 +207,44 @@ def bench_prefill(torch, ga, timer, batch_cpu, steps, warmup, label):
     tf = flops / (r["step_ms"] * 1e-3) / 1e12
     return {"workload": label, "algorithmic_flops": flops, "ms": round(r["step_ms"], 4),
             "TFLOP_per_s": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}, out
+
+
+def bench_window(torch, ga, timer, steps, warmup, wl, window=128):
+    """The gpt-oss decode and prefill workloads under a sliding window of 128
+    (the local layers of the "GPT OSS" notes, section 4.1): each call timed
+    whole, against the HBM roofline (decode) and against the larger of the
+    HBM and MFMA times (prefill)."""
+    dec = wl.gptoss_decode(0)
+    g = dec.to("cuda")
+    out = torch.empty_like(g.q)
+    ws = decode_workspace(torch, ga, g)
+    r = timer.run([("decode_window", lambda: ga.attn_sinks_decode_window(
+        g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.sinks, g.scale, window, out,
+        ws, g.max_seq_len))], steps, warmup, flush=True)
+    nb = window_decode_bytes(dec, window)
+    d_gbs = nb / (r["step_ms"] * 1e-3) / 1e9
+    del g, out, ws
+    pre = wl.gptoss_prefill(0)
+    gp = pre.to("cuda")
+    outp = torch.empty_like(gp.q)
+    rp = timer.run([("prefill_window", lambda: ga.attn_sinks_prefill_window(
+        gp.q, gp.k_cache, gp.v_cache, gp.block_table, gp.seq_lens, gp.cu_seqlens_q, gp.sinks,
+        gp.scale, window, outp, pre.max_q_len, pre.max_seq_len))], steps, warmup, flush=True)
+    fl, pb = window_prefill_work(pre, window)
+    t = rp["step_ms"] * 1e-3
+    t_hbm, t_mfma = pb / (HBM_PEAK_GBS * 1e9), fl / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    return {
+        "window": window,
+        "decode": {"workload": f"gpt-oss decode workload, sliding window {window}",
+                   "algorithmic_bytes": nb, "ms": round(r["step_ms"], 4),
+                   "GB_per_s": round(d_gbs, 1), "hbm_frac": round(d_gbs / HBM_PEAK_GBS, 4)},
+        "prefill": {"workload": f"gpt-oss prefill workload, sliding window {window}",
+                    "algorithmic_flops": fl, "algorithmic_bytes": pb,
+                    "ms": round(rp["step_ms"], 4),
+                    "TFLOP_per_s": round(fl / t / 1e12, 1), "GB_per_s": round(pb / t / 1e9, 1),
+                    "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                    "roofline_frac": round(max(t_hbm, t_mfma) / t, 4)},
+    }
 
 
 def bench_mixed(torch, ga, timer, steps, warmup, wl):
@@ -383,6 +450,9 @@ def main():
         log("generating mixed workload")
         extra["mixed"] = bench_mixed(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["mixed"]))
+        log("sliding-window legs (window 128)")
+        extra["sliding_window"] = bench_window(torch, ga, timer, K, W, wl)
+        log(json.dumps(extra["sliding_window"]))
         log("generating qwen decode workload (about a minute)")
         qw = wl.qwen_decode(0)
         q_res, _, keep = bench_decode(torch, ga, timer, qw, max(K // 2, 3), max(W // 2, 1),
