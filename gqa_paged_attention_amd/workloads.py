@@ -278,6 +278,32 @@ def from_logical(dtype: str, q, k, v, seq_lens, q_lens, sinks, scale: float,
                     scale, page_size, True, poison)
 
 
+def split_new_tokens(batch: PagedBatch):
+    """For a batch whose query rows are the newest tokens of each sequence
+    (the last Lq_b of its L_b keys), return (pool_before, k_new, v_new):
+    the same batch with those tokens' K/V slots overwritten with NaN (the pool
+    as it stands before the append), and the tokens' K/V rows
+    [total_q][Hkv][d] in query order.  Pure data movement, for the append
+    tests; it needs nothing but the table and the pool."""
+    cu = batch.cu_seqlens_q.tolist()
+    P = batch.page_size
+    k_old = batch.k_cache.clone()
+    v_old = batch.v_cache.clone()
+    k_new = torch.empty(batch.total_q, batch.num_kv_heads, batch.head_dim, dtype=k_old.dtype)
+    v_new = torch.empty_like(k_new)
+    for b in range(batch.num_seqs):
+        L = int(batch.seq_lens[b])
+        n = cu[b + 1] - cu[b]
+        for i in range(n):
+            pos = L - n + i
+            page, slot = int(batch.block_table[b, pos // P]), pos % P
+            k_new[cu[b] + i] = batch.k_cache[page, :, slot]
+            v_new[cu[b] + i] = batch.v_cache[page, :, slot]
+            k_old[page, :, slot] = float("nan")
+            v_old[page, :, slot] = float("nan")
+    return replace(batch, k_cache=k_old, v_cache=v_old), k_new, v_new
+
+
 # --------------------------------------------------------------------------
 # The five named workloads.  Shapes follow the attention of gpt-oss-20b
 # (64 q heads, 8 KV heads, head_dim 64) and Qwen3-235B (64 q heads, 4 KV

@@ -5,7 +5,8 @@ CPU-baseline leg may import this package.  The product path (the HIP library
 and its binding) never imports, links or calls it, and it never touches the
 GPU or the HIP library.
 
-Two independent implementations of one definition live here:
+Two independent implementations of one definition live here (plus the KV
+append of ``append_kv``, which the attention step follows):
 
 * ``attention_rows`` / ``attention`` -- ctypes binding of ``oracle.c``: fp64,
   OpenMP over (query token, head) rows, two passes over the keys in logical
@@ -129,3 +130,31 @@ def attention(batch, threads: Optional[int] = None, with_lse: bool = False, lib=
         out, lse = res
         return out.reshape(T, H, batch.head_dim), lse.reshape(T, H)
     return res.reshape(T, H, batch.head_dim)
+
+
+def append_kv(batch, k_new: torch.Tensor, v_new: torch.Tensor):
+    """The cache after appending the newest tokens ("GPT OSS" model notes,
+    section 3: the layer's (K, V) are appended to the KV cache before the
+    attention step; section 11: paged K/V per layer).
+
+    Token i of the n_b = cu_seqlens_q[b+1] - cu_seqlens_q[b] new tokens of
+    sequence b sits at position p = L_b - n_b + i (seq_lens already count
+    them); its rows go to page block_table[b][p // page_size], slot
+    p % page_size, of every KV head.  k_new / v_new are [total_q][Hkv][d] in
+    query order.  Returns new (k_cache, v_cache) CPU tensors; nothing else
+    changes.  Plain Python loop over the tokens.
+    """
+    k = batch.k_cache.clone()
+    v = batch.v_cache.clone()
+    cu = batch.cu_seqlens_q.tolist()
+    table = batch.block_table.tolist()
+    P = batch.page_size
+    for b in range(batch.num_seqs):
+        L = int(batch.seq_lens[b])
+        n = cu[b + 1] - cu[b]
+        for i in range(n):
+            p = L - n + i
+            page = table[b][p // P]
+            k[page, :, p % P, :] = k_new[cu[b] + i]
+            v[page, :, p % P, :] = v_new[cu[b] + i]
+    return k, v

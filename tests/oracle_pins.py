@@ -24,7 +24,12 @@ The facts used:
     force with the same window; plain softmax attention under a band mask
     (torch SDPA) times sigmoid(LSE - sink); W = 1 is the single-key closed
     form on the query's own key; and a windowed decode equals an unwindowed
-    decode over a pool that holds only the last W tokens.
+    decode over a pool that holds only the last W tokens;
+  * KV append (model notes, section 3: K and V are appended before the
+    attention step): appending the newest tokens into a pool where their
+    slots are blank rebuilds, bit for bit, the pool the input generator laid
+    out with those tokens already in place; the tiny workload's documented
+    slot of token 256 is the one written.
 """
 from __future__ import annotations
 
@@ -32,6 +37,8 @@ import json
 import math
 import os
 from fractions import Fraction
+
+from dataclasses import replace
 
 import numpy as np
 import torch
@@ -337,7 +344,40 @@ def pin_window_truncation(attn):
         _close(attn(b, window=w), attn(t), 1e-12, 1e-14, f"window {w} vs truncated pool")
 
 
+# ----------------------------------------------------------------- KV append
+
+def _same_bits(a, b):
+    if a.dtype == torch.bfloat16:
+        return torch.equal(a.view(torch.int16), b.view(torch.int16))
+    return torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def check_append(append):
+    """`append(batch, k_new, v_new) -> (k_cache, v_cache)` against the pools
+    the generator lays out directly."""
+    for seed, dt, L, Lq, Hkv, d in ((141, "bf16", [33, 1, 70, 16], [4, 1, 70, 16], 2, 64),
+                                     (142, "f32", [5, 129, 64], [5, 30, 1], 3, 128),
+                                     (143, "bf16", [0, 17, 40], [0, 17, 2], 1, 64)):
+        full = wl.small_batch(seed, dt, L, Lq, 4 * Hkv, Hkv, d, sink_mode="normal")
+        before, k_new, v_new = wl.split_new_tokens(full)
+        assert not _same_bits(before.k_cache, full.k_cache) or sum(Lq) == 0
+        k, v = append(before, k_new, v_new)
+        assert _same_bits(k, full.k_cache), f"append K differs (seed {seed})"
+        assert _same_bits(v, full.v_cache), f"append V differs (seed {seed})"
+    pre, dec, (page, slot, nk, nv) = wl.tiny_fp32(0)
+    q1 = replace(dec, cu_seqlens_q=torch.tensor([0, 1], dtype=torch.int32))
+    k, v = append(replace(q1, k_cache=pre.k_cache, v_cache=pre.v_cache), nk[None], nv[None])
+    assert _same_bits(k[page, :, slot], nk) and _same_bits(v[page, :, slot], nv)
+    assert _same_bits(k, dec.k_cache) and _same_bits(v, dec.v_cache)
+
+
+def pin_append(attn):
+    """The oracle's append (independent of `attn`, which it does not use)."""
+    import oracle
+    check_append(oracle.append_kv)
+
+
 ALL_PINS = [pin_golden, pin_brute, pin_plain_is_sdpa, pin_closed_form, pin_large_and_half_sink,
             pin_single_key, pin_page_permutation, pin_prefill_row_is_decode, pin_gqa_groups,
             pin_empty_rows, pin_window_wide_is_full, pin_window_brute, pin_window_band_sdpa,
-            pin_window_one, pin_window_truncation]
+            pin_window_one, pin_window_truncation, pin_append]

@@ -66,3 +66,35 @@ def test_mutant_is_caught(tmp_path, name):
         except (AssertionError, RuntimeError, ValueError):
             failures.append(pin.__name__)
     assert failures, f"no pin rejects the mutant '{name}'"
+
+
+# Plausible mistakes in a KV append, each of which check_append must reject.
+def _append_mutant(kind):
+    def append(batch, k_new, v_new):
+        k = batch.k_cache.clone()
+        v = batch.v_cache.clone()
+        cu = batch.cu_seqlens_q.tolist()
+        P = batch.page_size
+        for b in range(batch.num_seqs):
+            L = int(batch.seq_lens[b])
+            n = cu[b + 1] - cu[b]
+            for i in range(n):
+                p = L - n + i
+                if kind == "off by one":
+                    p = L - n + i - 1 if L - n + i > 0 else 0
+                if kind == "anchored at 0":
+                    p = i
+                page = int(batch.block_table[b, p // P])
+                slot = p % P if kind != "slot from page index" else (p // P) % P
+                src = cu[b] + i if kind != "rows of the wrong order" else cu[b] + n - 1 - i
+                k[page, :, slot, :] = k_new[src]
+                v[page, :, slot, :] = (v_new if kind != "K written as V" else k_new)[src]
+        return k, v
+    return append
+
+
+@pytest.mark.parametrize("kind", ["off by one", "anchored at 0", "slot from page index",
+                                  "rows of the wrong order", "K written as V"])
+def test_append_mutant_is_caught(kind):
+    with pytest.raises(AssertionError):
+        pins.check_append(_append_mutant(kind))
