@@ -59,6 +59,12 @@ def library():
     lib.attn_sinks_decode_window.restype = I
     lib.attn_sinks_prefill_window.argtypes = [I] * 11 + [P] * 7 + [F, I, P, P]
     lib.attn_sinks_prefill_window.restype = I
+    lib.attn_sinks_append_kv.argtypes = [I] * 9 + [P] * 7 + [P]
+    lib.attn_sinks_append_kv.restype = I
+    lib.attn_sinks_decode_append.argtypes = [I] * 9 + [P] * 8 + [F, I, P, P, Z, P]
+    lib.attn_sinks_decode_append.restype = I
+    lib.attn_sinks_prefill_append.argtypes = [I] * 11 + [P] * 9 + [F, I, P, P]
+    lib.attn_sinks_prefill_append.restype = I
     lib.attn_sinks_status_string.argtypes = [I]
     lib.attn_sinks_status_string.restype = ctypes.c_char_p
     lib.attn_sinks_version.argtypes = []
@@ -252,6 +258,87 @@ def _prefill(window, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, s
         status = library().attn_sinks_prefill(*head, *tail)
     else:
         status = library().attn_sinks_prefill_window(*head, window, *tail)
+    _raise(status)
+
+
+def attn_sinks_append_kv(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                         v_cache: torch.Tensor, block_table: torch.Tensor,
+                         seq_lens: torch.Tensor, cu_seqlens_new: Optional[torch.Tensor],
+                         max_seq_len: int, stream=None) -> None:
+    """Enqueue attn_sinks_append_kv: rows k_new / v_new [total_new][Hkv][d]
+    into their page slots (the last n_b positions of each sequence, n_b from
+    cu_seqlens_new [B+1] int32, or one token per sequence when None)."""
+    dt = _DTYPE_CODE.get(k_cache.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {k_cache.dtype}")
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        _check_dense(name, t, k_cache.dtype)
+    _check_dense("block_table", block_table, torch.int32)
+    _check_dense("seq_lens", seq_lens, torch.int32)
+    _check_dense("cu_seqlens_new", cu_seqlens_new, torch.int32)
+    num_pages, Hkv, P, d = k_cache.shape
+    T = k_new.shape[0]
+    B = seq_lens.numel()
+    if tuple(k_new.shape) != (T, Hkv, d) or tuple(v_new.shape) != (T, Hkv, d) or \
+            tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_new / v_new / cache shapes disagree")
+    status = library().attn_sinks_append_kv(
+        dt, B, Hkv, d, P, num_pages, block_table.shape[1], int(max_seq_len), T, _ptr(k_new),
+        _ptr(v_new), _ptr(block_table), _ptr(seq_lens), _ptr(cu_seqlens_new), _ptr(k_cache),
+        _ptr(v_cache), _stream_handle(stream))
+    _raise(status)
+
+
+def attn_sinks_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, sinks,
+                             scale: float, window: int, out, workspace, max_seq_len: int,
+                             stream=None) -> None:
+    """Enqueue attn_sinks_decode_append: append one token per sequence, then
+    the (windowed) decode."""
+    dt = _DTYPE_CODE.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                    ("v_cache", v_cache), ("out", out)):
+        _check_dense(name, t, q.dtype)
+    _check_dense("block_table", block_table, torch.int32)
+    _check_dense("seq_lens", seq_lens, torch.int32)
+    _check_dense("sinks", sinks, torch.float32)
+    _check_dense("workspace", workspace)
+    B, Hq, d = q.shape
+    num_pages, Hkv, P, _ = k_cache.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    status = library().attn_sinks_decode_append(
+        dt, B, Hq, Hkv, d, P, num_pages, block_table.shape[1], int(max_seq_len), _ptr(q),
+        _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), _ptr(sinks), ctypes.c_float(scale), int(window), _ptr(out),
+        _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream))
+    _raise(status)
+
+
+def attn_sinks_prefill_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+                              cu_seqlens_q, sinks, scale: float, window: int, out,
+                              max_q_len: int, max_seq_len: int, stream=None) -> None:
+    """Enqueue attn_sinks_prefill_append: append the chunk's tokens, then the
+    (windowed) causal prefill."""
+    dt = _DTYPE_CODE.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                    ("v_cache", v_cache), ("out", out)):
+        _check_dense(name, t, q.dtype)
+    _check_dense("block_table", block_table, torch.int32)
+    _check_dense("seq_lens", seq_lens, torch.int32)
+    _check_dense("cu_seqlens_q", cu_seqlens_q, torch.int32)
+    _check_dense("sinks", sinks, torch.float32)
+    T, Hq, d = q.shape
+    num_pages, Hkv, P, _ = k_cache.shape
+    B = seq_lens.numel()
+    status = library().attn_sinks_prefill_append(
+        dt, B, Hq, Hkv, d, P, num_pages, block_table.shape[1], T, int(max_q_len),
+        int(max_seq_len), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_table), _ptr(seq_lens), _ptr(cu_seqlens_q), _ptr(sinks),
+        ctypes.c_float(scale), int(window), _ptr(out), _stream_handle(stream))
     _raise(status)
 
 

@@ -23,7 +23,7 @@ LIB_NAME = "libattn_sinks.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "rows_f32.hip"]
+SOURCES = ["api.cpp", "append.hip", "decode.hip", "prefill.hip", "rows_f32.hip"]
 
 
 def hipcc() -> str:

@@ -196,6 +196,38 @@ int prepare_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, i
     return ATTN_OK;
 }
 
+// Checks of a KV append (beyond those of the attention call it may precede).
+int check_append(int dtype, int num_seqs, int num_kv_heads, int head_dim, int page_size,
+                 int num_pages, int max_pages_per_seq, int max_seq_len, int total_new,
+                 const void *k_new, const void *v_new, const int32_t *block_table,
+                 const int32_t *seq_lens, const int32_t *cu_seqlens_new, const void *k_cache,
+                 const void *v_cache)
+{
+    int rc = check_common(dtype, num_seqs, num_kv_heads, num_kv_heads, head_dim, page_size,
+                          num_pages, max_pages_per_seq, max_seq_len);
+    if (rc != ATTN_OK)
+        return rc;
+    if (total_new < 0 || (!cu_seqlens_new && total_new != num_seqs))
+        return ATTN_ERR_SHAPE;
+    if (num_seqs == 0 || total_new == 0)
+        return ATTN_OK;
+    if (max_seq_len == 0)
+        return ATTN_ERR_SHAPE;  // new tokens need a place in some page
+    if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !seq_lens)
+        return ATTN_ERR_NULL;
+    const void *vec[] = {k_new, v_new, k_cache, v_cache};
+    for (const void *p : vec)
+        if (!aligned16(p))
+            return ATTN_ERR_ALIGN;
+    const void *words[] = {block_table, seq_lens, cu_seqlens_new};
+    for (const void *p : words)
+        if (p && !aligned4(p))
+            return ATTN_ERR_ALIGN;
+    return ATTN_OK;
+}
+
+int elem_bytes(int dtype) { return dtype == ATTN_DTYPE_F32 ? 4 : 2; }
+
 }  // namespace
 
 extern "C" {
@@ -358,6 +390,95 @@ int attn_sinks_prefill_window(int dtype, int num_seqs, int num_q_heads, int num_
     p.out = out;
     p.stream = s;
     return attn::launch_prefill_bf16(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_sinks_append_kv(int dtype, int num_seqs, int num_kv_heads, int head_dim, int page_size,
+                         int num_pages, int max_pages_per_seq, int max_seq_len, int total_new,
+                         const void *k_new, const void *v_new, const int32_t *block_table,
+                         const int32_t *seq_lens, const int32_t *cu_seqlens_new, void *k_cache,
+                         void *v_cache, void *stream)
+{
+    int rc = check_append(dtype, num_seqs, num_kv_heads, head_dim, page_size, num_pages,
+                          max_pages_per_seq, max_seq_len, total_new, k_new, v_new, block_table,
+                          seq_lens, cu_seqlens_new, k_cache, v_cache);
+    if (rc != ATTN_OK || num_seqs == 0 || total_new == 0)
+        return rc;
+    return attn::launch_append_kv(elem_bytes(dtype), num_seqs, num_kv_heads, head_dim,
+                                  max_pages_per_seq, total_new, k_new, v_new, block_table,
+                                  seq_lens, cu_seqlens_new, k_cache, v_cache,
+                                  reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? ATTN_OK
+               : ATTN_ERR_HIP;
+}
+
+int attn_sinks_decode_append(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                             int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                             int max_seq_len, const void *q, const void *k_new,
+                             const void *v_new, void *k_cache, void *v_cache,
+                             const int32_t *block_table, const int32_t *seq_lens,
+                             const float *sinks, float scale, int window, void *out,
+                             void *workspace, size_t workspace_bytes, void *stream)
+{
+    // every check of both steps runs before anything is enqueued
+    attn::DecodeLaunch p;
+    int rc = prepare_decode(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                            num_pages, max_pages_per_seq, max_seq_len, q, k_cache, v_cache,
+                            block_table, seq_lens, sinks, scale, window, out, workspace,
+                            workspace_bytes, stream, true, true, &p);
+    if (rc != ATTN_OK || num_seqs == 0)
+        return rc;
+    rc = check_append(dtype, num_seqs, num_kv_heads, head_dim, page_size, num_pages,
+                      max_pages_per_seq, max_seq_len, num_seqs, k_new, v_new, block_table,
+                      seq_lens, nullptr, k_cache, v_cache);
+    if (rc != ATTN_OK)
+        return rc;
+    if (attn::launch_append_kv(elem_bytes(dtype), num_seqs, num_kv_heads, head_dim,
+                               max_pages_per_seq, num_seqs, k_new, v_new, block_table, seq_lens,
+                               nullptr, k_cache, v_cache, p.stream) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return attn_sinks_decode_window(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                    page_size, num_pages, max_pages_per_seq, max_seq_len, q,
+                                    k_cache, v_cache, block_table, seq_lens, sinks, scale, window,
+                                    out, workspace, workspace_bytes, stream);
+}
+
+int attn_sinks_prefill_append(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                              int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                              int total_q, int max_q_len, int max_seq_len, const void *q,
+                              const void *k_new, const void *v_new, void *k_cache,
+                              void *v_cache, const int32_t *block_table,
+                              const int32_t *seq_lens, const int32_t *cu_seqlens_q,
+                              const float *sinks, float scale, int window, void *out,
+                              void *stream)
+{
+    // the prefill's own checks first (they enqueue nothing when they fail)
+    int rc = check_common(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                          num_pages, max_pages_per_seq, max_seq_len);
+    if (rc != ATTN_OK)
+        return rc;
+    if (total_q < 0 || max_q_len < 0 || max_q_len > max_seq_len || max_q_len > total_q ||
+        !std::isfinite(scale) || window < 0)
+        return ATTN_ERR_SHAPE;
+    if (num_seqs == 0 || total_q == 0)
+        return ATTN_OK;
+    if (!q || !out || !cu_seqlens_q)
+        return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out) || !aligned4(cu_seqlens_q) || (sinks && !aligned4(sinks)))
+        return ATTN_ERR_ALIGN;
+    rc = check_append(dtype, num_seqs, num_kv_heads, head_dim, page_size, num_pages,
+                      max_pages_per_seq, max_seq_len, total_q, k_new, v_new, block_table,
+                      seq_lens, cu_seqlens_q, k_cache, v_cache);
+    if (rc != ATTN_OK)
+        return rc;
+    if (attn::launch_append_kv(elem_bytes(dtype), num_seqs, num_kv_heads, head_dim,
+                               max_pages_per_seq, total_q, k_new, v_new, block_table, seq_lens,
+                               cu_seqlens_q, k_cache, v_cache,
+                               reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return attn_sinks_prefill_window(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                     page_size, num_pages, max_pages_per_seq, total_q, max_q_len,
+                                     max_seq_len, q, k_cache, v_cache, block_table, seq_lens,
+                                     cu_seqlens_q, sinks, scale, window, out, stream);
 }
 
 const char *attn_sinks_status_string(int status)

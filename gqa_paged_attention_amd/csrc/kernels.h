@@ -49,6 +49,13 @@ hipError_t launch_decode_split_bf16(const DecodeLaunch &p);
 // write out in p.dtype.
 hipError_t launch_decode_merge(const DecodeLaunch &p);
 hipError_t launch_prefill_bf16(const PrefillLaunch &p);
+// KV append: new rows [total_new][Hkv][d] into their page slots (f32 or bf16,
+// elem_bytes 4 or 2); cu_seqlens_new NULL means one new token per sequence.
+hipError_t launch_append_kv(int elem_bytes, int num_seqs, int num_kv_heads, int head_dim,
+                            int max_pages_per_seq, int total_new, const void *k_new,
+                            const void *v_new, const int32_t *block_table,
+                            const int32_t *seq_lens, const int32_t *cu_seqlens_new,
+                            void *k_cache, void *v_cache, hipStream_t stream);
 // fp32 path (full rows, no split), used for both decode and prefill.
 hipError_t launch_rows_f32(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                            int max_pages_per_seq, int total_q, const void *q,

@@ -231,6 +231,62 @@ int attn_sinks_prefill_window(int dtype, int num_seqs, int num_q_heads, int num_
                               const int32_t *cu_seqlens_q, const float *sinks, float scale,
                               int window, void *out, void *stream);
 
+/*
+ * KV append.  Before the attention step each layer appends the new tokens'
+ * K and V to its KV cache ("GPT OSS" model notes, section 3, forward graph;
+ * section 11: per-layer paged K/V).  The n_b new tokens of sequence b are its
+ * last ones: seq_lens[b] = L_b already counts them, and token i of them
+ * (i = 0 .. n_b - 1) sits at position p = L_b - n_b + i.  Its rows are
+ * written to
+ *     k_cache[block_table[b * max_pages_per_seq + p / page_size]][g][p % page_size][:]
+ * (and v_cache likewise) for every KV head g.  Nothing else in the pool is
+ * written.  The caller maps the pages (the table entries for the new
+ * positions must be valid page ids).
+ *
+ *   k_new, v_new    [total_new][num_kv_heads][head_dim]  dtype, the new tokens
+ *                   of sequence 0, then of sequence 1, ...
+ *   cu_seqlens_new  [num_seqs + 1] int32 offsets of each sequence's new
+ *                   tokens in k_new / v_new (0 .. total_new), or NULL for one
+ *                   new token per sequence (then total_new must equal
+ *                   num_seqs)
+ *   k_cache, v_cache, block_table, seq_lens, max_seq_len: as for decode;
+ *                   the caches are written.
+ * Device preconditions (unchecked): n_b <= L_b and the written slots of two
+ * tokens never coincide.  Other conventions as above.
+ */
+int attn_sinks_append_kv(int dtype, int num_seqs, int num_kv_heads, int head_dim, int page_size,
+                         int num_pages, int max_pages_per_seq, int max_seq_len, int total_new,
+                         const void *k_new, const void *v_new, const int32_t *block_table,
+                         const int32_t *seq_lens, const int32_t *cu_seqlens_new, void *k_cache,
+                         void *v_cache, void *stream);
+
+/*
+ * One layer's attention step as the forward graph of the model notes
+ * (section 3) orders it: append the new tokens' K and V, then attend with
+ * the sink, with an optional sliding window (0: none).  These are the
+ * append above followed, on the same stream, by attn_sinks_decode_window or
+ * attn_sinks_prefill_window; every check of both runs before anything is
+ * enqueued.  Decode appends one token per sequence (k_new, v_new
+ * [num_seqs][num_kv_heads][head_dim]); prefill appends the chunk's tokens,
+ * whose offsets are cu_seqlens_q (k_new, v_new [total_q][num_kv_heads][head_dim]).
+ */
+int attn_sinks_decode_append(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                             int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                             int max_seq_len, const void *q, const void *k_new,
+                             const void *v_new, void *k_cache, void *v_cache,
+                             const int32_t *block_table, const int32_t *seq_lens,
+                             const float *sinks, float scale, int window, void *out,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+int attn_sinks_prefill_append(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                              int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                              int total_q, int max_q_len, int max_seq_len, const void *q,
+                              const void *k_new, const void *v_new, void *k_cache,
+                              void *v_cache, const int32_t *block_table,
+                              const int32_t *seq_lens, const int32_t *cu_seqlens_q,
+                              const float *sinks, float scale, int window, void *out,
+                              void *stream);
+
 /* Static English text for a status code (never NULL). */
 const char *attn_sinks_status_string(int status);
 

@@ -196,3 +196,57 @@ def test_window_entry_points_check_like_the_plain_ones(lib, call):
     assert call(lib, 128, scale=float("nan")) == ERR_SHAPE
     assert call(lib, 0, B=0) == OK
     assert call(lib, 128, B=0) == OK
+
+
+def _append(lib, **kw):
+    args = dict(dtype=1, B=2, Hkv=2, d=64, P=16, pages=8, max_pages=4, max_len=64, T=5,
+                k_new=FAKE, v_new=FAKE, bt=FAKE, sl=FAKE, cu=FAKE, kc=FAKE, vc=FAKE)
+    args.update(kw)
+    return lib.attn_sinks_append_kv(
+        args["dtype"], args["B"], args["Hkv"], args["d"], args["P"], args["pages"],
+        args["max_pages"], args["max_len"], args["T"], args["k_new"], args["v_new"], args["bt"],
+        args["sl"], args["cu"], args["kc"], args["vc"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), ERR_UNSUPPORTED),
+    (dict(d=80), ERR_UNSUPPORTED),
+    (dict(P=8), ERR_UNSUPPORTED),
+    (dict(T=-1), ERR_SHAPE),
+    (dict(cu=None, T=5), ERR_SHAPE),          # one token per sequence needs T == B
+    (dict(max_len=0), ERR_SHAPE),             # new tokens need a page
+    (dict(max_len=65), ERR_SHAPE),
+    (dict(k_new=None), ERR_NULL),
+    (dict(vc=None), ERR_NULL),
+    (dict(bt=None), ERR_NULL),
+    (dict(v_new=FAKE + 8), ERR_ALIGN),
+    (dict(kc=FAKE + 4), ERR_ALIGN),
+    (dict(cu=FAKE + 2), ERR_ALIGN),
+])
+def test_append_rejects(lib, kw, code):
+    assert _append(lib, **kw) == code
+
+
+def test_append_empty_enqueues_nothing(lib):
+    assert _append(lib, T=0) == OK
+    assert _append(lib, B=0, T=0) == OK
+
+
+def test_combined_calls_check_before_enqueueing(lib):
+    # bad decode arguments: rejected before the append is launched
+    rc = lib.attn_sinks_decode_append(1, 2, 8, 2, 64, 16, 8, 4, 64, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, FAKE, FAKE, None, ctypes.c_float(0.125), -1, FAKE,
+                                      FAKE, ctypes.c_size_t(1 << 30), None)
+    assert rc == ERR_SHAPE
+    rc = lib.attn_sinks_decode_append(1, 2, 8, 2, 64, 16, 8, 4, 64, FAKE, None, FAKE, FAKE,
+                                      FAKE, FAKE, FAKE, None, ctypes.c_float(0.125), 0, FAKE,
+                                      FAKE, ctypes.c_size_t(1 << 30), None)
+    assert rc == ERR_NULL
+    rc = lib.attn_sinks_prefill_append(1, 2, 8, 2, 64, 16, 8, 4, 40, 32, 64, FAKE, FAKE, FAKE,
+                                       FAKE + 4, FAKE, FAKE, FAKE, FAKE, None,
+                                       ctypes.c_float(0.125), 0, FAKE, None)
+    assert rc == ERR_ALIGN
+    rc = lib.attn_sinks_prefill_append(1, 2, 8, 2, 64, 16, 8, 4, 40, 41, 64, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                       ctypes.c_float(0.125), 0, FAKE, None)
+    assert rc == ERR_SHAPE
