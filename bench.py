@@ -247,6 +247,43 @@ def bench_window(torch, ga, timer, steps, warmup, wl, window=128):
     }
 
 
+def bench_append(torch, ga, timer, steps, warmup, wl):
+    """KV append ("GPT OSS" notes, section 3) of the gpt-oss prefill chunk
+    (32768 tokens x 8 KV heads into their pages: read once, written once,
+    against the HBM roofline), and the gpt-oss decode step with its append
+    (attn_sinks_decode_append) next to the decode alone."""
+    pre = wl.gptoss_prefill(0)
+    before, k_new, v_new = wl.split_new_tokens(pre)
+    g = before.to("cuda")
+    kn, vn = k_new.cuda(), v_new.cuda()
+    r = timer.run([("append", lambda: ga.attn_sinks_append_kv(
+        kn, vn, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.cu_seqlens_q,
+        before.max_seq_len))], steps, warmup, flush=True)
+    nb = 2 * 2 * k_new.numel() * k_new.element_size()  # K and V, read and written
+    nb += 4 * (g.num_seqs * 2 + 1)
+    a_gbs = nb / (r["step_ms"] * 1e-3) / 1e9
+    del g, kn, vn, before, pre
+    dec = wl.gptoss_decode(0)
+    dbefore, dk, dv = wl.split_new_tokens(dec)
+    gd = dbefore.to("cuda")
+    out = torch.empty_like(gd.q)
+    ws = decode_workspace(torch, ga, gd)
+    dkc, dvc = dk.cuda(), dv.cuda()
+    rd = timer.run([("decode_append", lambda: ga.attn_sinks_decode_append(
+        gd.q, dkc, dvc, gd.k_cache, gd.v_cache, gd.block_table, gd.seq_lens, gd.sinks,
+        gd.scale, 0, out, ws, gd.max_seq_len))], steps, warmup, flush=True)
+    return {
+        "prefill_chunk_append": {
+            "workload": "gpt-oss prefill chunk: 32768 tokens x 8 KV heads x 64, bf16",
+            "bytes": nb, "ms": round(r["step_ms"], 4), "GB_per_s": round(a_gbs, 1),
+            "hbm_frac": round(a_gbs / HBM_PEAK_GBS, 4)},
+        "decode_step_with_append": {
+            "workload": "gpt-oss decode workload, its 64 tokens appended first",
+            "ms": round(rd["step_ms"], 4),
+            "GB_per_s": round(decode_bytes(dec) / (rd["step_ms"] * 1e-3) / 1e9, 1)},
+    }
+
+
 def bench_mixed(torch, ga, timer, steps, warmup, wl):
     full, dec, pre = wl.mixed(0)
     gd, gp = dec.to("cuda"), pre.to("cuda")
@@ -453,6 +490,9 @@ def main():
         log("sliding-window legs (window 128)")
         extra["sliding_window"] = bench_window(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["sliding_window"]))
+        log("KV append legs")
+        extra["kv_append"] = bench_append(torch, ga, timer, K, W, wl)
+        log(json.dumps(extra["kv_append"]))
         log("generating qwen decode workload (about a minute)")
         qw = wl.qwen_decode(0)
         q_res, _, keep = bench_decode(torch, ga, timer, qw, max(K // 2, 3), max(W // 2, 1),

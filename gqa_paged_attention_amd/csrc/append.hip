@@ -6,9 +6,11 @@
 // Token i of the n_b new tokens of sequence b sits at position
 // p = L_b - n_b + i (the lengths already count the new tokens) and goes to
 // page block_table[b][p / 16], slot p % 16, of every KV head.  The work is a
-// scatter of rows of d elements: one thread per 16-byte chunk of a (token,
-// head) row, consecutive threads on consecutive chunks, so a wave reads 1 KiB
-// of contiguous input and writes whole rows of the destination slabs.
+// scatter of rows of d elements, one thread per 16-byte chunk.  A wave takes
+// the rows of one KV head for 64 / (row chunks) consecutive new tokens, so
+// that when they are consecutive positions of one page (the usual case) its
+// stores fill one contiguous stretch of that page's head slab; its loads
+// read whole rows.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,7 +26,9 @@ struct AppendArgs {
     const int32_t *__restrict__ seq_lens;
     const int32_t *__restrict__ cu_new;  // [B + 1], or NULL: one new token per sequence
     int num_seqs, num_kv_heads, max_pages, row_chunks;
-    long long total_chunks;
+    int tokens_per_wave;  // 64 / row_chunks
+    int total_new;
+    long long total_threads;
 };
 
 constexpr int kAppendThreads = 256;
@@ -32,12 +36,18 @@ constexpr int kAppendThreads = 256;
 __global__ __launch_bounds__(kAppendThreads) void append_kv(AppendArgs a)
 {
     const long long i = (long long)blockIdx.x * kAppendThreads + threadIdx.x;
-    if (i >= a.total_chunks)
+    if (i >= a.total_threads)
         return;
-    const long long row = i / a.row_chunks;  // (token, KV head)
-    const int c = (int)(i - row * a.row_chunks);
-    const int t = (int)(row / a.num_kv_heads);
-    const int g = (int)(row - (long long)t * a.num_kv_heads);
+    // i = ((token block * Hkv + g) * tokens_per_wave + token in block) * row_chunks + c
+    const int c = (int)(i % a.row_chunks);
+    const long long r = i / a.row_chunks;
+    const int t_in = (int)(r % a.tokens_per_wave);
+    const long long bg = r / a.tokens_per_wave;
+    const int g = (int)(bg % a.num_kv_heads);
+    const int t = (int)(bg / a.num_kv_heads) * a.tokens_per_wave + t_in;
+    if (t >= a.total_new)
+        return;  // past the last token of a partial block
+    const size_t src = ((size_t)t * a.num_kv_heads + g) * a.row_chunks + c;
     int b = t, n = 1, first = t;
     if (a.cu_new) {
         // the sequence of token t: the last b with cu_new[b] <= t (empty
@@ -57,8 +67,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_kv(AppendArgs a)
     const int pos = a.seq_lens[b] - n + (t - first);
     const int page = a.block_table[(size_t)b * a.max_pages + (pos >> 4)];
     const size_t dst = (((size_t)page * a.num_kv_heads + g) * 16 + (pos & 15)) * a.row_chunks + c;
-    a.k_cache[dst] = a.k_new[i];
-    a.v_cache[dst] = a.v_new[i];
+    a.k_cache[dst] = a.k_new[src];
+    a.v_cache[dst] = a.v_new[src];
 }
 
 }  // namespace
@@ -82,9 +92,12 @@ hipError_t launch_append_kv(int elem_bytes, int num_seqs, int num_kv_heads, int 
     a.num_seqs = num_seqs;
     a.num_kv_heads = num_kv_heads;
     a.max_pages = max_pages_per_seq;
-    a.row_chunks = head_dim * elem_bytes / 16;
-    a.total_chunks = (long long)total_new * num_kv_heads * a.row_chunks;
-    const long long blocks = (a.total_chunks + kAppendThreads - 1) / kAppendThreads;
+    a.row_chunks = head_dim * elem_bytes / 16;  // 8, 16 or 32
+    a.tokens_per_wave = 64 / a.row_chunks;
+    a.total_new = total_new;
+    const long long token_blocks = (total_new + a.tokens_per_wave - 1) / a.tokens_per_wave;
+    a.total_threads = token_blocks * num_kv_heads * 64;
+    const long long blocks = (a.total_threads + kAppendThreads - 1) / kAppendThreads;
     if (blocks > 0x7fffffffLL)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(append_kv, dim3((unsigned)blocks), dim3(kAppendThreads), 0, stream, a);
