@@ -65,6 +65,10 @@ def library():
     lib.attn_sinks_decode_append.restype = I
     lib.attn_sinks_prefill_append.argtypes = [I] * 11 + [P] * 9 + [F, I, P, P]
     lib.attn_sinks_prefill_append.restype = I
+    lib.attn_sinks_decode_multi_workspace_bytes.argtypes = [I] * 6
+    lib.attn_sinks_decode_multi_workspace_bytes.restype = Z
+    lib.attn_sinks_decode_multi.argtypes = [I] * 11 + [P] * 7 + [F, P, P, Z, P]
+    lib.attn_sinks_decode_multi.restype = I
     lib.attn_sinks_status_string.argtypes = [I]
     lib.attn_sinks_status_string.restype = ctypes.c_char_p
     lib.attn_sinks_version.argtypes = []
@@ -339,6 +343,41 @@ def attn_sinks_prefill_append(q, k_new, v_new, k_cache, v_cache, block_table, se
         int(max_seq_len), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
         _ptr(block_table), _ptr(seq_lens), _ptr(cu_seqlens_q), _ptr(sinks),
         ctypes.c_float(scale), int(window), _ptr(out), _stream_handle(stream))
+    _raise(status)
+
+
+def attn_sinks_decode_multi_workspace_bytes(num_seqs: int, num_q_heads: int,
+                                            num_kv_heads: int, head_dim: int, max_seq_len: int,
+                                            max_q_len: int) -> int:
+    return int(library().attn_sinks_decode_multi_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, max_q_len))
+
+
+def attn_sinks_decode_multi(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, sinks,
+                            scale: float, out, workspace, max_q_len: int, max_seq_len: int,
+                            stream=None) -> None:
+    """Enqueue attn_sinks_decode_multi: a few new tokens per sequence (rows
+    of q as cu_seqlens_q says); the result of attn_sinks_prefill, computed by
+    the split decode passes with GQA-packed rows where the shape allows."""
+    dt = _DTYPE_CODE.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out)):
+        _check_dense(name, t, q.dtype)
+    _check_dense("block_table", block_table, torch.int32)
+    _check_dense("seq_lens", seq_lens, torch.int32)
+    _check_dense("cu_seqlens_q", cu_seqlens_q, torch.int32)
+    _check_dense("sinks", sinks, torch.float32)
+    _check_dense("workspace", workspace)
+    T, Hq, d = q.shape
+    num_pages, Hkv, P, _ = k_cache.shape
+    B = seq_lens.numel()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    status = library().attn_sinks_decode_multi(
+        dt, B, Hq, Hkv, d, P, num_pages, block_table.shape[1], T, int(max_q_len),
+        int(max_seq_len), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), _ptr(cu_seqlens_q), _ptr(sinks), ctypes.c_float(scale), _ptr(out),
+        _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream))
     _raise(status)
 
 

@@ -87,6 +87,15 @@ DecodeShape decode_shape(int num_seqs, int num_kv_heads, int max_seq_len)
     return s;
 }
 
+// Multi-token decode shapes the split pass takes: G x (query tokens per
+// sequence) packed rows per KV head within its column blocks.
+bool multi_packed(int group, int head_dim, int max_q_len)
+{
+    const int rows = group * max_q_len;
+    return group > 0 && max_q_len >= 1 &&
+           rows <= (head_dim == 64 ? attn::kMultiRowsD64 : attn::kMultiRowsD128);
+}
+
 int check_common(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                  int page_size, int num_pages, int max_pages_per_seq, int max_seq_len)
 {
@@ -115,10 +124,12 @@ int check_common(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, int
     return ATTN_OK;
 }
 
-// Workspace: ml [slots][Hq][2] then, 16-byte aligned, acc [slots][Hq][d]
-// (fp32), with slots = num_seqs + workgroups per head group.
+// Workspace: ml [slots][q_max][Hq][2] then, 16-byte aligned, acc
+// [slots][q_max][Hq][d] (fp32), with slots = num_seqs + workgroups per head
+// group and q_max query rows per sequence (1 for decode).
 size_t decode_workspace(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                        int max_seq_len, DecodeShape *shape_out, size_t *acc_offset_floats)
+                        int max_seq_len, DecodeShape *shape_out, size_t *acc_offset_floats,
+                        int q_max = 1)
 {
     const DecodeShape shape = decode_shape(num_seqs, num_kv_heads, max_seq_len);
     if (shape_out)
@@ -128,11 +139,11 @@ size_t decode_workspace(int num_seqs, int num_q_heads, int num_kv_heads, int hea
             *acc_offset_floats = 0;
         return 0;
     }
-    const size_t slots = (size_t)num_seqs + (size_t)shape.wgs;
-    const size_t ml = (slots * num_q_heads * 2 + 3) / 4 * 4;
+    const size_t rows = ((size_t)num_seqs + (size_t)shape.wgs) * (size_t)q_max;
+    const size_t ml = (rows * num_q_heads * 2 + 3) / 4 * 4;
     if (acc_offset_floats)
         *acc_offset_floats = ml;
-    return (ml + slots * num_q_heads * (size_t)head_dim) * sizeof(float);
+    return (ml + rows * num_q_heads * (size_t)head_dim) * sizeof(float);
 }
 
 // Checks shared by the decode entry points; fills the launch description.
@@ -181,6 +192,8 @@ int prepare_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, i
     p->num_wgs = shape.wgs;
     p->heads_per_wg = shape.heads_per_wg;
     p->window = window;
+    p->cu_seqlens_q = nullptr;
+    p->q_max = 1;
     p->q = q;
     p->k_cache = k_cache;
     p->v_cache = v_cache;
@@ -479,6 +492,65 @@ int attn_sinks_prefill_append(int dtype, int num_seqs, int num_q_heads, int num_
                                      page_size, num_pages, max_pages_per_seq, total_q, max_q_len,
                                      max_seq_len, q, k_cache, v_cache, block_table, seq_lens,
                                      cu_seqlens_q, sinks, scale, window, out, stream);
+}
+
+size_t attn_sinks_decode_multi_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                               int head_dim, int max_seq_len, int max_q_len)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 ||
+        max_q_len < 0 || !supported_head_dim(head_dim) || num_q_heads % num_kv_heads != 0 ||
+        num_q_heads / num_kv_heads > kMaxGroup)
+        return 0;
+    if (!multi_packed(num_q_heads / num_kv_heads, head_dim, max_q_len))
+        return 0;  // such calls run the prefill kernel, which needs no scratch
+    return decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, nullptr,
+                            nullptr, max_q_len);
+}
+
+int attn_sinks_decode_multi(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                            int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                            int total_q, int max_q_len, int max_seq_len, const void *q,
+                            const void *k_cache, const void *v_cache, const int32_t *block_table,
+                            const int32_t *seq_lens, const int32_t *cu_seqlens_q,
+                            const float *sinks, float scale, void *out, void *workspace,
+                            size_t workspace_bytes, void *stream)
+{
+    const bool packed = dtype == ATTN_DTYPE_BF16 &&
+                        multi_packed(num_kv_heads > 0 ? num_q_heads / num_kv_heads : 0, head_dim,
+                                     max_q_len);
+    if (!packed)  // fp32, or more packed rows than the split pass takes
+        return attn_sinks_prefill(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                  page_size, num_pages, max_pages_per_seq, total_q, max_q_len,
+                                  max_seq_len, q, k_cache, v_cache, block_table, seq_lens,
+                                  cu_seqlens_q, sinks, scale, out, stream);
+    attn::DecodeLaunch p;
+    int rc = prepare_decode(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                            num_pages, max_pages_per_seq, max_seq_len, q, k_cache, v_cache,
+                            block_table, seq_lens, sinks, scale, 0, out, workspace,
+                            workspace_bytes, stream, true, true, &p);
+    if (rc != ATTN_OK)
+        return rc;
+    if (total_q < 0 || max_q_len < 0 || max_q_len > max_seq_len || max_q_len > total_q)
+        return ATTN_ERR_SHAPE;
+    if (num_seqs == 0 || total_q == 0)
+        return ATTN_OK;
+    if (!cu_seqlens_q)
+        return ATTN_ERR_NULL;
+    if (!aligned4(cu_seqlens_q) || (workspace && !aligned16(workspace)))
+        return ATTN_ERR_ALIGN;
+    size_t acc_offset = 0;
+    const size_t need = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         max_seq_len, nullptr, &acc_offset, max_q_len);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return workspace ? ATTN_ERR_WORKSPACE : ATTN_ERR_NULL;
+    p.cu_seqlens_q = cu_seqlens_q;
+    p.q_max = max_q_len;
+    float *ws = static_cast<float *>(workspace);
+    p.part_ml = ws;
+    p.part_acc = ws ? ws + acc_offset : nullptr;
+    if (attn::launch_decode_split_bf16(p) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return attn::launch_decode_merge(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 const char *attn_sinks_status_string(int status)

@@ -53,6 +53,8 @@ struct SplitArgs {
     int num_wgs;        // workgroups per head group
     int heads_per_wg;   // KV heads (waves) per workgroup
     int window;         // sliding window W (0: none)
+    const int32_t *__restrict__ cu_seqlens_q;  // multi-token decode: [B + 1]; NULL: one token
+    int q_max;          // query rows per sequence in the partial results (1 for decode)
     float scale_log2;
 };
 
@@ -219,18 +221,25 @@ __device__ __forceinline__ void load_block(Block<D> &blk, const uint16_t *__rest
     }
 }
 
-template <int D>
+// Query rows of one KV head, packed GQA-style into the 16 columns of the
+// matrix instructions: column block cb, column n holds packed row
+// r = 16 cb + n, i.e. query token r / G of the sequence's new tokens and
+// query head g G + r % G.  Plain decode (one token) uses one block whose
+// columns past G are idle; a multi-token decode (Lq tokens per sequence, as
+// speculative or MTP drafts are verified) uses ceil(G Lq / 16) blocks, which
+// share every K and V operand.
+template <int D, int NCB>
 struct WaveState {
-    float m;     // running reference maximum (base-2 units), shared by the 4 lanes of a head
-    float lsum;  // this lane's share of the running sum
-    f32x4_t acc[D / 16];
+    float m[NCB];     // running reference maximum (base-2 units), per column
+    float lsum[NCB];  // this lane's share of its column's running sum
+    f32x4_t acc[NCB][D / 16];
 };
 
-template <int D, bool kMasked>
-__device__ __forceinline__ void compute_block(WaveState<D> &st, Block<D> &blk,
-                                              const u32x4_t (&qop)[D / 32], int t0, int t_lo,
-                                              int t_end, float scale_log2, int lg,
-                                              u32x4_t *klds)
+template <int D, int NCB, bool kMasked>
+__device__ __forceinline__ void compute_block(WaveState<D, NCB> &st, Block<D> &blk,
+                                              const u32x4_t (&qop)[NCB][D / 32], int t0,
+                                              int t_lo, int t_end, const int (&col_end)[NCB],
+                                              float scale_log2, int lg, u32x4_t *klds)
 {
     using VRow = typename VRowT<D>::type;
     constexpr int kChunks = D / 8;  // 16-byte chunks per K row
@@ -254,58 +263,76 @@ __device__ __forceinline__ void compute_block(WaveState<D> &st, Block<D> &blk,
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
             kop[s][kk] = klds[(s * 16 + n) * kChunks + ((kk * 4 + lg) ^ k_swizzle<D>(n))];
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-        s0 = mfma16x16x32(kop[0][kk], qop[kk], s0);
-        s1 = mfma16x16x32(kop[1][kk], qop[kk], s1);
-    }
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[i] = s0[i] * scale_log2;
-        x[4 + i] = s1[i] * scale_log2;
-    }
     if (kMasked) {
-        // first or last block of a piece: mask scores and zero the V rows of
-        // tokens outside [t_lo, t_end) (past the end they may hold NaN, and
-        // 0 * NaN would poison every head); the block holds at least one
-        // token of the range, so its maximum below is finite
+        // first or last block of a piece: zero the V rows of tokens outside
+        // [t_lo, t_end) (past the end they may hold NaN, and 0 * NaN would
+        // poison every column)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int ta = t0 + 4 * lg + i, tb = ta + 16;
-            if (ta >= t_end || ta < t_lo) {
-                x[i] = kNegInf;
+            if (ta >= t_end || ta < t_lo)
                 blk.v[i] = VRow{};
-            }
-            if (tb >= t_end || tb < t_lo) {
-                x[4 + i] = kNegInf;
+            if (tb >= t_end || tb < t_lo)
                 blk.v[4 + i] = VRow{};
-            }
         }
     }
-    float bm = x[0];
+    u32x4_t pop[NCB];
 #pragma unroll
-    for (int i = 1; i < 8; ++i)
-        bm = fmaxf(bm, x[i]);
-    bm = group4_max(bm);
-    const float m_new = (bm > st.m + kRescaleSlack) ? bm : st.m;
-    if (__any(m_new != st.m)) {
-        const float alpha = exp2_fast(st.m - m_new);  // 0 on the first block
-        st.lsum *= alpha;
+    for (int cb = 0; cb < NCB; ++cb) {
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < D / 16; ++e)
-            st.acc[e] *= alpha;
-        st.m = m_new;
+        for (int kk = 0; kk < D / 32; ++kk) {
+            s0 = mfma16x16x32(kop[0][kk], qop[cb][kk], s0);
+            s1 = mfma16x16x32(kop[1][kk], qop[cb][kk], s1);
+        }
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = s0[i] * scale_log2;
+            x[4 + i] = s1[i] * scale_log2;
+        }
+        if (kMasked) {
+            // tokens outside [t_lo, min(t_end, col_end)) are invisible to this
+            // column's row; the block holds at least one visible token of
+            // every row that has any key at all
+            const int te = min(t_end, col_end[cb]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ta = t0 + 4 * lg + i, tb = ta + 16;
+                if (ta >= te || ta < t_lo)
+                    x[i] = kNegInf;
+                if (tb >= te || tb < t_lo)
+                    x[4 + i] = kNegInf;
+            }
+        }
+        float bm = x[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i)
+            bm = fmaxf(bm, x[i]);
+        bm = group4_max(bm);
+        const float m_new = (bm > st.m[cb] + kRescaleSlack) ? bm : st.m[cb];
+        if (__any(m_new != st.m[cb])) {
+            // 0 on a column's first visible block; 1 on columns the branch
+            // does not concern (their rows may still have seen no key: then
+            // both maxima are -inf)
+            const float alpha = m_new == st.m[cb] ? 1.f : exp2_fast(st.m[cb] - m_new);
+            st.lsum[cb] *= alpha;
+#pragma unroll
+            for (int e = 0; e < D / 16; ++e)
+                st.acc[cb][e] *= alpha;
+            st.m[cb] = m_new;
+        }
+        // a column whose row has seen no key yet keeps m = -inf: weights 0
+        const float m_ref = st.m[cb] == kNegInf ? 0.f : st.m[cb];
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            p[i] = exp2_fast(x[i] - m_ref);
+            st.lsum[cb] += p[i];
+        }
+        pop[cb] = u32x4_t{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                          pack_bf16(p[6], p[7])};
     }
-    float p[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        p[i] = exp2_fast(x[i] - st.m);
-        st.lsum += p[i];
-    }
-    const u32x4_t pop = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
-                         pack_bf16(p[6], p[7])};
 #pragma unroll
     for (int e = 0; e < D / 16; ++e) {
         const int w = e >> 1, sel = e & 1;
@@ -313,40 +340,59 @@ __device__ __forceinline__ void compute_block(WaveState<D> &st, Block<D> &blk,
                              pair_half(blk.v[2][w], blk.v[3][w], sel),
                              pair_half(blk.v[4][w], blk.v[5][w], sel),
                              pair_half(blk.v[6][w], blk.v[7][w], sel)};
-        st.acc[e] = mfma16x16x32(aop, pop, st.acc[e]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+            st.acc[cb][e] = mfma16x16x32(aop, pop[cb], st.acc[cb][e]);
     }
 }
 
 // One piece: the tokens of [t_begin, t_end) (t_begin a multiple of 32) from
-// t_lo on, of segment (b, g); the result goes to `slot`.
-template <int D>
+// t_lo on, of segment (b, g); the result goes to `slot`.  q_first / q_len:
+// the sequence's query rows (q_len new tokens, the last ones of its L keys).
+template <int D, int NCB>
 __device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int t_begin,
-                                          int t_lo, int t_end, long long slot, int n, int lg,
-                                          u32x4_t *klds)
+                                          int t_lo, int t_end, int L, int q_first, int q_len,
+                                          long long slot, int n, int lg, u32x4_t *klds)
 {
     b = uniform(b);
     g = uniform(g);
     t_begin = uniform(t_begin);
     t_lo = uniform(t_lo);
     t_end = uniform(t_end);
-    // Q^T operand: column n = query head g*G + n, dims kk*32 + lg*8 .. +7
-    u32x4_t qop[D / 32];
-    if (n < a.group) {
-        const uint16_t *qrow = a.q + ((size_t)b * a.num_q_heads + g * a.group + n) * D;
+    L = uniform(L);
+    q_first = uniform(q_first);
+    q_len = uniform(q_len);
+    // Q^T operands: column n of block cb = packed row 16 cb + n (query token
+    // tok = row / G, head g G + row % G), dims kk*32 + lg*8 .. +7; rows of
+    // no token are zero and never stored.  col_end: one past the row's last
+    // visible key (bottom-right causal among the new tokens).
+    u32x4_t qop[NCB][D / 32];
+    int col_end[NCB];
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-            qop[kk] = *(const u32x4_t *)(qrow + kk * 32 + lg * 8);
-    } else {
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int row = 16 * cb + n, tok = row / a.group;
+        col_end[cb] = L - q_len + tok + 1;
+        if (tok < q_len) {
+            const uint16_t *qrow =
+                a.q + ((size_t)(q_first + tok) * a.num_q_heads + g * a.group + row % a.group) * D;
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-            qop[kk] = u32x4_t{0, 0, 0, 0};
+            for (int kk = 0; kk < D / 32; ++kk)
+                qop[cb][kk] = *(const u32x4_t *)(qrow + kk * 32 + lg * 8);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk)
+                qop[cb][kk] = u32x4_t{0, 0, 0, 0};
+        }
     }
-    WaveState<D> st;
-    st.m = kNegInf;
-    st.lsum = 0.f;
+    WaveState<D, NCB> st;
 #pragma unroll
-    for (int e = 0; e < D / 16; ++e)
-        st.acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NCB; ++cb) {
+        st.m[cb] = kNegInf;
+        st.lsum[cb] = 0.f;
+#pragma unroll
+        for (int e = 0; e < D / 16; ++e)
+            st.acc[cb][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 
     const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
     if (t_begin < t_lo) {
@@ -354,19 +400,23 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int 
         Block<D> head;
         load_block<D, false>(head, a.k_cache, a.v_cache, bt, t_begin, t_end, g, a.num_kv_heads,
                              n, lg);
-        compute_block<D, true>(st, head, qop, t_begin, t_lo, t_end, a.scale_log2, lg, klds);
+        compute_block<D, NCB, true>(st, head, qop, t_begin, t_lo, t_end, col_end, a.scale_log2,
+                                    lg, klds);
         t_begin += kUnitTokens;
     }
-    // Full blocks stream through a ring of register buffers with loads issued
-    // ahead of the matrix work (two blocks ahead at d = 64, one at d = 128,
-    // where a block is 16 KiB per wave).  Prefetches past the last full block
-    // re-read that block (a cache hit), so the loop body has no branches
-    // around loads.  A partial last block is handled after the loop.
-    const int nfull = t_end > t_begin ? (t_end - t_begin) / kUnitTokens : 0;
+    // Full blocks (keys every row sees) stream through a ring of register
+    // buffers with loads issued ahead of the matrix work (two blocks ahead at
+    // d = 64, one at d = 128, where a block is 16 KiB per wave, and one when
+    // the packed query rows need the registers).  Prefetches
+    // past the last full block re-read that block (a cache hit), so the loop
+    // body has no branches around loads.  The rest -- a partial last block,
+    // and the blocks with keys some new token may not see -- comes after.
+    const int t_all = min(t_end, L - q_len + 1);  // keys below it: seen by every row
+    const int nfull = t_all > t_begin ? (t_all - t_begin) / kUnitTokens : 0;
     const int t_last = t_begin + kUnitTokens * (nfull - 1);
     auto at = [&](int ib) { return min(t_begin + kUnitTokens * ib, t_last); };
     if (nfull > 0) {
-        if constexpr (D == 64) {
+        if constexpr (D == 64 && NCB < 4) {
             Block<D> b0, b1, b2;
             load_block<D, true>(b0, a.k_cache, a.v_cache, bt, at(0), t_end, g, a.num_kv_heads, n,
                                 lg);
@@ -376,17 +426,20 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int 
                 const int t0 = t_begin + kUnitTokens * ib;
                 load_block<D, true>(b2, a.k_cache, a.v_cache, bt, at(ib + 2), t_end, g,
                                     a.num_kv_heads, n, lg);
-                compute_block<D, false>(st, b0, qop, t0, t_lo, t_end, a.scale_log2, lg, klds);
+                compute_block<D, NCB, false>(st, b0, qop, t0, t_lo, t_end, col_end,
+                                             a.scale_log2, lg, klds);
                 if (ib + 1 >= nfull)
                     break;
                 load_block<D, true>(b0, a.k_cache, a.v_cache, bt, at(ib + 3), t_end, g,
                                     a.num_kv_heads, n, lg);
-                compute_block<D, false>(st, b1, qop, t0 + 32, t_lo, t_end, a.scale_log2, lg, klds);
+                compute_block<D, NCB, false>(st, b1, qop, t0 + 32, t_lo, t_end, col_end,
+                                             a.scale_log2, lg, klds);
                 if (ib + 2 >= nfull)
                     break;
                 load_block<D, true>(b1, a.k_cache, a.v_cache, bt, at(ib + 4), t_end, g,
                                     a.num_kv_heads, n, lg);
-                compute_block<D, false>(st, b2, qop, t0 + 64, t_lo, t_end, a.scale_log2, lg, klds);
+                compute_block<D, NCB, false>(st, b2, qop, t0 + 64, t_lo, t_end, col_end,
+                                             a.scale_log2, lg, klds);
             }
         } else {
             Block<D> b0, b1;
@@ -396,40 +449,48 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int 
                 const int t0 = t_begin + kUnitTokens * ib;
                 load_block<D, true>(b1, a.k_cache, a.v_cache, bt, at(ib + 1), t_end, g,
                                     a.num_kv_heads, n, lg);
-                compute_block<D, false>(st, b0, qop, t0, t_lo, t_end, a.scale_log2, lg, klds);
+                compute_block<D, NCB, false>(st, b0, qop, t0, t_lo, t_end, col_end,
+                                             a.scale_log2, lg, klds);
                 if (ib + 1 >= nfull)
                     break;
                 load_block<D, true>(b0, a.k_cache, a.v_cache, bt, at(ib + 2), t_end, g,
                                     a.num_kv_heads, n, lg);
-                compute_block<D, false>(st, b1, qop, t0 + 32, t_lo, t_end, a.scale_log2, lg, klds);
+                compute_block<D, NCB, false>(st, b1, qop, t0 + 32, t_lo, t_end, col_end,
+                                             a.scale_log2, lg, klds);
             }
         }
     }
-    if (t_begin + kUnitTokens * nfull < t_end) {
+    for (int t0 = t_begin + kUnitTokens * nfull; t0 < t_end; t0 += kUnitTokens) {
         Block<D> bt_tail;
-        const int t0 = t_begin + kUnitTokens * nfull;
         load_block<D, false>(bt_tail, a.k_cache, a.v_cache, bt, t0, t_end, g, a.num_kv_heads, n,
                              lg);
-        compute_block<D, true>(st, bt_tail, qop, t0, t_lo, t_end, a.scale_log2, lg, klds);
+        compute_block<D, NCB, true>(st, bt_tail, qop, t0, t_lo, t_end, col_end, a.scale_log2,
+                                    lg, klds);
     }
-    const float lsum = group4_sum(st.lsum);
-    if (n < a.group) {
-        const size_t row = (size_t)slot * a.num_q_heads + (size_t)g * a.group + n;
-        if (lg == 0)
-            *(float2 *)(a.part_ml + row * 2) = make_float2(st.m, lsum);
-        // lane (n, lg) holds dims (D/16)*(4*lg + i) + e of head n
-        float *dst = a.part_acc + row * D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int cb = 0; cb < NCB; ++cb) {
+        const float lsum = group4_sum(st.lsum[cb]);
+        const int row = 16 * cb + n, tok = row / a.group;
+        if (tok < q_len) {
+            // partial-result row: (slot, query token, query head)
+            const size_t prow = ((size_t)slot * a.q_max + tok) * a.num_q_heads +
+                                (size_t)g * a.group + row % a.group;
+            if (lg == 0)
+                *(float2 *)(a.part_ml + prow * 2) = make_float2(st.m[cb], lsum);
+            // lane (n, lg) holds dims (D/16)*(4*lg + i) + e of its row
+            float *dst = a.part_acc + prow * D;
 #pragma unroll
-            for (int e4 = 0; e4 < D / 16; e4 += 4)
-                *(f32x4_t *)(dst + (D / 16) * (4 * lg + i) + e4) =
-                    f32x4_t{st.acc[e4][i], st.acc[e4 + 1][i], st.acc[e4 + 2][i],
-                            st.acc[e4 + 3][i]};
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e4 = 0; e4 < D / 16; e4 += 4)
+                    *(f32x4_t *)(dst + (D / 16) * (4 * lg + i) + e4) =
+                        f32x4_t{st.acc[cb][e4][i], st.acc[cb][e4 + 1][i],
+                                st.acc[cb][e4 + 2][i], st.acc[cb][e4 + 3][i]};
+        }
     }
 }
 
-template <int D>
+template <int D, int NCB>
 __global__ __launch_bounds__(512) void decode_split_bf16(SplitArgs a)
 {
     const int lane = threadIdx.x & 63;
@@ -463,8 +524,13 @@ __global__ __launch_bounds__(512) void decode_split_bf16(SplitArgs a)
         const long long piece_end = min(u_stop, base + nblk);
         const int t_begin = ((int)(u - base) + fu) * kUnitTokens;
         const int t_end = min(((int)(piece_end - base) + fu) * kUnitTokens, L);
-        run_piece<D>(a, b, g, t_begin, oldest_key(L, a.window), t_end, (long long)b + w, n, lg,
-                     klds);
+        int q_first = b, q_len = 1;
+        if (a.cu_seqlens_q) {
+            q_first = load_scalar(a.cu_seqlens_q, b);
+            q_len = load_scalar(a.cu_seqlens_q, b + 1) - q_first;
+        }
+        run_piece<D, NCB>(a, b, g, t_begin, oldest_key(L, a.window), t_end, L, q_first, q_len,
+                          (long long)b + w, n, lg, klds);
         u = piece_end;
         if (u < u_stop) {
             // next sequence with at least one unit
@@ -484,11 +550,13 @@ struct MergeArgs {
     void *__restrict__ out;
     int num_seqs, num_q_heads, num_kv_heads, num_wgs;
     int window;  // sliding window W (0: none); places the pieces as the split pass does
+    const int32_t *__restrict__ cu_seqlens_q;  // multi-token decode: [B + 1]; NULL: one token
+    int q_max;   // query rows per sequence in the partial results
 };
 
-// One workgroup per (sequence, KV head), one wave per query head of the
-// group: combine the pieces of the sequence in logical order and fold the
-// sink.  The work is two dependent memory round trips: the sequence lengths
+// One workgroup per (sequence, KV head, query token), one wave per query
+// head of the group: combine the pieces of the sequence in logical order and
+// fold the sink.  The work is two dependent memory round trips: the sequence lengths
 // (which place the sequence's pieces), then every piece's (m, l) -- one
 // piece per lane -- together with the accumulators of up to kBatch pieces.
 template <int D, bool kBf16Out>
@@ -496,7 +564,14 @@ __global__ __launch_bounds__(1024) void decode_merge(MergeArgs a)
 {
     constexpr int kPer = D / 64;   // output dims per lane
     constexpr int kBatch = 4;      // pieces whose accumulators are loaded at once
-    const int b = blockIdx.x, lane = threadIdx.x & 63;
+    const int b = blockIdx.x, lane = threadIdx.x & 63, tok = blockIdx.z;
+    int q_first = b, q_len = 1;
+    if (a.cu_seqlens_q) {
+        q_first = a.cu_seqlens_q[b];
+        q_len = a.cu_seqlens_q[b + 1] - q_first;
+    }
+    if (tok >= q_len)
+        return;  // uniform over the workgroup
     const int group = a.num_q_heads / a.num_kv_heads;
     const int h = blockIdx.y * group + (threadIdx.x >> 6);
     const float sink2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
@@ -529,7 +604,7 @@ __global__ __launch_bounds__(1024) void decode_merge(MergeArgs a)
     auto live = [&](int w) {
         return wave_first_unit(w, U, a.num_wgs) < wave_first_unit(w + 1, U, a.num_wgs);
     };
-    auto row_of = [&](int w) { return (size_t)(b + w) * a.num_q_heads + h; };
+    auto row_of = [&](int w) { return ((size_t)(b + w) * a.q_max + tok) * a.num_q_heads + h; };
 
     // (m, l) of piece w_lo + i + 64 k in lane i
     float M = sink2;
@@ -587,7 +662,7 @@ __global__ __launch_bounds__(1024) void decode_merge(MergeArgs a)
         }
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    const size_t o = ((size_t)b * a.num_q_heads + h) * D;
+    const size_t o = ((size_t)(q_first + tok) * a.num_q_heads + h) * D;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const float v = acc[k] * inv;
@@ -598,7 +673,7 @@ __global__ __launch_bounds__(1024) void decode_merge(MergeArgs a)
     }
 }
 
-template <int D>
+template <int D, int NCB>
 hipError_t launch_split_d(const DecodeLaunch &p)
 {
     SplitArgs a;
@@ -617,11 +692,30 @@ hipError_t launch_split_d(const DecodeLaunch &p)
     a.num_wgs = p.num_wgs;
     a.heads_per_wg = p.heads_per_wg;
     a.window = p.window;
+    a.cu_seqlens_q = p.cu_seqlens_q;
+    a.q_max = p.q_max;
     a.scale_log2 = p.scale * kLog2e;
     const dim3 grid(p.num_wgs, (p.num_kv_heads + p.heads_per_wg - 1) / p.heads_per_wg);
     const size_t lds = (size_t)p.heads_per_wg * 2 * 16 * (D / 8) * sizeof(u32x4_t);
-    hipLaunchKernelGGL(decode_split_bf16<D>, grid, dim3(64 * p.heads_per_wg), lds, p.stream, a);
+    hipLaunchKernelGGL((decode_split_bf16<D, NCB>), grid, dim3(64 * p.heads_per_wg), lds,
+                       p.stream, a);
     return hipGetLastError();
+}
+
+// Column blocks of packed query rows: G * (query rows per sequence) <= 16 NCB.
+template <int D>
+hipError_t launch_split_rows(const DecodeLaunch &p)
+{
+    const int rows = (p.num_q_heads / p.num_kv_heads) * p.q_max;
+    if (rows <= 16)
+        return launch_split_d<D, 1>(p);
+    if constexpr (D == 64) {
+        if (rows <= 32)
+            return launch_split_d<D, 2>(p);
+        if (rows <= 64)
+            return launch_split_d<D, 4>(p);
+    }
+    return hipErrorInvalidValue;  // the host checks keep such shapes away
 }
 
 template <int D>
@@ -638,7 +732,9 @@ hipError_t launch_merge_d(const DecodeLaunch &p)
     m.num_kv_heads = p.num_kv_heads;
     m.num_wgs = p.num_wgs;
     m.window = p.window;
-    const dim3 grid(p.num_seqs, p.num_kv_heads);
+    m.cu_seqlens_q = p.cu_seqlens_q;
+    m.q_max = p.q_max;
+    const dim3 grid(p.num_seqs, p.num_kv_heads, p.q_max);
     const dim3 block(64 * (p.num_q_heads / p.num_kv_heads));
     if (p.dtype == 1)
         hipLaunchKernelGGL((decode_merge<D, true>), grid, block, 0, p.stream, m);
@@ -653,7 +749,7 @@ hipError_t launch_decode_split_bf16(const DecodeLaunch &p)
 {
     if (p.num_seqs == 0 || p.num_wgs == 0)
         return hipSuccess;
-    return p.head_dim == 64 ? launch_split_d<64>(p) : launch_split_d<128>(p);
+    return p.head_dim == 64 ? launch_split_rows<64>(p) : launch_split_rows<128>(p);
 }
 
 hipError_t launch_decode_merge(const DecodeLaunch &p)

@@ -13,13 +13,17 @@ struct DecodeLaunch {
     int num_wgs;        // split-pass workgroups per KV-head group
     int heads_per_wg;   // KV heads (one wave each) per split-pass workgroup
     int window;         // sliding window W (keys L - W .. L - 1), 0: none
+    // multi-token decode: query offsets [num_seqs + 1] (NULL: one token per
+    // sequence) and the largest number of query tokens of a sequence
+    const int32_t *cu_seqlens_q;
+    int q_max;
     const void *q, *k_cache, *v_cache;
     const int32_t *block_table, *seq_lens;
     const float *sinks;
     float scale;
     void *out;
-    float *part_ml;     // [slots][Hq][2],   slots = num_seqs + num_wgs
-    float *part_acc;    // [slots][Hq][head_dim]
+    float *part_ml;     // [slots][q_max][Hq][2],   slots = num_seqs + num_wgs
+    float *part_acc;    // [slots][q_max][Hq][head_dim]
     hipStream_t stream;
 };
 
@@ -35,6 +39,12 @@ struct PrefillLaunch {
     void *out;
     hipStream_t stream;
 };
+
+// The most packed query rows (G times query tokens per sequence) the
+// multi-token decode handles per KV head: 64 at d = 64, 16 at d = 128 (one
+// column block; more would not fit the registers next to the K/V ring).
+constexpr int kMultiRowsD64 = 64;
+constexpr int kMultiRowsD128 = 16;
 
 // Decode split pass: up to 4 KV heads (waves) per workgroup; the grid gives
 // every one of MI355X's 256 CUs the same number of workgroups, with at least

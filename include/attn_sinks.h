@@ -287,6 +287,40 @@ int attn_sinks_prefill_append(int dtype, int num_seqs, int num_q_heads, int num_
                               const float *sinks, float scale, int window, void *out,
                               void *stream);
 
+/*
+ * Multi-token decode: a few new query tokens per sequence (Lq_b of them,
+ * the last of its L_b keys), as when speculative or MTP draft tokens are
+ * verified ("Hosting Qwen on Blackwell": decoding with speculative MTP
+ * layers; "GPT-OSS on day 0": speculative and MTP decoders).  The result is
+ * exactly that of attn_sinks_prefill on the same arguments (bottom-right
+ * causal among the new tokens, sink in every row); the difference is the
+ * kernel.  The split-KV decode passes run with the query rows of each KV
+ * head packed GQA-style into the matrix columns (G x Lq rows share every K
+ * and V block read), when
+ *     dtype is bf16 and G * max_q_len <= 64 (head_dim 64) or <= 16 (head_dim 128);
+ * other shapes run attn_sinks_prefill and need no workspace.
+ *
+ *   q, out        [total_q][num_q_heads][head_dim], rows as cu_seqlens_q says
+ *   cu_seqlens_q  [num_seqs + 1] int32 query offsets (0 .. total_q)
+ *   max_q_len     host upper bound of every Lq_b
+ *   workspace     at least attn_sinks_decode_multi_workspace_bytes(...) bytes
+ *                 (0 bytes, and NULL allowed, when that returns 0; the count
+ *                 depends on the shape only, and fp32 calls never use it)
+ * Everything else as for attn_sinks_prefill / attn_sinks_decode.  The
+ * workspace layout is that of attn_sinks_decode_merge with max_q_len query
+ * rows per slot: ml [slots][max_q_len][num_q_heads][2], acc likewise.
+ */
+size_t attn_sinks_decode_multi_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                               int head_dim, int max_seq_len, int max_q_len);
+
+int attn_sinks_decode_multi(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                            int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                            int total_q, int max_q_len, int max_seq_len, const void *q,
+                            const void *k_cache, const void *v_cache, const int32_t *block_table,
+                            const int32_t *seq_lens, const int32_t *cu_seqlens_q,
+                            const float *sinks, float scale, void *out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
 /* Static English text for a status code (never NULL). */
 const char *attn_sinks_status_string(int status);
 

@@ -250,3 +250,51 @@ def test_combined_calls_check_before_enqueueing(lib):
                                        FAKE, FAKE, FAKE, FAKE, FAKE, None,
                                        ctypes.c_float(0.125), 0, FAKE, None)
     assert rc == ERR_SHAPE
+
+
+def test_multi_workspace_bytes(lib):
+    # packed shapes: the decode layout with max_q_len query rows per slot
+    for B, Hq, Hkv, d, L, q in [(64, 64, 8, 64, 8192, 4), (3, 8, 2, 64, 100, 2),
+                                (16, 16, 1, 128, 5000, 1), (5, 8, 8, 64, 300, 8)]:
+        one = _expected_ws(B, Hq, Hkv, d, L)
+        got = ga.attn_sinks_decode_multi_workspace_bytes(B, Hq, Hkv, d, L, q)
+        assert got > 0 and got >= one * q * 0.99, (B, Hq, Hkv, d, L, q)
+        if q == 1:
+            assert got == one
+    # shapes that run the prefill kernel need no workspace
+    assert ga.attn_sinks_decode_multi_workspace_bytes(64, 64, 8, 64, 8192, 9) == 0   # 72 rows
+    assert ga.attn_sinks_decode_multi_workspace_bytes(4, 64, 4, 128, 9000, 2) == 0   # 32 rows
+    assert ga.attn_sinks_decode_multi_workspace_bytes(4, 64, 8, 96, 9000, 2) == 0    # head_dim
+
+
+def _multi(lib, **kw):
+    args = dict(dtype=1, B=2, Hq=8, Hkv=2, d=64, P=16, pages=8, max_pages=4, total_q=6,
+                max_q=4, max_len=64, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, cu=FAKE,
+                sinks=None, scale=0.125, out=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    return lib.attn_sinks_decode_multi(
+        args["dtype"], args["B"], args["Hq"], args["Hkv"], args["d"], args["P"], args["pages"],
+        args["max_pages"], args["total_q"], args["max_q"], args["max_len"], args["q"],
+        args["k"], args["v"], args["bt"], args["sl"], args["cu"], args["sinks"],
+        ctypes.c_float(args["scale"]), args["out"], args["ws"],
+        ctypes.c_size_t(args["ws_bytes"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), ERR_UNSUPPORTED),
+    (dict(max_q=7), ERR_SHAPE),             # > total_q
+    (dict(max_q=65, total_q=100), ERR_SHAPE),  # > max_len (prefill path)
+    (dict(cu=None), ERR_NULL),
+    (dict(ws=None), ERR_NULL),
+    (dict(ws_bytes=64), ERR_WORKSPACE),
+    (dict(cu=FAKE + 2), ERR_ALIGN),
+    (dict(q=FAKE + 8), ERR_ALIGN),
+    (dict(scale=float("nan")), ERR_SHAPE),
+])
+def test_multi_rejects(lib, kw, code):
+    assert _multi(lib, **kw) == code
+
+
+def test_multi_empty(lib):
+    assert _multi(lib, B=0) == OK
+    assert _multi(lib, total_q=0, max_q=0) == OK
