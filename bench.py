@@ -284,6 +284,36 @@ def bench_append(torch, ga, timer, steps, warmup, wl):
     }
 
 
+def bench_multi(torch, ga, timer, steps, warmup, wl, q_len=4):
+    """Multi-token decode: the gpt-oss decode shape (64 seqs, L ~ U[1024,
+    8192], 64/8 heads, d 64) with `q_len` new tokens per sequence, through
+    attn_sinks_decode_multi (packed split passes) and, for comparison, the
+    same call through attn_sinks_prefill.  Bytes: K and V of every key once,
+    plus q and out of every new token."""
+    gen = torch.Generator().manual_seed(0)
+    L = torch.randint(1024, 8193, (64,), generator=gen, dtype=torch.int64).to(torch.int32)
+    b = wl.build_batch(gen, "bf16", L, torch.full((64,), q_len, dtype=torch.int32), 64, 8, 64,
+                       sink_mode="normal")
+    g = b.to("cuda")
+    out = torch.empty_like(g.q)
+    nb = ga.attn_sinks_decode_multi_workspace_bytes(g.num_seqs, g.num_q_heads, g.num_kv_heads,
+                                                    g.head_dim, b.max_seq_len, b.max_q_len)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    args = (g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.cu_seqlens_q, g.sinks,
+            g.scale)
+    r = timer.run([("multi", lambda: ga.attn_sinks_decode_multi(
+        *args, out, ws, b.max_q_len, b.max_seq_len))], steps, warmup, flush=True)
+    rp = timer.run([("as_prefill", lambda: ga.attn_sinks_prefill(
+        *args, out, b.max_q_len, b.max_seq_len))], steps, warmup, flush=True)
+    nbytes = b.algorithmic_kv_bytes() + 2 * b.q.numel() * 2 + \
+        int(((L.long() + 15) // 16).sum()) * 4 + 4 * (2 * 64 + 1) + 4 * 64
+    gbs = nbytes / (r["step_ms"] * 1e-3) / 1e9
+    return {"workload": f"gpt-oss decode shape, {q_len} new tokens per sequence",
+            "algorithmic_bytes": nbytes, "ms": round(r["step_ms"], 4),
+            "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "same_call_as_prefill_ms": round(rp["step_ms"], 4)}
+
+
 def bench_mixed(torch, ga, timer, steps, warmup, wl):
     full, dec, pre = wl.mixed(0)
     gd, gp = dec.to("cuda"), pre.to("cuda")
@@ -490,6 +520,9 @@ def main():
         log("sliding-window legs (window 128)")
         extra["sliding_window"] = bench_window(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["sliding_window"]))
+        log("multi-token decode leg")
+        extra["multi_token_decode"] = bench_multi(torch, ga, timer, K, W, wl)
+        log(json.dumps(extra["multi_token_decode"]))
         log("KV append legs")
         extra["kv_append"] = bench_append(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["kv_append"]))
