@@ -52,7 +52,7 @@ def load_library(path: str):
     lib = ctypes.CDLL(path)
     f = lib.oracle_attention_rows
     P = ctypes.c_void_p
-    f.argtypes = [ctypes.c_int] * 7 + [P] * 6 + [P, ctypes.c_double, ctypes.c_int,
+    f.argtypes = [ctypes.c_int] * 7 + [P] * 6 + [P, ctypes.c_double, ctypes.c_int, ctypes.c_int,
                                                  ctypes.c_int64, P, P, P, P, ctypes.c_int]
     f.restype = ctypes.c_int
     return lib
@@ -80,12 +80,14 @@ def _ptr(t: Optional[torch.Tensor]):
 
 def attention_rows(batch, row_token: Sequence[int], row_head: Sequence[int],
                    threads: Optional[int] = None, with_lse: bool = False, lib=None,
-                   window: int = 0):
+                   window: int = 0, causal: bool = True):
     """fp64 outputs for the listed (query token, query head) pairs.
 
     `batch` is a workloads.PagedBatch on the CPU.  Returns an array
     [n_rows][head_dim] (and the natural-log LSE per row when asked).
-    `window` > 0 limits each query at position p to keys p - window + 1 .. p.
+    `window` > 0 limits each query at position p to keys p - window + 1 .. p;
+    causal=False lets every row see all keys of its sequence.  The LSE is
+    the natural log of the row's softmax denominator, sink included.
     `lib` selects another compiled copy of oracle.c (used by the tests that
     check the pins catch planted mistakes).
     """
@@ -111,7 +113,8 @@ def attention_rows(batch, row_token: Sequence[int], row_head: Sequence[int],
         DTYPE_CODE[batch.dtype], batch.num_seqs, batch.num_q_heads, batch.num_kv_heads,
         batch.head_dim, batch.page_size, batch.max_pages_per_seq,
         _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), _ptr(cu), _ptr(sinks),
-        ctypes.c_double(batch.scale), int(window), ctypes.c_int64(n), _ptr(rt), _ptr(rh),
+        ctypes.c_double(batch.scale), int(window), int(bool(causal)), ctypes.c_int64(n),
+        _ptr(rt), _ptr(rh),
         _ptr(out), _ptr(lse), int(threads or default_threads()))
     if rc != 0:
         raise RuntimeError(f"oracle_attention_rows failed with code {rc}")
@@ -119,13 +122,13 @@ def attention_rows(batch, row_token: Sequence[int], row_head: Sequence[int],
 
 
 def attention(batch, threads: Optional[int] = None, with_lse: bool = False, lib=None,
-              window: int = 0):
+              window: int = 0, causal: bool = True):
     """fp64 output for every query row: array [total_q][Hq][head_dim]."""
     T, H = batch.total_q, batch.num_q_heads
     tok = np.repeat(np.arange(T, dtype=np.int64), H)
     head = np.tile(np.arange(H, dtype=np.int32), T)
     res = attention_rows(batch, tok, head, threads=threads, with_lse=with_lse, lib=lib,
-                         window=window)
+                         window=window, causal=causal)
     if with_lse:
         out, lse = res
         return out.reshape(T, H, batch.head_dim), lse.reshape(T, H)

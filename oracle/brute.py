@@ -19,11 +19,12 @@ def _tolist(t):
     return t.tolist() if hasattr(t, "tolist") else list(t)
 
 
-def brute_force(batch, window: int = 0):
+def brute_force(batch, window: int = 0, causal: bool = True):
     """Return nested lists out[total_q][Hq][d] for a small CPU PagedBatch.
 
     With window > 0 the query at position p lists only the keys at positions
-    p - window + 1 .. p (the sliding window of the model notes, section 4.1)."""
+    p - window + 1 .. p (the sliding window of the model notes, section 4.1);
+    with causal=False every row lists all keys of its sequence."""
     q = _tolist(batch.q.double())
     k_pool = _tolist(batch.k_cache.double())
     v_pool = _tolist(batch.v_cache.double())
@@ -40,7 +41,8 @@ def brute_force(batch, window: int = 0):
         n_q = cu[b + 1] - cu[b]
         for i in range(n_q):
             t = cu[b] + i
-            newest = seq_lens[b] - n_q + i  # position of this query token
+            # the row's last visible key: its own position, or the last key
+            newest = seq_lens[b] - n_q + i if causal else seq_lens[b] - 1
             rows = []
             for h in range(Hq):
                 kv_head = h // per_kv

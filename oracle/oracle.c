@@ -26,6 +26,10 @@
  *                                       sees every cached key)
  *   j0     = 0, or max(0, p - W + 1) with a sliding window of W > 0
  *   s_j    = scale * sum_c q[c] * K_b[j][c],   j = j0 .. p
+ *
+ *   Without the causal mask (the ragged, cache-free attention of encoder-style
+ *   embedding models, "Fast embeddings on GPUs": ragged inputs, no KV cache)
+ *   every row of sequence b sees all L_b keys: p = L_b - 1 for every row.
  *   m      = max(max_j s_j, sink_h)
  *   den    = sum_j exp(s_j - m) + exp(sink_h - m)
  *   out    = sum_j exp(s_j - m) * V_b[j] / den
@@ -104,6 +108,7 @@ static int owner_seq(const int32_t *cu_seqlens_q, int num_seqs, int64_t t)
  *   cu_seqlens_q [num_seqs + 1] query offsets (decode: 0, 1, 2, ...)
  *   sinks        [Hq] fp32, or NULL meaning every sink is -inf
  *   window       sliding window W (keys p - W + 1 .. p), or 0 for none
+ *   causal       1: bottom-right causal mask; 0: every row sees all keys
  *   row_token    [n_rows] query token index t in [0, total_q)
  *   row_head     [n_rows] query head h in [0, Hq)
  *   out          [n_rows][d] fp64
@@ -116,7 +121,7 @@ int oracle_attention_rows(int dtype, int num_seqs, int num_q_heads, int num_kv_h
                           const void *q, const void *k_cache, const void *v_cache,
                           const int32_t *block_table, const int32_t *seq_lens,
                           const int32_t *cu_seqlens_q, const float *sinks, double scale,
-                          int window, int64_t n_rows, const int64_t *row_token, const int32_t *row_head,
+                          int window, int causal, int64_t n_rows, const int64_t *row_token, const int32_t *row_head,
                           double *out, double *lse, int num_threads)
 {
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
@@ -155,7 +160,9 @@ int oracle_attention_rows(int dtype, int num_seqs, int num_q_heads, int num_kv_h
             const int q_len = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
             const int i = (int)(t - cu_seqlens_q[b]);
             const int pos = seq_lens[b] - q_len + i;
-            const int n_vis = pos + 1 < 0 ? 0 : pos + 1;
+            /* the row's last visible key */
+            const int last = causal ? pos : seq_lens[b] - 1;
+            const int n_vis = last + 1 < 0 ? 0 : last + 1;
             const int j0 = (window > 0 && n_vis - window > 0) ? n_vis - window : 0;
             const int g = h / group;
             const double sink = sinks ? (double)sinks[h] : -INFINITY;

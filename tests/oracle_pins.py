@@ -25,6 +25,11 @@ The facts used:
     (torch SDPA) times sigmoid(LSE - sink); W = 1 is the single-key closed
     form on the query's own key; and a windowed decode equals an unwindowed
     decode over a pool that holds only the last W tokens;
+  * without the causal mask (ragged, cache-free attention of embedding
+    models, "Fast embeddings on GPUs"): the brute force and unmasked SDPA
+    times sigmoid(LSE - sink);
+  * the LSE the oracle reports is log(sum_j e^(s_j) + e^sink), i.e.
+    torch.logaddexp(torch.logsumexp(visible logits), sink);
   * KV append (model notes, section 3: K and V are appended before the
     attention step): appending the newest tokens into a pool where their
     slots are blank rebuilds, bit for bit, the pool the input generator laid
@@ -52,12 +57,12 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "han
 
 # ---------------------------------------------------------------- references
 
-def sdpa_reference(batch, window=0):
+def sdpa_reference(batch, window=0, causal=True):
     """Plain softmax attention (no sink) and per-row LSE, via torch fp64 CPU.
 
     Uses the logical K/V rows kept by the generator, GQA through
     enable_gqa=True, and an explicit bottom-right causal mask (a band of the
-    last `window` positions when window > 0).
+    last `window` positions when window > 0; every key when causal=False).
     Returns (out [total_q][Hq][d], lse [total_q][Hq]) as numpy fp64.
     """
     assert batch.k_logical is not None, "build the batch with keep_logical=True"
@@ -75,6 +80,8 @@ def sdpa_reference(batch, window=0):
         i = torch.arange(nq).unsqueeze(1)
         j = torch.arange(L).unsqueeze(0)
         mask = j <= (L - nq + i)                                               # nq, L
+        if not causal:
+            mask = torch.ones_like(mask)
         if window > 0:
             mask = mask & (j > (L - nq + i) - window)
         o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=batch.scale,
@@ -344,6 +351,35 @@ def pin_window_truncation(attn):
         _close(attn(b, window=w), attn(t), 1e-12, 1e-14, f"window {w} vs truncated pool")
 
 
+# ------------------------------------------------------ no causal mask, LSE
+
+def pin_noncausal_brute(attn):
+    for b in tiny_batches():
+        ref = np.array(brute_force(b, causal=False))
+        _close(attn(b, causal=False), ref, 1e-12, 1e-13, f"brute force, no mask {b.dtype}")
+
+
+def pin_noncausal_sdpa(attn):
+    for seed, mode in ((151, "normal"), (152, "neginf")):
+        b = medium_batch(seed, sink_mode=mode)
+        ref, lse = sdpa_reference(b, causal=False)
+        if mode == "normal":
+            ref = ref * sigmoid(lse - b.sinks.double().numpy()[None, :])[..., None]
+        _close(attn(b, causal=False), ref, 1e-11, 1e-13, f"unmasked SDPA ({mode})")
+
+
+def pin_lse(attn):
+    for seed, causal in ((161, True), (162, False)):
+        b = medium_batch(seed)
+        _, lse = attn(b, with_lse=True, causal=causal)
+        _, lse_keys = sdpa_reference(b, causal=causal)
+        expect = np.logaddexp(lse_keys, b.sinks.double().numpy()[None, :])
+        _close(lse, expect, 1e-12, 1e-12, f"LSE with the sink (causal {causal})")
+        nb = replace(b, sinks=None)
+        _, lse0 = attn(nb, with_lse=True, causal=causal)
+        _close(lse0, lse_keys, 1e-12, 1e-12, f"LSE without a sink (causal {causal})")
+
+
 # ----------------------------------------------------------------- KV append
 
 def _same_bits(a, b):
@@ -380,4 +416,5 @@ def pin_append(attn):
 ALL_PINS = [pin_golden, pin_brute, pin_plain_is_sdpa, pin_closed_form, pin_large_and_half_sink,
             pin_single_key, pin_page_permutation, pin_prefill_row_is_decode, pin_gqa_groups,
             pin_empty_rows, pin_window_wide_is_full, pin_window_brute, pin_window_band_sdpa,
-            pin_window_one, pin_window_truncation, pin_append]
+            pin_window_one, pin_window_truncation, pin_append, pin_noncausal_brute,
+            pin_noncausal_sdpa, pin_lse]

@@ -7,8 +7,8 @@ from gqa_paged_attention_amd import workloads as wl
 from tests import oracle_pins as pins
 
 
-def _attn(batch, with_lse=False, window=0):
-    return oracle.attention(batch, threads=4, with_lse=with_lse, window=window)
+def _attn(batch, with_lse=False, window=0, causal=True):
+    return oracle.attention(batch, threads=4, with_lse=with_lse, window=window, causal=causal)
 
 
 @pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)

@@ -21,8 +21,12 @@ MUTANTS = {
     "scale dropped": ("scores[j] = scale * dot;", "scores[j] = dot;"),
     "GQA head mapping h % Hkv": ("const int g = h / group;", "const int g = h % num_kv_heads;"),
     "top-left causal alignment": ("const int pos = seq_lens[b] - q_len + i;", "const int pos = i;"),
-    "last key excluded": ("const int n_vis = pos + 1 < 0 ? 0 : pos + 1;",
-                          "const int n_vis = pos < 0 ? 0 : pos;"),
+    "last key excluded": ("const int n_vis = last + 1 < 0 ? 0 : last + 1;",
+                          "const int n_vis = last < 0 ? 0 : last;"),
+    "causal flag ignored": ("const int last = causal ? pos : seq_lens[b] - 1;",
+                            "const int last = pos;"),
+    "unmasked rows stop at the chunk start": ("const int last = causal ? pos : seq_lens[b] - 1;",
+                                              "const int last = causal ? pos : seq_lens[b] - q_len;"),
     "page slot from the wrong index": ("* page_size + (j % page_size)) * head_dim;",
                                        "* page_size + (j / page_size) % page_size) * head_dim;"),
     "K and V swapped": ("dot += qrow[c] * widen(k_cache, row + c, dtype);",
@@ -56,8 +60,9 @@ def test_mutant_is_caught(tmp_path, name):
     old, new = MUTANTS[name]
     lib = _build(tmp_path, name, old, new)
 
-    def attn(batch, with_lse=False, window=0):
-        return oracle.attention(batch, threads=4, with_lse=with_lse, lib=lib, window=window)
+    def attn(batch, with_lse=False, window=0, causal=True):
+        return oracle.attention(batch, threads=4, with_lse=with_lse, lib=lib, window=window,
+                                causal=causal)
 
     failures = []
     for pin in pins.ALL_PINS:
