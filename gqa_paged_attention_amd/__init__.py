@@ -69,6 +69,8 @@ def library():
     lib.attn_sinks_decode_multi_workspace_bytes.restype = Z
     lib.attn_sinks_decode_multi.argtypes = [I] * 11 + [P] * 7 + [F, P, P, Z, P]
     lib.attn_sinks_decode_multi.restype = I
+    lib.attn_sinks_ragged.argtypes = [I] * 10 + [P] * 6 + [F, P, P, P]
+    lib.attn_sinks_ragged.restype = I
     lib.attn_sinks_status_string.argtypes = [I]
     lib.attn_sinks_status_string.restype = ctypes.c_char_p
     lib.attn_sinks_version.argtypes = []
@@ -378,6 +380,34 @@ def attn_sinks_decode_multi(q, k_cache, v_cache, block_table, seq_lens, cu_seqle
         int(max_seq_len), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(seq_lens), _ptr(cu_seqlens_q), _ptr(sinks), ctypes.c_float(scale), _ptr(out),
         _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream))
+    _raise(status)
+
+
+def attn_sinks_ragged(q, k, v, cu_seqlens_q, cu_seqlens_kv, sinks, scale: float, causal: bool,
+                      out, lse, max_q_len: int, max_kv_len: int, stream=None) -> None:
+    """Enqueue attn_sinks_ragged: contiguous K/V rows per sequence (no KV
+    cache), optional causal mask, out [total_q][Hq][d] and, when `lse` is a
+    tensor, the fp32 natural-log LSE [total_q][Hq]."""
+    dt = _DTYPE_CODE.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check_dense(name, t, q.dtype)
+    _check_dense("cu_seqlens_q", cu_seqlens_q, torch.int32)
+    _check_dense("cu_seqlens_kv", cu_seqlens_kv, torch.int32)
+    _check_dense("sinks", sinks, torch.float32)
+    _check_dense("lse", lse, torch.float32)
+    T, Hq, d = q.shape
+    Tk, Hkv, d2 = k.shape
+    B = cu_seqlens_q.numel() - 1
+    if d2 != d or tuple(v.shape) != tuple(k.shape) or tuple(out.shape) != (T, Hq, d):
+        raise ValueError("q / k / v / out shapes disagree")
+    if cu_seqlens_kv.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv differ in length")
+    status = library().attn_sinks_ragged(
+        dt, B, Hq, Hkv, d, T, Tk, int(max_q_len), int(max_kv_len), int(bool(causal)), _ptr(q),
+        _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), _ptr(sinks),
+        ctypes.c_float(scale), _ptr(out), _ptr(lse), _stream_handle(stream))
     _raise(status)
 
 

@@ -392,6 +392,9 @@ int attn_sinks_prefill_window(int dtype, int num_seqs, int num_q_heads, int num_
     p.max_q_len = max_q_len;
     p.max_seq_len = max_seq_len;
     p.window = window;
+    p.cu_seqlens_kv = nullptr;
+    p.causal = 1;
+    p.lse = nullptr;
     p.q = q;
     p.k_cache = k_cache;
     p.v_cache = v_cache;
@@ -551,6 +554,70 @@ int attn_sinks_decode_multi(int dtype, int num_seqs, int num_q_heads, int num_kv
     if (attn::launch_decode_split_bf16(p) != hipSuccess)
         return ATTN_ERR_HIP;
     return attn::launch_decode_merge(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_sinks_ragged(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int total_q, int total_kv, int max_q_len, int max_kv_len, int causal,
+                      const void *q, const void *k, const void *v, const int32_t *cu_seqlens_q,
+                      const int32_t *cu_seqlens_kv, const float *sinks, float scale, void *out,
+                      float *lse, void *stream)
+{
+    if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16)
+        return ATTN_ERR_UNSUPPORTED;
+    if (dtype != ATTN_DTYPE_BF16 || !supported_head_dim(head_dim))
+        return ATTN_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || total_q < 0 || total_kv < 0 ||
+        max_q_len < 0 || max_kv_len < 0 || max_q_len > total_q || max_kv_len > total_kv ||
+        (causal != 0 && causal != 1) || num_q_heads % num_kv_heads != 0)
+        return ATTN_ERR_SHAPE;
+    if (num_q_heads / num_kv_heads > kMaxGroup)
+        return ATTN_ERR_UNSUPPORTED;
+    if (causal && max_q_len > max_kv_len)
+        return ATTN_ERR_SHAPE;
+    if (num_seqs > 65535 || num_q_heads > 65535)
+        return ATTN_ERR_SHAPE;
+    // the per-lane byte offsets of a sequence's K/V rows must fit 31 bits
+    if ((long long)max_kv_len * num_kv_heads * head_dim * 2 >= (1LL << 31))
+        return ATTN_ERR_SHAPE;
+    if (!std::isfinite(scale))
+        return ATTN_ERR_SHAPE;
+    if (num_seqs == 0 || total_q == 0)
+        return ATTN_OK;
+    if (!q || !out || !cu_seqlens_q || !cu_seqlens_kv || (total_kv > 0 && (!k || !v)))
+        return ATTN_ERR_NULL;
+    const void *vec[] = {q, k, v, out};
+    for (const void *ptr : vec)
+        if (ptr && !aligned16(ptr))
+            return ATTN_ERR_ALIGN;
+    const void *words[] = {cu_seqlens_q, cu_seqlens_kv, sinks, lse};
+    for (const void *ptr : words)
+        if (ptr && !aligned4(ptr))
+            return ATTN_ERR_ALIGN;
+    attn::PrefillLaunch p;
+    p.dtype = dtype;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.head_dim = head_dim;
+    p.max_pages_per_seq = 0;
+    p.total_q = total_q;
+    p.max_q_len = max_q_len;
+    p.max_seq_len = max_kv_len;
+    p.window = 0;
+    p.cu_seqlens_kv = cu_seqlens_kv;
+    p.causal = causal;
+    p.lse = lse;
+    p.q = q;
+    p.k_cache = k;
+    p.v_cache = v;
+    p.block_table = nullptr;
+    p.seq_lens = nullptr;
+    p.cu_seqlens_q = cu_seqlens_q;
+    p.sinks = sinks;
+    p.scale = scale;
+    p.out = out;
+    p.stream = reinterpret_cast<hipStream_t>(stream);
+    return attn::launch_prefill_bf16(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 const char *attn_sinks_status_string(int status)

@@ -32,6 +32,11 @@ struct PrefillLaunch {
     int num_seqs, num_q_heads, num_kv_heads, head_dim;
     int max_pages_per_seq, total_q, max_q_len, max_seq_len;
     int window;         // sliding window W (keys p - W + 1 .. p), 0: none
+    // ragged cache-free attention: K/V rows [tokens][Hkv][d] at offsets
+    // cu_seqlens_kv [num_seqs + 1] (NULL: the paged cache and block_table)
+    const int32_t *cu_seqlens_kv;
+    int causal;         // 0: every row sees all keys of its sequence
+    float *lse;         // [total_q][Hq] natural-log LSE (sink included), or NULL
     const void *q, *k_cache, *v_cache;
     const int32_t *block_table, *seq_lens, *cu_seqlens_q;
     const float *sinks;

@@ -58,6 +58,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kKB = 32;          // keys per block: one 32x32 S^T tile
+constexpr float kLn2 = 0.693147180559945309417f;
 // A running row sum (per lane) above this triggers the exact recompute.
 constexpr float kWeightSumLimit = 18446744073709551616.0f;  // 2^64
 
@@ -144,6 +145,13 @@ struct PrefillArgs {
     int num_seqs, num_q_heads, num_kv_heads, group, max_pages, num_q_tiles;
     int xcd_groups;  // (sequence, KV head) groups laid out XCD by XCD
     int window;      // sliding window W (keys p - W + 1 .. p), 0: none
+    // Ragged cache-free mode: K/V rows [tokens][Hkv][d] with per-sequence
+    // offsets cu_seqlens_kv (NULL: the paged cache above), row stride
+    // kv_stride = Hkv d elements.
+    const int32_t *__restrict__ cu_seqlens_kv;
+    int kv_stride;
+    int causal;        // 1: bottom-right causal; 0: every row sees all keys
+    float *__restrict__ lse;  // [total_q][Hq] natural-log row LSE (sink included), or NULL
     float scale_log2;
 };
 
@@ -261,9 +269,13 @@ __device__ __forceinline__ ChunkPages chunk_pages(const int32_t *__restrict__ bt
 // Issue this wave's direct loads of tile t (keys t*BN ..) into stage t % S.
 // Rows past the sequence repeat its last row (finite; the causal mask hides
 // them); their page index is clamped to the last page, which holds that row.
-template <int D>
+// kContig: K/V rows are contiguous [tokens][Hkv][d] and kv_off is the element
+// offset of the sequence's key 0 for this KV head (the 16-byte chunks of one
+// load then come from R rows kv_stride apart).  Paged: kv_off is the head's
+// offset inside a page (g * 16 * d).
+template <int D, bool kContig>
 __device__ __forceinline__ void load_tile(const Smem<D> &sm, const PrefillArgs &a, const ChunkPages &cp,
-                                          int t, int L, size_t head_off, int wave,
+                                          int t, int L, size_t kv_off, int wave,
                                           const LoadLanes<D> &ll)
 {
     using C = Cfg<D>;
@@ -272,10 +284,17 @@ __device__ __forceinline__ void load_tile(const Smem<D> &sm, const PrefillArgs &
 #pragma unroll
     for (int i = 0; i < C::kChunksPerWave; ++i) {
         const int j = wave + kWaves * i;
-        const size_t slab = (size_t)cp.p[i] * a.num_kv_heads * 16 * D + head_off;
-        const int row = kv0 + ll.key[i] < L ? (ll.key[i] & 15) : ((L - 1) & 15);
-        dma16(a.k_cache + slab, 2 * (row * D + ll.kc[i]), sm.k(stage) + 512 * j);
-        dma16(a.v_cache + slab, 2 * (row * D + ll.vc[i]), sm.v(stage) + 512 * j);
+        if constexpr (kContig) {
+            const int tok = min(kv0 + ll.key[i], L - 1);
+            const uint32_t row = (uint32_t)tok * (uint32_t)a.kv_stride;
+            dma16(a.k_cache + kv_off, 2 * (row + ll.kc[i]), sm.k(stage) + 512 * j);
+            dma16(a.v_cache + kv_off, 2 * (row + ll.vc[i]), sm.v(stage) + 512 * j);
+        } else {
+            const size_t slab = (size_t)cp.p[i] * a.num_kv_heads * 16 * D + kv_off;
+            const int row = kv0 + ll.key[i] < L ? (ll.key[i] & 15) : ((L - 1) & 15);
+            dma16(a.k_cache + slab, 2 * (row * D + ll.kc[i]), sm.k(stage) + 512 * j);
+            dma16(a.v_cache + slab, 2 * (row * D + ll.vc[i]), sm.v(stage) + 512 * j);
+        }
     }
 }
 
@@ -440,7 +459,7 @@ template <int D, bool kQK, bool kPV, bool kMasked, bool kFirst>
 __device__ __forceinline__ void step(WaveState<D> &w, const Smem<D> &sm, int b,
                                      f32x16_t (&s_cur)[Cfg<D>::kNRB],
                                      f32x16_t (&s_next)[Cfg<D>::kNRB], int thr0, float scale_log2,
-                                     int lane, bool &bad)
+                                     int lane, bool &bad, int rb_step)
 {
     constexpr int NRB = Cfg<D>::kNRB;
     u32x4_t kop[D / 16], vop[D / 32][2];
@@ -458,7 +477,7 @@ __device__ __forceinline__ void step(WaveState<D> &w, const Smem<D> &sm, int b,
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
         if (kMasked)
-            apply_mask(s_cur[rb], thr0 + 32 * rb);
+            apply_mask(s_cur[rb], thr0 + rb_step * rb);
         // the first block sets the reference exactly; key 0 is visible to
         // every row, so it is finite from then on
         if (kFirst)
@@ -504,10 +523,10 @@ struct RawBlock {
     u32x4_t k[kPer], v[kPer];
 };
 
-template <int D>
+template <int D, bool kContig = false>
 __device__ __forceinline__ void fetch_block(RawBlock<D> &rb, const PrefillArgs &a,
                                             const int32_t *__restrict__ bt, int L,
-                                            size_t head_off, int k0, int lane)
+                                            size_t kv_off, int k0, int lane)
 {
     constexpr int kChunks = D / 8;
 #pragma unroll
@@ -515,9 +534,14 @@ __device__ __forceinline__ void fetch_block(RawBlock<D> &rb, const PrefillArgs &
         const int c = lane + 64 * i;
         const int key = c / kChunks, chunk = c % kChunks;
         const int tok = min(k0 + key, L - 1);
-        const int page = bt[tok >> 4];
-        const size_t off = (size_t)page * a.num_kv_heads * 16 * D + head_off +
-                           (size_t)(tok & 15) * D + 8 * chunk;
+        size_t off;
+        if constexpr (kContig) {
+            off = kv_off + (size_t)tok * a.kv_stride + 8 * chunk;
+        } else {
+            const int page = bt[tok >> 4];
+            off = (size_t)page * a.num_kv_heads * 16 * D + kv_off + (size_t)(tok & 15) * D +
+                  8 * chunk;
+        }
         rb.k[i] = *(const u32x4_t *)(a.k_cache + off);
         rb.v[i] = *(const u32x4_t *)(a.v_cache + off);
     }
@@ -548,7 +572,8 @@ __device__ __forceinline__ void stash_block(const RawBlock<D> &rb, uint16_t *kt,
 template <int D, bool kBand>
 __device__ __forceinline__ void exact_block(WaveState<D> &w, const uint16_t *kt,
                                             const uint16_t *vt, bool masked, int thr,
-                                            int window, float scale_log2, int lane)
+                                            int window, float scale_log2, int lane,
+                                            int rb_step = 32)
 {
     u32x4_t kop[D / 16], vop[D / 32][2];
     read_k<D>(kop, kt, 0, lane);
@@ -557,9 +582,9 @@ __device__ __forceinline__ void exact_block(WaveState<D> &w, const uint16_t *kt,
     for (int rb = 0; rb < Cfg<D>::kNRB; ++rb) {
         f32x16_t s = qk_mfma<D>(w.qop[rb], kop);
         if (kBand)
-            apply_band(s, thr + 32 * rb, window);
+            apply_band(s, thr + rb_step * rb, window);
         else if (masked)
-            apply_mask(s, thr + 32 * rb);
+            apply_mask(s, thr + rb_step * rb);
         const float m_new = fmaxf(w.m[rb], block_max(s, scale_log2));
         const float m_ref = m_new == kNegInf ? 0.f : m_new;
         const float alpha = exp2_fast(w.m[rb] - m_ref);  // 0 while m is -inf
@@ -579,10 +604,10 @@ __device__ __forceinline__ void exact_block(WaveState<D> &w, const uint16_t *kt,
 // overflow against the reference taken from the first block).  K and V come
 // straight from the paged cache into this wave's own part of the LDS (the
 // workgroup has met after its pipelined loop, so nothing else reads it).
-template <int D>
+template <int D, bool kContig>
 __device__ void exact_rows(WaveState<D> &w, uint16_t *lds_wave, const PrefillArgs &a,
-                           const int32_t *__restrict__ bt, int L, size_t head_off, int nb,
-                           int wpf, int thr, int lane)
+                           const int32_t *__restrict__ bt, int L, size_t kv_off, int nb,
+                           int wpf, int thr, int rb_step, int lane)
 {
     constexpr int NRB = Cfg<D>::kNRB;
     uint16_t *kt = lds_wave;
@@ -598,9 +623,10 @@ __device__ void exact_rows(WaveState<D> &w, uint16_t *lds_wave, const PrefillArg
     for (int blk = 0; blk < nb; ++blk) {
         const int k0 = kKB * blk;
         RawBlock<D> raw;
-        fetch_block<D>(raw, a, bt, L, head_off, k0, lane);
+        fetch_block<D, kContig>(raw, a, bt, L, kv_off, k0, lane);
         stash_block<D>(raw, kt, vt, lane);
-        exact_block<D, false>(w, kt, vt, k0 + kKB - 1 > wpf, thr - k0, 0, a.scale_log2, lane);
+        exact_block<D, false>(w, kt, vt, k0 + kKB - 1 > wpf, thr - k0, 0, a.scale_log2, lane,
+                              rb_step);
     }
 }
 
@@ -678,14 +704,19 @@ __device__ __forceinline__ void store_rows(const WaveState<D> &w, uint16_t *stag
         halves(w.lsum[rb], lx, ly);
         const float lsum = lx + ly;
         const float M = fmaxf(w.m[rb], sink2);
-        float scale = 0.f;
+        float scale = 0.f, lse = kNegInf;
         if (M != kNegInf) {
             const float f = w.m[rb] == kNegInf ? 0.f : exp2_fast(w.m[rb] - M);
             const float den = lsum * f + (sink2 == kNegInf ? 0.f : exp2_fast(sink2 - M));
             scale = den > 0.f ? f / den : 0.f;
+            // natural log of the row's softmax denominator, sink included
+            if (den > 0.f)
+                lse = (M + __builtin_amdgcn_logf(den)) * kLn2;
         }
         // lane l holds dims 32 db + 8 r4 + 4 (l/32) .. +3 of row 32 rb + l%32
         const int r = 32 * rb + r32;
+        if (a.lse && half == 0 && row_w + r < q_len)
+            a.lse[(size_t)(q0 + row_w + r) * a.num_q_heads + h] = lse;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -710,7 +741,9 @@ __device__ __forceinline__ void store_rows(const WaveState<D> &w, uint16_t *stag
     }
 }
 
-template <int D>
+// kContig: ragged cache-free attention over contiguous K/V rows (with or
+// without the causal mask); otherwise the paged cache.
+template <int D, bool kContig>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
 {
     using C = Cfg<D>;
@@ -723,37 +756,56 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     const int row0 = qt * C::kBM;
     if (row0 >= q_len)
         return;  // uniform over the workgroup
-    const int L = a.seq_lens[b];
+    const int kv_first = kContig ? a.cu_seqlens_kv[b] : 0;
+    const int L = kContig ? a.cu_seqlens_kv[b + 1] - kv_first : a.seq_lens[b];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int r32 = lane & 31, half = lane >> 5;
-    const int shift = L - q_len;  // position of query row i is shift + i
+    // Position of query row i: shift + i (causal, aligned to the end of the
+    // keys); without the causal mask every row is treated as the last
+    // position, L - 1, so that it sees all keys.
+    const bool causal = !kContig || a.causal;
+    const int shift = L - q_len;
+    const int row_step = causal ? 1 : 0;
+    const int rbs = 32 * row_step;  // position step between row blocks
 
     // this wave's rows: row_w + 32 rb + r32
     const int row_w = row0 + 32 * NRB * wave;
 
     // keys needed by the workgroup (tiles) and by this wave (blocks)
     const int last_row = min(row0 + C::kBM, q_len) - 1;
-    const int kv_end = min(shift + last_row + 1, L);
+    const int kv_end = causal ? min(shift + last_row + 1, L) : L;
     const int ntiles = (kv_end + C::kBN - 1) / C::kBN;
     const int wave_last = min(row_w + 32 * NRB - 1, q_len - 1);
-    const int nb = row_w < q_len ? (min(shift + wave_last + 1, L) + kKB - 1) / kKB : 0;
-    const int wpf = shift + row_w;  // position of the wave's first row
+    const int nb = row_w < q_len
+                       ? ((causal ? min(shift + wave_last + 1, L) : L) + kKB - 1) / kKB
+                       : 0;
+    // position of the wave's first row
+    const int wpf = causal ? shift + row_w : L - 1;
 
     extern __shared__ __align__(16) uint16_t lds[];
     const Smem<D> sm{lds};
-    const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
+    const int32_t *bt = kContig ? nullptr : a.block_table + (size_t)b * a.max_pages;
     const int last_page = (L - 1) >> 4;
-    const size_t head_off = (size_t)g * 16 * D;
+    // the KV head's data: element offset of its key 0 (contiguous rows), or
+    // its offset inside a page
+    const size_t kv_off = kContig ? (size_t)kv_first * a.kv_stride + (size_t)g * D
+                                  : (size_t)g * 16 * D;
 
     // tiles 0 and 1 in flight before the loop; tile T+2 is issued when the
     // wave starts reading tile T
     const LoadLanes<D> ll = load_lanes<D>(wave, lane);
+    auto pages = [&](int t) {
+        if constexpr (kContig)
+            return ChunkPages{{0, 0}};
+        else
+            return chunk_pages<D>(bt, t, last_page, wave);
+    };
 #pragma unroll
     for (int t = 0; t < 2; ++t)
         if (t < ntiles)
-            load_tile<D>(sm, a, chunk_pages<D>(bt, t, last_page, wave), t, L, head_off, wave, ll);
-    ChunkPages next_pages = chunk_pages<D>(bt, 2, last_page, wave);
+            load_tile<D, kContig>(sm, a, pages(t), t, L, kv_off, wave, ll);
+    ChunkPages next_pages = pages(2);
 
     // Q while the first tiles load; one wait covers both (the compiler then
     // knows the Q registers are ready and adds no waits inside the loops)
@@ -775,15 +827,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
             if (t < ntiles) {
                 wait_loads_and_sync<2 * C::kChunksPerWave>(t + 1 >= ntiles);
                 if (t + 2 < ntiles) {
-                    load_tile<D>(sm, a, next_pages, t + 2, L, head_off, wave, ll);
-                    next_pages = chunk_pages<D>(bt, t + 3, last_page, wave);
+                    load_tile<D, kContig>(sm, a, next_pages, t + 2, L, kv_off, wave, ll);
+                    next_pages = pages(t + 3);
                 }
             }
         }
     };
     // blocks from bm on hold keys past the wave's first row: causal mask
     const int bm = (wpf + 1) / kKB;
-    const int thr = wpf + r32 - 4 * half;  // minus the block start
+    const int thr = wpf + row_step * r32 - 4 * half;  // minus the block start
     const float sl2 = a.scale_log2;
     // S^T of the block whose weights are next, and of the one after: two
     // register sets that trade roles every step (the steady loop is unrolled
@@ -800,14 +852,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     tile_start(0);
     if (nb > 1) {
         if (bm == 0)
-            step<D, true, false, true, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad);
+            step<D, true, false, true, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad, rbs);
         else
-            step<D, true, false, false, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad);
+            step<D, true, false, false, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad, rbs);
     } else if (nb == 1) {
         if (bm == 0)
-            step<D, false, false, true, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad);
+            step<D, false, false, true, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad, rbs);
         else
-            step<D, false, false, false, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad);
+            step<D, false, false, false, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad, rbs);
     }
     // Steps 1 .. nb-2: all three stages, in pairs (sb then sa holds the
     // current S^T), so that no register copy is needed; step 0 left S^T of
@@ -819,9 +871,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     if (nb >= 3 && (nb & 1)) {
         tile_start(1);
         if (bm <= 1)
-            step<D, true, true, true, false>(w, sm, 1, sb, sa, thr - kKB, sl2, lane, bad);
+            step<D, true, true, true, false>(w, sm, 1, sb, sa, thr - kKB, sl2, lane, bad, rbs);
         else
-            step<D, true, true, false, false>(w, sm, 1, sb, sa, 0, sl2, lane, bad);
+            step<D, true, true, false, false>(w, sm, 1, sb, sa, 0, sl2, lane, bad, rbs);
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
             sb[rb] = sa[rb];
@@ -829,25 +881,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     }
     for (; j + 1 < min(bm, nb - 1); j += 2) {
         tile_start(j);
-        step<D, true, true, false, false>(w, sm, j, sb, sa, 0, sl2, lane, bad);
+        step<D, true, true, false, false>(w, sm, j, sb, sa, 0, sl2, lane, bad, rbs);
         tile_start(j + 1);
-        step<D, true, true, false, false>(w, sm, j + 1, sa, sb, 0, sl2, lane, bad);
+        step<D, true, true, false, false>(w, sm, j + 1, sa, sb, 0, sl2, lane, bad, rbs);
     }
     for (; j + 1 < nb - 1; j += 2) {
         tile_start(j);
-        step<D, true, true, true, false>(w, sm, j, sb, sa, thr - kKB * j, sl2, lane, bad);
+        step<D, true, true, true, false>(w, sm, j, sb, sa, thr - kKB * j, sl2, lane, bad, rbs);
         tile_start(j + 1);
         step<D, true, true, true, false>(w, sm, j + 1, sa, sb, thr - kKB * (j + 1), sl2, lane,
-                                         bad);
+                                         bad, rbs);
     }
     // step nb-1: weights of the last block (S^T in sb), P*V of the one before
     if (nb > 1) {
         tile_start(nb - 1);
         if (nb - 1 >= bm)
             step<D, false, true, true, false>(w, sm, nb - 1, sb, sb, thr - kKB * (nb - 1), sl2,
-                                              lane, bad);
+                                              lane, bad, rbs);
         else
-            step<D, false, true, false, false>(w, sm, nb - 1, sb, sb, 0, sl2, lane, bad);
+            step<D, false, true, false, false>(w, sm, nb - 1, sb, sb, 0, sl2, lane, bad, rbs);
     }
     // step nb: P*V of the last block
     if (nb > 0) {
@@ -858,8 +910,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
         tile_start(j);
     __syncthreads();  // every wave is past its last read of the stages
     if (__any(bad))
-        exact_rows<D>(w, lds + wave * (C::kLdsBytes / 2 / kWaves), a, bt, L, head_off, nb, wpf, thr,
-                      lane);
+        exact_rows<D, kContig>(w, lds + wave * (C::kLdsBytes / 2 / kWaves), a, bt, L, kv_off, nb,
+                               wpf, thr, rbs, lane);
 
     // Epilogue through this wave's part of the (now free) LDS.
     store_rows<D>(w, lds + wave * (C::kLdsBytes / 2 / kWaves), a, q0, q_len, row_w, h, lane);
@@ -953,6 +1005,10 @@ hipError_t launch_d(const PrefillLaunch &p)
     const int groups = p.num_seqs * p.num_kv_heads;
     a.xcd_groups = groups / 8 * 8;
     a.window = p.window;
+    a.cu_seqlens_kv = p.cu_seqlens_kv;
+    a.kv_stride = p.num_kv_heads * D;
+    a.causal = p.causal;
+    a.lse = p.lse;
     a.scale_log2 = p.scale * kLog2e;
     const long long wgs = (long long)groups * a.group * a.num_q_tiles;
     if (wgs > 0x7fffffffLL)
@@ -970,12 +1026,23 @@ hipError_t launch_d(const PrefillLaunch &p)
         return hipGetLastError();
     }
     // more than 64 KiB of LDS (d = 128) has to be allowed once per kernel
+    if (p.cu_seqlens_kv) {
+        static const hipError_t cattr = hipFuncSetAttribute(
+            (const void *)prefill_bf16<D, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+            C::kLdsBytes);
+        if (cattr != hipSuccess)
+            return cattr;
+        hipLaunchKernelGGL((prefill_bf16<D, true>), dim3((unsigned)wgs), dim3(kThreads),
+                           C::kLdsBytes, p.stream, a);
+        return hipGetLastError();
+    }
     static const hipError_t attr = hipFuncSetAttribute(
-        (const void *)prefill_bf16<D>, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+        (const void *)prefill_bf16<D, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        C::kLdsBytes);
     if (attr != hipSuccess)
         return attr;
-    hipLaunchKernelGGL(prefill_bf16<D>, dim3((unsigned)wgs), dim3(kThreads), C::kLdsBytes,
-                       p.stream, a);
+    hipLaunchKernelGGL((prefill_bf16<D, false>), dim3((unsigned)wgs), dim3(kThreads),
+                       C::kLdsBytes, p.stream, a);
     return hipGetLastError();
 }
 

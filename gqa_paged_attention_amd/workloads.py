@@ -160,6 +160,7 @@ def build_batch(
     page_size: int = PAGE_SIZE,
     keep_logical: bool = False,
     poison: bool = True,
+    causal_rows: bool = True,
 ) -> PagedBatch:
     """Draw q/K/V/sinks (steps 2-4 of the recipe) and lay them out in pages.
 
@@ -173,7 +174,8 @@ def build_batch(
     q_lens = torch.as_tensor(q_lens, dtype=torch.int32).flatten()
     if seq_lens.numel() != q_lens.numel():
         raise ValueError("seq_lens and q_lens differ in length")
-    if torch.any(q_lens > seq_lens):
+    if causal_rows and torch.any(q_lens > seq_lens):
+        # (rows without the causal mask may outnumber the keys)
         raise ValueError("a sequence has more query tokens than visible keys")
     B = seq_lens.numel()
     pages_per_seq = [(int(L) + page_size - 1) // page_size for L in seq_lens]
@@ -302,6 +304,51 @@ def split_new_tokens(batch: PagedBatch):
             k_old[page, :, slot] = float("nan")
             v_old[page, :, slot] = float("nan")
     return replace(batch, k_cache=k_old, v_cache=v_old), k_new, v_new
+
+
+@dataclass
+class RaggedBatch:
+    """Ragged inputs without a KV cache: q [total_q][Hq][d], k/v
+    [total_kv][Hkv][d] contiguous per sequence, offsets cu_seqlens_q /
+    cu_seqlens_kv.  `paged` holds the same values laid out in a paged pool
+    (for the oracle, which reads pages)."""
+
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    cu_seqlens_q: torch.Tensor
+    cu_seqlens_kv: torch.Tensor
+    sinks: Optional[torch.Tensor]
+    scale: float
+    paged: PagedBatch
+
+    @property
+    def max_q_len(self) -> int:
+        return int((self.cu_seqlens_q[1:] - self.cu_seqlens_q[:-1]).max().item())
+
+    @property
+    def max_kv_len(self) -> int:
+        return int((self.cu_seqlens_kv[1:] - self.cu_seqlens_kv[:-1]).max().item())
+
+    def to(self, device) -> "RaggedBatch":
+        mv = lambda t: None if t is None else t.to(device)
+        return replace(self, q=mv(self.q), k=mv(self.k), v=mv(self.v),
+                       cu_seqlens_q=mv(self.cu_seqlens_q), cu_seqlens_kv=mv(self.cu_seqlens_kv),
+                       sinks=mv(self.sinks))
+
+
+def ragged_batch(seed: int, dtype: str, kv_lens, q_lens, num_q_heads: int, num_kv_heads: int,
+                 head_dim: int, sink_mode: str = "normal", sink_std: float = 1.0) -> RaggedBatch:
+    """Same recipe as build_batch (lengths given; q, K, V, sinks drawn in that
+    order), K/V kept contiguous per sequence."""
+    gen = torch.Generator().manual_seed(seed)
+    b = build_batch(gen, dtype, kv_lens, q_lens, num_q_heads, num_kv_heads, head_dim,
+                    sink_mode=sink_mode, sink_std=sink_std, keep_logical=True,
+                    causal_rows=False)
+    cu_kv = b.kv_offsets.to(torch.int32)
+    return RaggedBatch(q=b.q, k=b.k_logical.contiguous(), v=b.v_logical.contiguous(),
+                       cu_seqlens_q=b.cu_seqlens_q, cu_seqlens_kv=cu_kv, sinks=b.sinks,
+                       scale=b.scale, paged=b)
 
 
 # --------------------------------------------------------------------------

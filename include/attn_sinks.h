@@ -321,6 +321,40 @@ int attn_sinks_decode_multi(int dtype, int num_seqs, int num_q_heads, int num_kv
                             const float *sinks, float scale, void *out, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/*
+ * Ragged attention without a KV cache: each sequence's keys and values are
+ * contiguous rows, as when an embedding model runs attention over ragged
+ * inputs and instantiates no KV cache ("Fast embeddings on GPUs": ragged
+ * attention kernels, no padding, no KV cache).  The same sink softmax as
+ * above; with causal = 1 the rows of sequence b (Lq_b <= L_b) are the last
+ * Lq_b positions of its L_b keys as in attn_sinks_prefill; with causal = 0
+ * every row sees all L_b keys.  Also writes each row's log-sum-exp, so that
+ * the result can be combined with attention states computed elsewhere.
+ *
+ *   q             [total_q][num_q_heads][head_dim]   bf16, rows as cu_seqlens_q says
+ *   k, v          [total_kv][num_kv_heads][head_dim] bf16, sequence b's keys are rows
+ *                 cu_seqlens_kv[b] .. cu_seqlens_kv[b+1]-1
+ *   cu_seqlens_q, cu_seqlens_kv  [num_seqs + 1] int32 offsets from 0
+ *   max_q_len, max_kv_len  host upper bounds of Lq_b and L_b
+ *   causal        1 or 0
+ *   sinks, scale  as above
+ *   out           [total_q][num_q_heads][head_dim] bf16 (written)
+ *   lse           [total_q][num_q_heads] fp32 (written), or NULL: the natural
+ *                 log of the row's softmax denominator,
+ *                 ln(sum_j e^(s_j) + e^(sink_h)), -inf for an empty row
+ *                 without a sink.  With sinks == NULL it is the plain LSE of
+ *                 the row's scores, which is what merging partial states
+ *                 needs (fold the sink once, at the end).
+ * bf16 only (ATTN_ERR_UNSUPPORTED otherwise); max_kv_len * num_kv_heads *
+ * head_dim * 2 must stay below 2^31 (ATTN_ERR_SHAPE).  Other conventions
+ * as above; nothing is allocated and no workspace is needed.
+ */
+int attn_sinks_ragged(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int total_q, int total_kv, int max_q_len, int max_kv_len, int causal,
+                      const void *q, const void *k, const void *v, const int32_t *cu_seqlens_q,
+                      const int32_t *cu_seqlens_kv, const float *sinks, float scale, void *out,
+                      float *lse, void *stream);
+
 /* Static English text for a status code (never NULL). */
 const char *attn_sinks_status_string(int status);
 

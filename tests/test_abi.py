@@ -298,3 +298,39 @@ def test_multi_rejects(lib, kw, code):
 def test_multi_empty(lib):
     assert _multi(lib, B=0) == OK
     assert _multi(lib, total_q=0, max_q=0) == OK
+
+
+def _ragged(lib, **kw):
+    args = dict(dtype=1, B=2, Hq=8, Hkv=2, d=64, Tq=40, Tk=100, mq=32, mk=64, causal=1,
+                q=FAKE, k=FAKE, v=FAKE, cq=FAKE, ck=FAKE, sinks=None, scale=0.125, out=FAKE,
+                lse=None)
+    args.update(kw)
+    return lib.attn_sinks_ragged(
+        args["dtype"], args["B"], args["Hq"], args["Hkv"], args["d"], args["Tq"], args["Tk"],
+        args["mq"], args["mk"], args["causal"], args["q"], args["k"], args["v"], args["cq"],
+        args["ck"], args["sinks"], ctypes.c_float(args["scale"]), args["out"], args["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), ERR_UNSUPPORTED),        # bf16 only
+    (dict(dtype=9), ERR_UNSUPPORTED),
+    (dict(d=256), ERR_UNSUPPORTED),
+    (dict(Hkv=3), ERR_SHAPE),
+    (dict(causal=2), ERR_SHAPE),
+    (dict(mq=41), ERR_SHAPE),                # > total_q
+    (dict(mk=101), ERR_SHAPE),               # > total_kv
+    (dict(mq=40, mk=30), ERR_SHAPE),         # causal rows need Lq <= L
+    (dict(mk=1 << 21, Tk=1 << 22, Hkv=8, Hq=8), ERR_SHAPE),   # 31-bit row offsets
+    (dict(scale=float("nan")), ERR_SHAPE),
+    (dict(ck=None), ERR_NULL),
+    (dict(k=None), ERR_NULL),
+    (dict(out=FAKE + 8), ERR_ALIGN),
+    (dict(lse=FAKE + 2), ERR_ALIGN),
+])
+def test_ragged_rejects(lib, kw, code):
+    assert _ragged(lib, **kw) == code
+
+
+def test_ragged_noncausal_allows_more_rows_than_keys(lib):
+    assert _ragged(lib, causal=0, mq=40, mk=30, B=0) == OK
+    assert _ragged(lib, Tq=0, mq=0) == OK
