@@ -314,6 +314,28 @@ def bench_multi(torch, ga, timer, steps, warmup, wl, q_len=4):
             "same_call_as_prefill_ms": round(rp["step_ms"], 4)}
 
 
+def bench_ragged(torch, ga, timer, steps, warmup, wl):
+    """Ragged cache-free attention (contiguous K/V, LSE written) on the
+    gpt-oss prefill shape, causal and unmasked, against the MFMA roofline."""
+    r = wl.ragged_batch(0, "bf16", [4096] * 8, [4096] * 8, 64, 8, 64, sink_mode="normal")
+    g = r.to("cuda")
+    out = torch.empty_like(g.q)
+    lse = torch.empty(g.q.shape[0], g.q.shape[1], dtype=torch.float32, device="cuda")
+    res = {}
+    for causal in (True, False):
+        t = timer.run([("ragged", lambda: ga.attn_sinks_ragged(
+            g.q, g.k, g.v, g.cu_seqlens_q, g.cu_seqlens_kv, g.sinks, g.scale, causal, out, lse,
+            r.max_q_len, r.max_kv_len))], steps, warmup, flush=True)
+        pairs = 8 * (4096 * 4097 // 2 if causal else 4096 * 4096)
+        fl = 4 * 64 * 64 * pairs
+        tf = fl / (t["step_ms"] * 1e-3) / 1e12
+        res["causal" if causal else "unmasked"] = {
+            "workload": "8 seqs x 4096 tokens, 64/8 heads, d 64, bf16, contiguous K/V, LSE out",
+            "algorithmic_flops": fl, "ms": round(t["step_ms"], 4), "TFLOP_per_s": round(tf, 1),
+            "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    return res
+
+
 def bench_mixed(torch, ga, timer, steps, warmup, wl):
     full, dec, pre = wl.mixed(0)
     gd, gp = dec.to("cuda"), pre.to("cuda")
@@ -523,6 +545,9 @@ def main():
         log("multi-token decode leg")
         extra["multi_token_decode"] = bench_multi(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["multi_token_decode"]))
+        log("ragged cache-free legs")
+        extra["ragged"] = bench_ragged(torch, ga, timer, K, W, wl)
+        log(json.dumps(extra["ragged"]))
         log("KV append legs")
         extra["kv_append"] = bench_append(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["kv_append"]))
