@@ -118,6 +118,9 @@ class Timer:
         self.flush_buf = flush_buf
 
     def run(self, stages, steps, warmup, flush=True):
+        """Time `steps` steps twice after the warm-up: once with events only
+        around each whole step (step_ms: nothing recorded between its
+        launches), once with an event after every stage (stage_ms)."""
         torch = self.torch
         n = len(stages)
         t_w = time.perf_counter()
@@ -129,28 +132,34 @@ class Timer:
                 fn()
             torch.cuda.synchronize()
             done += 1
-        events = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        walls = []
+        totals = []
+        per_stage = {name: [] for name, _ in stages}
+        for instrumented in (False, True):
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
                   for _ in range(steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for k in range(steps):
-            if flush:
-                self.flush_buf.fill_(k & 0xff)
-            ev = events[k]
-            ev[0].record()
-            for i, (_, fn) in enumerate(stages):
-                fn()
-                ev[i + 1].record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        per_stage = {name: [events[k][i].elapsed_time(events[k][i + 1]) for k in range(steps)]
-                     for i, (name, _) in enumerate(stages)}
-        total = [events[k][0].elapsed_time(events[k][n]) for k in range(steps)]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for k in range(steps):
+                if flush:
+                    self.flush_buf.fill_(k & 0xff)
+                ev[k][0].record()
+                for i, (_, fn) in enumerate(stages):
+                    fn()
+                    if instrumented or i == n - 1:
+                        ev[k][i + 1 if instrumented else n].record()
+            torch.cuda.synchronize()
+            walls.append(time.perf_counter() - t0)
+            if instrumented:
+                for i, (name, _) in enumerate(stages):
+                    per_stage[name] = [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)]
+            else:
+                totals = [ev[k][0].elapsed_time(ev[k][n]) for k in range(steps)]
         return {"stage_ms": {k: sum(v) / len(v) for k, v in per_stage.items()},
                 "stage_ms_min": {k: min(v) for k, v in per_stage.items()},
-                "step_ms": sum(total) / len(total),
-                "step_ms_median": sorted(total)[len(total) // 2],
-                "wall_s": wall}
+                "step_ms": sum(totals) / len(totals),
+                "step_ms_median": sorted(totals)[len(totals) // 2],
+                "wall_s": walls[0]}
 
 
 # --------------------------------------------------------------- workloads
