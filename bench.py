@@ -14,7 +14,9 @@ mixed batch, each against its own roofline, plus the fp64 CPU oracle timed on
 the host cores (a baseline, not a target).
 
 Modes used to make the committed profiles:
-    --profile-run            decode + prefill only, no oracle (run under rocprofv3)
+    --profile-run            decode + prefill only, no oracle (run under rocprofv3);
+                             with --only next also the window, multi-token, ragged
+                             and KV-append legs
     --summarize-trace DIR NAME              kernel durations -> profiles/NAME.txt
     --summarize-traffic FDIR WDIR KERNEL NAME
                                             FETCH/WRITE_SIZE -> HBM bytes per launch
@@ -493,7 +495,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["decode", "all"], default="all")
+    ap.add_argument("--only", choices=["decode", "all", "next"], default="all",
+                    help="decode: the headline only; next (with --profile-run): also the "
+                         "window, multi-token, ragged and KV-append legs")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "NAME"))
     ap.add_argument("--summarize-traffic", nargs=4,
@@ -548,6 +552,7 @@ def main():
         log("generating mixed workload")
         extra["mixed"] = bench_mixed(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["mixed"]))
+    if args.only == "all" or args.only == "next":
         log("sliding-window legs (window 128)")
         extra["sliding_window"] = bench_window(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["sliding_window"]))
@@ -560,6 +565,7 @@ def main():
         log("KV append legs")
         extra["kv_append"] = bench_append(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["kv_append"]))
+    if args.only == "all" and not args.profile_run:
         log("generating qwen decode workload (about a minute)")
         qw = wl.qwen_decode(0)
         q_res, _, keep = bench_decode(torch, ga, timer, qw, max(K // 2, 3), max(W // 2, 1),
