@@ -446,6 +446,23 @@ def summarize_trace(outdir: str, name: str, command: str):
                      f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}")
+    hits = glob.glob(os.path.join(outdir, "**", "*kernel_trace.csv"), recursive=True)
+    if hits:
+        # the same kernels split by launch shape, so that each workload's
+        # launches can be told apart; scratch 0 means no register spills
+        shapes = {}
+        for r in _read_csv(hits[0]):
+            key = (_short(r["Kernel_Name"]), r["Grid_Size_X"], r["Grid_Size_Y"],
+                   r["Grid_Size_Z"], r["Workgroup_Size_X"], r["VGPR_Count"],
+                   r["Accum_VGPR_Count"], r["Scratch_Size"], r["LDS_Block_Size"])
+            shapes.setdefault(key, []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines += ["", "by launch shape:",
+                  "kernel | grid (threads) | block | vgpr | agpr | scratch | lds | calls | avg_us | min_us"]
+        for key, ds in sorted(shapes.items(), key=lambda kv: -sum(kv[1])):
+            k, gx, gy, gz, bx, vg, ag, sc, lds = key
+            lines.append(f"{k} | {gx}x{gy}x{gz} | {bx} | {vg} | {ag} | {sc} | {lds} | "
+                         f"{len(ds)} | {sum(ds) / len(ds):.2f} | {min(ds):.2f}")
     _write_profile(name, lines)
 
 
