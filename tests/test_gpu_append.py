@@ -28,6 +28,10 @@ CASES = [
     ("bf16_d128", "bf16", [129, 64, 17], [30, 1, 17], 4, 128),
     ("f32_d64", "f32", [5, 129, 64], [5, 30, 1], 3, 64),
     ("f32_d128_one_each", "f32", [7, 300, 16], [1, 1, 1], 1, 128),
+    # a token's rows over 72 heads exceed one workgroup's pass group
+    ("f32_d128_72_heads", "f32", [40, 3, 17], [40, 1, 17], 72, 128),
+    # long runs of tokens: several tokens a workgroup, a partial last one
+    ("bf16_d64_long_runs", "bf16", [3000, 1200, 9], [2501, 700, 9], 1, 64),
 ]
 
 
