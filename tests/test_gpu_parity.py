@@ -131,6 +131,45 @@ def test_prefill_large_late_logits(d, L, Lq):
     compare(run_decode(dec), oracle_full(dec), "bf16", f"decode large late logits d={d}")
 
 
+def _aligned_scores(b, seed, q_norm, k_norm):
+    """Every query of KV head g is q_norm u_g (+ noise 0.1) and every stored
+    key of it is -k_norm u_g (+ noise 0.5), u_g a random unit vector: all
+    logits near -scale q_norm k_norm, spread by a few units."""
+    gen = torch.Generator().manual_seed(seed)
+    G = b.num_q_heads // b.num_kv_heads
+    u = torch.randn(b.num_kv_heads, b.head_dim, generator=gen)
+    u = u / u.norm(dim=1, keepdim=True)
+    q = (q_norm * u.repeat_interleave(G, dim=0)[None] +
+         0.1 * torch.randn(b.q.shape, generator=gen)).to(b.q.dtype)
+    k = b.k_cache.float().clone()
+    for s_ in range(b.num_seqs):
+        for t in range(int(b.seq_lens[s_])):
+            page = int(b.block_table[s_, t // 16])
+            k[page, :, t % 16, :] = -k_norm * u + 0.5 * torch.randn(u.shape, generator=gen)
+    return replace(b, q=q, k_cache=k.to(b.k_cache.dtype))
+
+
+@pytest.mark.parametrize("d,L,Lq", [(64, 300, 300), (64, 700, 190), (128, 400, 400)])
+def test_prefill_all_logits_far_below_zero(d, L, Lq):
+    """Every logit near -150 (natural units) and no sink: the unshifted
+    weights 2^s would underflow to 0, yet the softmax is a proper average of
+    V.  The kernel must find the rows out of range and recompute them."""
+    b = wl.small_batch(200 + d + L, "bf16", [L], [Lq], 8, 2, d, sink_mode="none")
+    b = _aligned_scores(b, 7 + d, 30.0, 150.0 / (30.0 * b.scale))
+    note(f"prefill logits near -150, no sink, d={d} L={L} Lq={Lq}")
+    compare(run_prefill(b), oracle_full(b), "bf16", f"prefill low logits d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_all_logits_large(d):
+    """All keys scaled by 100 (logits of std ~100 from the first key on):
+    unshifted weights overflow in most rows, which must be recomputed."""
+    b = wl.small_batch(300 + d, "bf16", [500, 129], [500, 64], 8, 2, d)
+    b = _scale_keys(b, 0, 100.0)
+    note(f"prefill all logits large d={d}")
+    compare(run_prefill(b), oracle_full(b), "bf16", f"prefill large logits d={d}")
+
+
 # -------------------------------------------------------- structural checks
 
 def _permuted(b, seed):
