@@ -241,6 +241,17 @@ int check_append(int dtype, int num_seqs, int num_kv_heads, int head_dim, int pa
 
 int elem_bytes(int dtype) { return dtype == ATTN_DTYPE_F32 ? 4 : 2; }
 
+// bf16 decode of one token per sequence: the direct kernel for a short window
+// that cuts some sequence (max_seq_len > window), else split + merge.
+int run_decode_bf16(const attn::DecodeLaunch &p, int max_seq_len)
+{
+    if (p.window > 0 && p.window <= attn::kDirectWindowMax && p.window < max_seq_len)
+        return attn::launch_decode_direct_bf16(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    if (attn::launch_decode_split_bf16(p) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return attn::launch_decode_merge(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -290,9 +301,7 @@ int attn_sinks_decode_window(int dtype, int num_seqs, int num_q_heads, int num_k
                                              out, p.stream);
         return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
     }
-    if (attn::launch_decode_split_bf16(p) != hipSuccess)
-        return ATTN_ERR_HIP;
-    return attn::launch_decode_merge(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    return run_decode_bf16(p, max_seq_len);
 }
 
 int attn_sinks_decode_partials(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,

@@ -56,6 +56,8 @@ struct SplitArgs {
     const int32_t *__restrict__ cu_seqlens_q;  // multi-token decode: [B + 1]; NULL: one token
     int q_max;          // query rows per sequence in the partial results (1 for decode)
     float scale_log2;
+    const float *__restrict__ sinks;  // direct decode: per-head sink logits, or NULL
+    uint16_t *__restrict__ out;       // direct decode: bf16 [B][Hq][D]
 };
 
 constexpr int kUnitTokens = 32;
@@ -346,10 +348,47 @@ __device__ __forceinline__ void compute_block(WaveState<D, NCB> &st, Block<D> &b
     }
 }
 
+// A sequence's whole result for one KV head and one query token: fold the
+// sink into the normalisation (as decode_merge does with a single piece) and
+// write the bf16 output rows.  Lane (n, lg) holds dims (D/16)(4 lg + i) + e
+// of query head g G + n, i.e. D/4 consecutive dims.
+template <int D>
+__device__ __forceinline__ void store_final(const SplitArgs &a, const WaveState<D, 1> &st, int q_row,
+                                            int g, int n, int lg)
+{
+    const float lsum = group4_sum(st.lsum[0]);
+    if (n >= a.group)
+        return;
+    const int h = g * a.group + n;
+    const float m = st.m[0];
+    const float sink2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+    const float M = fmaxf(m, sink2);
+    float scale = 0.f;
+    if (M != kNegInf) {
+        const float f = m == kNegInf ? 0.f : exp2_fast(m - M);
+        const float den = lsum * f + (sink2 == kNegInf ? 0.f : exp2_fast(sink2 - M));
+        scale = den > 0.f ? f / den : 0.f;
+    }
+    uint16_t *dst = a.out + ((size_t)q_row * a.num_q_heads + h) * D + (D / 4) * lg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t w[D / 32];
+#pragma unroll
+        for (int e = 0; e < D / 16; e += 2)
+            w[e / 2] = pack_bf16(st.acc[0][e][i] * scale, st.acc[0][e + 1][i] * scale);
+        if constexpr (D == 64)
+            *(u32x2_t *)(dst + (D / 16) * i) = u32x2_t{w[0], w[1]};
+        else
+            *(u32x4_t *)(dst + (D / 16) * i) = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+}
+
 // One piece: the tokens of [t_begin, t_end) (t_begin a multiple of 32) from
-// t_lo on, of segment (b, g); the result goes to `slot`.  q_first / q_len:
-// the sequence's query rows (q_len new tokens, the last ones of its L keys).
-template <int D, int NCB>
+// t_lo on, of segment (b, g); the result goes to `slot`, or, when kFinal (the
+// piece is the whole sequence, one query token), straight to the output.
+// q_first / q_len: the sequence's query rows (q_len new tokens, the last
+// ones of its L keys).
+template <int D, int NCB, bool kFinal = false>
 __device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int t_begin,
                                           int t_lo, int t_end, int L, int q_first, int q_len,
                                           long long slot, int n, int lg, u32x4_t *klds)
@@ -467,6 +506,11 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int 
         compute_block<D, NCB, true>(st, bt_tail, qop, t0, t_lo, t_end, col_end, a.scale_log2,
                                     lg, klds);
     }
+    if constexpr (kFinal) {
+        static_assert(NCB == 1, "one query token");
+        store_final<D>(a, st, q_first, g, n, lg);
+        return;
+    }
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         const float lsum = group4_sum(st.lsum[cb]);
@@ -540,6 +584,24 @@ __global__ __launch_bounds__(512) void decode_split_bf16(SplitArgs a)
             } while (load_scalar(a.seq_lens, b) == 0);
         }
     }
+}
+
+// Direct decode, for sliding windows short enough that one wave per
+// (sequence, KV head) covers a sequence's visible keys quickly: no split, no
+// partial results, no merge launch.  The wave runs the same block loop as a
+// split piece over the blocks from the one holding the oldest visible key to
+// the last, then folds the sink and writes the output.
+template <int D>
+__global__ __launch_bounds__(64) void decode_direct_bf16(SplitArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, lg = lane >> 4;
+    const int b = blockIdx.x, g = blockIdx.y;
+    extern __shared__ u32x4_t s_k[];
+    const int L = load_scalar(a.seq_lens, b);
+    const int t_lo = oldest_key(L, a.window);
+    run_piece<D, 1, true>(a, b, g, first_unit(L, a.window) * kUnitTokens, t_lo, L, L, b, 1, 0, n,
+                          lg, s_k);
 }
 
 struct MergeArgs {
@@ -750,6 +812,36 @@ hipError_t launch_decode_split_bf16(const DecodeLaunch &p)
     if (p.num_seqs == 0 || p.num_wgs == 0)
         return hipSuccess;
     return p.head_dim == 64 ? launch_split_rows<64>(p) : launch_split_rows<128>(p);
+}
+
+hipError_t launch_decode_direct_bf16(const DecodeLaunch &p)
+{
+    if (p.num_seqs == 0)
+        return hipSuccess;
+    SplitArgs a = {};
+    a.q = (const uint16_t *)p.q;
+    a.k_cache = (const uint16_t *)p.k_cache;
+    a.v_cache = (const uint16_t *)p.v_cache;
+    a.block_table = p.block_table;
+    a.seq_lens = p.seq_lens;
+    a.num_seqs = p.num_seqs;
+    a.num_q_heads = p.num_q_heads;
+    a.num_kv_heads = p.num_kv_heads;
+    a.group = p.num_q_heads / p.num_kv_heads;
+    a.max_pages = p.max_pages_per_seq;
+    a.window = p.window;
+    a.q_max = 1;
+    a.scale_log2 = p.scale * kLog2e;
+    a.sinks = p.sinks;
+    a.out = (uint16_t *)p.out;
+    const dim3 grid(p.num_seqs, p.num_kv_heads);
+    if (p.head_dim == 64)
+        hipLaunchKernelGGL(decode_direct_bf16<64>, grid, dim3(64), 2 * 16 * (64 / 8) * 16,
+                           p.stream, a);
+    else
+        hipLaunchKernelGGL(decode_direct_bf16<128>, grid, dim3(64), 2 * 16 * (128 / 8) * 16,
+                           p.stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_merge(const DecodeLaunch &p)

@@ -63,6 +63,11 @@ hipError_t launch_decode_split_bf16(const DecodeLaunch &p);
 // Merge pass: combine the splits of each (sequence, head), fold the sink,
 // write out in p.dtype.
 hipError_t launch_decode_merge(const DecodeLaunch &p);
+// Direct decode (bf16, one query token, 0 < window <= kDirectWindowMax and
+// window < the length bound): one wave per (sequence, KV head) over the
+// visible keys, sink folded, output written; no workspace, no merge.
+constexpr int kDirectWindowMax = 512;
+hipError_t launch_decode_direct_bf16(const DecodeLaunch &p);
 hipError_t launch_prefill_bf16(const PrefillLaunch &p);
 // KV append: new rows [total_new][Hkv][d] into their page slots (f32 or bf16,
 // elem_bytes 4 or 2); cu_seqlens_new NULL means one new token per sequence.
