@@ -212,8 +212,10 @@ int attn_sinks_prefill(int dtype, int num_seqs, int num_q_heads, int num_kv_head
  * (size from attn_sinks_decode_workspace_bytes, which covers every window),
  * ownership, checks and errors are as for the unwindowed calls.
  *
- * Decode reads only the blocks of each sequence that hold its last W keys.
- * Prefill with 0 < W < max_seq_len runs a kernel of its own in which each
+ * Decode reads only the blocks of each sequence that hold its last W keys;
+ * bf16 with 0 < W <= 512 and W < max_seq_len runs one wave per (sequence,
+ * KV head) over them and writes the output directly (the workspace is then
+ * not touched).  Prefill with 0 < W < max_seq_len runs a kernel of its own in which each
  * wave streams the few blocks its rows need straight from the paged cache.
  */
 int attn_sinks_decode_window(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
