@@ -600,6 +600,41 @@ __device__ __forceinline__ void exact_block(WaveState<D> &w, const uint16_t *kt,
     __builtin_amdgcn_wave_barrier();
 }
 
+// One block of the windowed prefill: the online softmax of exact_block with
+// a lazy maximum (raised only when a block's maximum exceeds it by more than
+// kRescaleSlack, so weights stay below 2^kRescaleSlack), which spares the
+// rescale of the accumulators on almost every block.
+template <int D>
+__device__ __forceinline__ void window_block(WaveState<D> &w, const uint16_t *kt,
+                                             const uint16_t *vt, int thr, int window,
+                                             float scale_log2, int lane)
+{
+    u32x4_t kop[D / 16], vop[D / 32][2];
+    read_k<D>(kop, kt, 0, lane);
+    read_v<D>(vop, vt, 0, lane);
+#pragma unroll
+    for (int rb = 0; rb < Cfg<D>::kNRB; ++rb) {
+        f32x16_t s = qk_mfma<D>(w.qop[rb], kop);
+        apply_band(s, thr + 32 * rb, window);
+        const float bm = block_max(s, scale_log2);
+        const float m_new = bm > w.m[rb] + kRescaleSlack ? bm : w.m[rb];
+        if (__any(m_new != w.m[rb])) {
+            // 0 on a row's first visible block (its state is empty)
+            const float alpha = m_new == w.m[rb] ? 1.f : exp2_fast(w.m[rb] - m_new);
+            w.lsum[rb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                w.acc[rb][db] *= alpha;
+            w.m[rb] = m_new;
+        }
+        const float m_ref = w.m[rb] == kNegInf ? 0.f : w.m[rb];
+        w.lsum[rb] = block_weights(s, m_ref, w.pop[rb], scale_log2, w.lsum[rb]);
+        pv_mfma<D>(w.acc[rb], vop, w.pop[rb]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block's writes
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Exact recompute of a wave's rows (rare: some row sum came too close to
 // overflow against the reference taken from the first block).  K and V come
 // straight from the paged cache into this wave's own part of the LDS (the
@@ -924,9 +959,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
 // few for the windows the notes name (W = 128: at most 7 per wave at d = 64).
 // Each wave streams its own blocks from the paged cache into its own LDS
 // tiles, the next block in registers while the current one is computed, and
-// runs the plain online softmax on each (a row's first blocks may hold none
-// of its keys, so no reference is fixed in advance).  The four waves of a
-// workgroup never wait for one another.
+// runs the online softmax on each with a lazy maximum (window_block: a row's
+// first blocks may hold none of its keys, so no reference is fixed in
+// advance).  The four waves of a workgroup never wait for one another.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void prefill_window_bf16(PrefillArgs a)
 {
@@ -973,7 +1008,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_window_bf16(PrefillArgs a
         stash_block<D>(raw, kt, vt, lane);
         if (kAhead && blk + 1 < nb)
             fetch_block<D>(raw, a, bt, L, head_off, k0 + kKB, lane);
-        exact_block<D, true>(w, kt, vt, true, thr - k0, a.window, a.scale_log2, lane);
+        window_block<D>(w, kt, vt, thr - k0, a.window, a.scale_log2, lane);
     }
     // the staging area of the epilogue is the wave's own K tile and more:
     // 32 NRB rows of d bf16 fit in its 2 * 32 * d elements
