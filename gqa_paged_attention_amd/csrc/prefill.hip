@@ -523,25 +523,33 @@ struct RawBlock {
     u32x4_t k[kPer], v[kPer];
 };
 
+// k0 is a multiple of 32, so a block spans two pages, whose ids the wave
+// reads once (scalar loads); chunk i lies on the first when i < kPer / 2.
 template <int D, bool kContig = false>
 __device__ __forceinline__ void fetch_block(RawBlock<D> &rb, const PrefillArgs &a,
                                             const int32_t *__restrict__ bt, int L,
                                             size_t kv_off, int k0, int lane)
 {
     constexpr int kChunks = D / 8;
+    constexpr int kPer = RawBlock<D>::kPer;
+    static_assert(kPer % 2 == 0, "half of the chunks on each page");
+    size_t slab[2] = {0, 0};  // element offsets of the two pages' head slabs
+    if constexpr (!kContig) {
 #pragma unroll
-    for (int i = 0; i < RawBlock<D>::kPer; ++i) {
+        for (int s = 0; s < 2; ++s)
+            slab[s] = (size_t)load_scalar(bt, min(k0 + 16 * s, L - 1) >> 4) * a.num_kv_heads *
+                          16 * D + kv_off;
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
         const int c = lane + 64 * i;
         const int key = c / kChunks, chunk = c % kChunks;
         const int tok = min(k0 + key, L - 1);
         size_t off;
-        if constexpr (kContig) {
+        if constexpr (kContig)
             off = kv_off + (size_t)tok * a.kv_stride + 8 * chunk;
-        } else {
-            const int page = bt[tok >> 4];
-            off = (size_t)page * a.num_kv_heads * 16 * D + kv_off + (size_t)(tok & 15) * D +
-                  8 * chunk;
-        }
+        else
+            off = slab[i < kPer / 2 ? 0 : 1] + (size_t)(tok & 15) * D + 8 * chunk;
         rb.k[i] = *(const u32x4_t *)(a.k_cache + off);
         rb.v[i] = *(const u32x4_t *)(a.v_cache + off);
     }
@@ -603,11 +611,13 @@ __device__ __forceinline__ void exact_block(WaveState<D> &w, const uint16_t *kt,
 // One block of the windowed prefill: the online softmax of exact_block with
 // a lazy maximum (raised only when a block's maximum exceeds it by more than
 // kRescaleSlack, so weights stay below 2^kRescaleSlack), which spares the
-// rescale of the accumulators on almost every block.
+// rescale of the accumulators on almost every block.  The block holds keys
+// k0 .. k0+31; the wave's rows sit at positions wpf + 32 rb + (0 .. 31), and
+// a row block to which every key is visible skips the band mask.
 template <int D>
 __device__ __forceinline__ void window_block(WaveState<D> &w, const uint16_t *kt,
-                                             const uint16_t *vt, int thr, int window,
-                                             float scale_log2, int lane)
+                                             const uint16_t *vt, int thr, int window, int k0,
+                                             int wpf, float scale_log2, int lane)
 {
     u32x4_t kop[D / 16], vop[D / 32][2];
     read_k<D>(kop, kt, 0, lane);
@@ -615,7 +625,9 @@ __device__ __forceinline__ void window_block(WaveState<D> &w, const uint16_t *kt
 #pragma unroll
     for (int rb = 0; rb < Cfg<D>::kNRB; ++rb) {
         f32x16_t s = qk_mfma<D>(w.qop[rb], kop);
-        apply_band(s, thr + 32 * rb, window);
+        const int p_first = wpf + 32 * rb;
+        if (!(k0 + kKB - 1 <= p_first && k0 >= p_first + 31 - window + 1))
+            apply_band(s, thr + 32 * rb, window);
         const float bm = block_max(s, scale_log2);
         const float m_new = bm > w.m[rb] + kRescaleSlack ? bm : w.m[rb];
         if (__any(m_new != w.m[rb])) {
@@ -1008,7 +1020,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_window_bf16(PrefillArgs a
         stash_block<D>(raw, kt, vt, lane);
         if (kAhead && blk + 1 < nb)
             fetch_block<D>(raw, a, bt, L, head_off, k0 + kKB, lane);
-        window_block<D>(w, kt, vt, thr - k0, a.window, a.scale_log2, lane);
+        window_block<D>(w, kt, vt, thr - k0, a.window, k0, wpf, a.scale_log2, lane);
     }
     // the staging area of the epilogue is the wave's own K tile and more:
     // 32 NRB rows of d bf16 fit in its 2 * 32 * d elements
