@@ -372,7 +372,7 @@ def bench_mixed(torch, ga, timer, steps, warmup, wl):
 
 # ------------------------------------------------------------ cpu baseline
 
-def cpu_baseline(batch_cpu, gpu_out, sample_seqs):
+def cpu_baseline(batch_cpu, gpu_out, sample_seqs, min_seconds=10.0):
     """The fp64 oracle on the first `sample_seqs` sequences of the decode
     workload, timed on this host's cores; the GPU output is checked on the
     same rows (the correctness gate before the timings are reported)."""
@@ -381,19 +381,36 @@ def cpu_baseline(batch_cpu, gpu_out, sample_seqs):
     sub = batch_cpu.rows(0, sample_seqs)
     threads = oracle.default_threads()
     oracle.attention(sub.rows(0, 1), threads=threads)  # load + warm
-    t0 = time.perf_counter()
-    ref = oracle.attention(sub, threads=threads)
-    dt = time.perf_counter() - t0
+    # the whole sample, repeated until at least min_seconds of host work
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        ref = oracle.attention(sub, threads=threads)
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
     got = gpu_out[:sample_seqs].double().cpu().numpy()
     err = np.abs(got - ref)
     ok = bool(np.all(np.isfinite(got)) and np.all(err <= 1e-2 + 2e-2 * np.abs(ref)))
     nbytes = decode_bytes(sub)
-    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+    return {"value": round(nbytes * runs / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"first {sample_seqs} of 64 sequences of the gpt-oss decode workload "
-                      f"({nbytes / 1e6:.1f} MB of K/V), all 64 heads, fp64, {dt:.2f} s",
+                      f"({nbytes / 1e6:.1f} MB of K/V), all 64 heads, fp64, {runs} runs in "
+                      f"{dt:.1f} s",
+            "cpu_model": cpu_model(),
             "seconds": round(dt, 3),
             "gpu_matches_oracle": ok, "gpu_max_abs_err": float(err.max())}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def read_traffic():
