@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of paged GQA attention with per-head sinks on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode|all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode|all|next]
 
 One step is one decode pass (split pass + merge pass) of the gpt-oss-20b-shaped
 decode workload: 64 sequences x 1 query token, 64 q / 8 KV heads, head_dim 64,
@@ -9,14 +9,16 @@ context lengths uniform in [1024, 8192], 16-token HND pages, bf16, seeded
 synthetic data.  Inputs are resident in HBM before timing starts.  L2 and the
 Infinity Cache are flushed (a 1 GiB write) before every step, outside the
 timed events.  The headline value is decode KV-read GB/s; the same line also
-carries the causal prefill (TFLOP/s), the Qwen3-235B-shaped decode and the
-mixed batch, each against its own roofline, plus the fp64 CPU oracle timed on
-the host cores (a baseline, not a target).
+carries the causal prefill (TFLOP/s), the Qwen3-235B-shaped decode, the
+mixed batch and the sliding-window, multi-token, ragged, KV-append and
+RoPE-append legs, each against its own roofline, plus the fp64 CPU oracle
+timed on the host cores (a baseline, not a target).  The RoPE-append leg
+rotates the same q in place every step: its values drift, its work does not.
 
 Modes used to make the committed profiles:
-    --profile-run            decode + prefill only, no oracle (run under rocprofv3);
-                             with --only next also the window, multi-token, ragged
-                             and KV-append legs
+    --profile-run            every leg but the mixed batch and the Qwen decode,
+                             no oracle (run under rocprofv3); with --only next
+                             the same
     --summarize-trace DIR NAME              kernel durations -> profiles/NAME.txt
     --summarize-traffic FDIR WDIR KERNEL NAME
                                             FETCH/WRITE_SIZE -> HBM bytes per launch
@@ -295,6 +297,36 @@ def bench_append(torch, ga, timer, steps, warmup, wl):
     }
 
 
+def bench_rope(torch, ga, timer, steps, warmup, wl):
+    """RoPE with YaRN scaling fused into the KV append ("GPT OSS" notes,
+    sections 3 and 4.1) on the gpt-oss prefill chunk (32768 tokens, 64 q / 8
+    KV heads, d 64, base 10000, scale 32, cache positions): q read and
+    written in place, K and V read and written into their pages, against
+    the HBM roofline."""
+    pre = wl.gptoss_prefill(0)
+    before, k_new, v_new = wl.split_new_tokens(pre)
+    g = before.to("cuda")
+    q = pre.q.cuda()
+    kn, vn = k_new.cuda(), v_new.cuda()
+    cu = pre.cu_seqlens_q.tolist()
+    pos = []
+    for b in range(pre.num_seqs):
+        n = cu[b + 1] - cu[b]
+        pos += [int(pre.seq_lens[b]) - n + i for i in range(n)]
+    pos = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    r = timer.run([("rope_append", lambda: ga.attn_sinks_rope_append(
+        q, kn, vn, pos, g.k_cache, g.v_cache, g.block_table, g.seq_lens, g.cu_seqlens_q,
+        before.max_seq_len, 10000.0, 32.0))], steps, warmup, flush=True)
+    nb = 2 * q.numel() * q.element_size() + 2 * 2 * kn.numel() * kn.element_size() + \
+        pos.numel() * 4 + 4 * (g.num_seqs * 2 + 1)
+    gbs = nb / (r["step_ms"] * 1e-3) / 1e9
+    return {"workload": "gpt-oss prefill chunk: 32768 tokens, q 64 heads rotated in place, "
+                        "K rotated and V appended into 8 KV heads' pages, d 64, bf16, YaRN "
+                        "scale 32",
+            "bytes": nb, "ms": round(r["step_ms"], 4), "GB_per_s": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def bench_multi(torch, ga, timer, steps, warmup, wl, q_len=4):
     """Multi-token decode: the gpt-oss decode shape (64 seqs, L ~ U[1024,
     8192], 64/8 heads, d 64) with `q_len` new tokens per sequence, through
@@ -531,7 +563,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["decode", "all", "next"], default="all",
                     help="decode: the headline only; next (with --profile-run): also the "
-                         "window, multi-token, ragged and KV-append legs")
+                         "window, multi-token, ragged, KV-append and RoPE-append legs")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "NAME"))
     ap.add_argument("--summarize-traffic", nargs=4,
@@ -599,6 +631,9 @@ def main():
         log("KV append legs")
         extra["kv_append"] = bench_append(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["kv_append"]))
+        log("RoPE + KV append leg")
+        extra["rope_append"] = bench_rope(torch, ga, timer, K, W, wl)
+        log(json.dumps(extra["rope_append"]))
     if args.only == "all" and not args.profile_run:
         log("generating qwen decode workload (about a minute)")
         qw = wl.qwen_decode(0)

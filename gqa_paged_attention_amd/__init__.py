@@ -61,6 +61,8 @@ def library():
     lib.attn_sinks_prefill_window.restype = I
     lib.attn_sinks_append_kv.argtypes = [I] * 9 + [P] * 7 + [P]
     lib.attn_sinks_append_kv.restype = I
+    lib.attn_sinks_rope_append.argtypes = [I] * 10 + [P] * 4 + [F, F, I, F, F] + [P] * 6
+    lib.attn_sinks_rope_append.restype = I
     lib.attn_sinks_decode_append.argtypes = [I] * 9 + [P] * 8 + [F, I, P, P, Z, P]
     lib.attn_sinks_decode_append.restype = I
     lib.attn_sinks_prefill_append.argtypes = [I] * 11 + [P] * 9 + [F, I, P, P]
@@ -293,6 +295,40 @@ def attn_sinks_append_kv(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torc
         dt, B, Hkv, d, P, num_pages, block_table.shape[1], int(max_seq_len), T, _ptr(k_new),
         _ptr(v_new), _ptr(block_table), _ptr(seq_lens), _ptr(cu_seqlens_new), _ptr(k_cache),
         _ptr(v_cache), _stream_handle(stream))
+    _raise(status)
+
+
+def attn_sinks_rope_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                           positions: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_table: torch.Tensor, seq_lens: torch.Tensor,
+                           cu_seqlens_new: Optional[torch.Tensor], max_seq_len: int,
+                           rope_base: float, rope_scale: float, orig_ctx: int = 4096,
+                           beta_fast: float = 32.0, beta_slow: float = 1.0, stream=None) -> None:
+    """Enqueue attn_sinks_rope_append: rotate q [total_new][Hq][d] in place and
+    the new K rows into their cache slots (NeoX RoPE, YaRN scaling, rotary
+    positions int32 [total_new]), append V; placement as attn_sinks_append_kv."""
+    dt = _DTYPE_CODE.get(k_cache.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {k_cache.dtype}")
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        _check_dense(name, t, k_cache.dtype)
+    for name, t in (("positions", positions), ("block_table", block_table),
+                    ("seq_lens", seq_lens), ("cu_seqlens_new", cu_seqlens_new)):
+        _check_dense(name, t, torch.int32)
+    num_pages, Hkv, P, d = k_cache.shape
+    T = k_new.shape[0]
+    Hq = q.shape[1]
+    B = seq_lens.numel()
+    if tuple(k_new.shape) != (T, Hkv, d) or tuple(v_new.shape) != (T, Hkv, d) or \
+            tuple(q.shape) != (T, Hq, d) or positions.numel() != T or \
+            tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q / k_new / v_new / positions / cache shapes disagree")
+    status = library().attn_sinks_rope_append(
+        dt, B, Hq, Hkv, d, P, num_pages, block_table.shape[1], int(max_seq_len), T, _ptr(q),
+        _ptr(k_new), _ptr(v_new), _ptr(positions), float(rope_base), float(rope_scale),
+        int(orig_ctx), float(beta_fast), float(beta_slow), _ptr(block_table), _ptr(seq_lens),
+        _ptr(cu_seqlens_new), _ptr(k_cache), _ptr(v_cache), _stream_handle(stream))
     _raise(status)
 
 

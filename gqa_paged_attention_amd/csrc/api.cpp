@@ -436,6 +436,63 @@ int attn_sinks_append_kv(int dtype, int num_seqs, int num_kv_heads, int head_dim
                : ATTN_ERR_HIP;
 }
 
+int attn_sinks_rope_append(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                           int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                           int max_seq_len, int total_new, void *q, const void *k_new,
+                           const void *v_new, const int32_t *positions, float rope_base,
+                           float rope_scale, int orig_ctx, float beta_fast, float beta_slow,
+                           const int32_t *block_table, const int32_t *seq_lens,
+                           const int32_t *cu_seqlens_new, void *k_cache, void *v_cache,
+                           void *stream)
+{
+    int rc = check_append(dtype, num_seqs, num_kv_heads, head_dim, page_size, num_pages,
+                          max_pages_per_seq, max_seq_len, total_new, k_new, v_new, block_table,
+                          seq_lens, cu_seqlens_new, k_cache, v_cache);
+    if (rc != ATTN_OK)
+        return rc;
+    rc = check_common(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                      max_pages_per_seq, max_seq_len);
+    if (rc != ATTN_OK)
+        return rc;
+    if (!(std::isfinite(rope_base) && rope_base > 0.f && std::isfinite(rope_scale) &&
+          rope_scale > 0.f && orig_ctx > 0))
+        return ATTN_ERR_SHAPE;
+    if (rope_scale != 1.f && !(std::isfinite(beta_fast) && std::isfinite(beta_slow) &&
+                               beta_fast > beta_slow))
+        return ATTN_ERR_SHAPE;
+    if (num_seqs == 0 || total_new == 0)
+        return ATTN_OK;
+    if (!q || !positions)
+        return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned4(positions))
+        return ATTN_ERR_ALIGN;
+    // YaRN frequencies: pair i turns at base^(-2i/d); pairs that turn fewer
+    // than beta_slow times in the original context are interpolated by the
+    // scale, pairs that turn more than beta_fast times are kept, linearly
+    // blended in between; q and k are multiplied by 0.1 ln(scale) + 1.
+    double freq[64];
+    const double s = rope_scale;
+    for (int i = 0; i < head_dim / 2; ++i) {
+        const double theta = std::pow((double)rope_base, -2.0 * i / head_dim);
+        if (s == 1.0) {
+            freq[i] = theta;
+            continue;
+        }
+        const double turns = orig_ctx * theta / (2.0 * M_PI);
+        double ramp = (turns - beta_slow) / ((double)beta_fast - beta_slow);
+        ramp = ramp < 0.0 ? 0.0 : (ramp > 1.0 ? 1.0 : ramp);
+        freq[i] = (1.0 - ramp) * theta / s + ramp * theta;
+    }
+    const float mscale = s > 1.0 ? (float)(0.1 * std::log(s) + 1.0) : 1.f;
+    return attn::launch_rope_append(elem_bytes(dtype), num_seqs, num_q_heads, num_kv_heads,
+                                    head_dim, max_pages_per_seq, total_new, q, k_new, v_new,
+                                    positions, freq, mscale, block_table, seq_lens,
+                                    cu_seqlens_new, k_cache, v_cache,
+                                    reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? ATTN_OK
+               : ATTN_ERR_HIP;
+}
+
 int attn_sinks_decode_append(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
                              int head_dim, int page_size, int num_pages, int max_pages_per_seq,
                              int max_seq_len, const void *q, const void *k_new,

@@ -76,6 +76,14 @@ hipError_t launch_append_kv(int elem_bytes, int num_seqs, int num_kv_heads, int 
                             const void *v_new, const int32_t *block_table,
                             const int32_t *seq_lens, const int32_t *cu_seqlens_new,
                             void *k_cache, void *v_cache, hipStream_t stream);
+// Rotary embedding (per-pair frequencies freq[head_dim / 2], factor mscale)
+// of q in place and of the new K rows into their cache slots, V appended.
+hipError_t launch_rope_append(int elem_bytes, int num_seqs, int num_q_heads, int num_kv_heads,
+                              int head_dim, int max_pages_per_seq, int total_new, void *q,
+                              const void *k_new, const void *v_new, const int32_t *positions,
+                              const double *freq, float mscale, const int32_t *block_table,
+                              const int32_t *seq_lens, const int32_t *cu_seqlens_new,
+                              void *k_cache, void *v_cache, hipStream_t stream);
 // fp32 path (full rows, no split), used for both decode and prefill.
 hipError_t launch_rows_f32(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                            int max_pages_per_seq, int total_q, const void *q,

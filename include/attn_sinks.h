@@ -263,6 +263,50 @@ int attn_sinks_append_kv(int dtype, int num_seqs, int num_kv_heads, int head_dim
                          void *v_cache, void *stream);
 
 /*
+ * Rotary embedding fused into the KV append.  Each layer rotates Q and K
+ * with NeoX-style RoPE under YaRN scaling before K is appended ("GPT OSS"
+ * model notes, section 3, forward graph: origCtxLen 4096, freqScale =
+ * 1 / RopeScale, beta_fast 32, beta_slow 1; section 4.1; section 11: the
+ * positions come as an explicit array).  The notes give those parameters,
+ * not the formula; the formula is YaRN's ("NTK-by-parts" interpolation with
+ * attention scaling):
+ *
+ *   theta_i = rope_base^(-2 i / head_dim)              i = 0 .. head_dim/2 - 1
+ *   r_i     = orig_ctx * theta_i / (2 pi)              turns within orig_ctx
+ *   gamma_i = clamp((r_i - beta_slow) / (beta_fast - beta_slow), 0, 1)
+ *   f_i     = (1 - gamma_i) theta_i / rope_scale + gamma_i theta_i
+ *   c       = 0.1 ln(rope_scale) + 1  (1 when rope_scale <= 1)
+ *
+ * and a row x at position p becomes, for every pair (i, i + head_dim/2):
+ *
+ *   y_i            = c (x_i cos(p f_i) - x_{i+d/2} sin(p f_i))
+ *   y_{i+head_dim/2} = c (x_i sin(p f_i) + x_{i+d/2} cos(p f_i))
+ *
+ * rope_scale = 1 is plain RoPE.  The call rotates every query head of the
+ * new tokens in q, in place, writes the rotated new K rows to their cache
+ * slots and appends V unchanged, all as attn_sinks_append_kv places them.
+ * Arithmetic is fp32 with the angle p f_i formed and reduced in fp64;
+ * results are rounded to dtype (RNE).
+ *
+ *   q              [total_new][num_q_heads][head_dim] dtype, read and written
+ *   positions      [total_new] int32 rotary position of each new token
+ *                  (usually its cache position; any value is accepted)
+ *   rope_base      > 0; rope_scale > 0; orig_ctx > 0; when rope_scale != 1,
+ *                  beta_fast > beta_slow (all finite), else ATTN_ERR_SHAPE
+ *   the rest       as for attn_sinks_append_kv (num_q_heads as for decode)
+ * The new K rows in k_new are read only.  Device preconditions as for
+ * attn_sinks_append_kv.
+ */
+int attn_sinks_rope_append(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                           int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                           int max_seq_len, int total_new, void *q, const void *k_new,
+                           const void *v_new, const int32_t *positions, float rope_base,
+                           float rope_scale, int orig_ctx, float beta_fast, float beta_slow,
+                           const int32_t *block_table, const int32_t *seq_lens,
+                           const int32_t *cu_seqlens_new, void *k_cache, void *v_cache,
+                           void *stream);
+
+/*
  * One layer's attention step as the forward graph of the model notes
  * (section 3) orders it: append the new tokens' K and V, then attend with
  * the sink, with an optional sliding window (0: none).  These are the

@@ -227,6 +227,48 @@ def test_append_rejects(lib, kw, code):
     assert _append(lib, **kw) == code
 
 
+def _rope(lib, **kw):
+    args = dict(dtype=1, B=2, Hq=8, Hkv=2, d=64, P=16, pages=8, max_pages=4, max_len=64, T=5,
+                q=FAKE, k_new=FAKE, v_new=FAKE, pos=FAKE, base=10000.0, scale=32.0, orig=4096,
+                bf=32.0, bs=1.0, bt=FAKE, sl=FAKE, cu=FAKE, kc=FAKE, vc=FAKE)
+    args.update(kw)
+    F = ctypes.c_float
+    return lib.attn_sinks_rope_append(
+        args["dtype"], args["B"], args["Hq"], args["Hkv"], args["d"], args["P"], args["pages"],
+        args["max_pages"], args["max_len"], args["T"], args["q"], args["k_new"], args["v_new"],
+        args["pos"], F(args["base"]), F(args["scale"]), args["orig"], F(args["bf"]),
+        F(args["bs"]), args["bt"], args["sl"], args["cu"], args["kc"], args["vc"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), ERR_UNSUPPORTED),
+    (dict(d=80), ERR_UNSUPPORTED),
+    (dict(Hq=7), ERR_SHAPE),                  # Hq not a multiple of Hkv
+    (dict(Hq=64), ERR_UNSUPPORTED),           # group of 32
+    (dict(T=-1), ERR_SHAPE),
+    (dict(base=0.0), ERR_SHAPE),
+    (dict(base=float("inf")), ERR_SHAPE),
+    (dict(scale=0.0), ERR_SHAPE),
+    (dict(scale=float("nan")), ERR_SHAPE),
+    (dict(orig=0), ERR_SHAPE),
+    (dict(bf=1.0, bs=1.0), ERR_SHAPE),        # empty ramp with scale != 1
+    (dict(bf=float("nan")), ERR_SHAPE),
+    (dict(q=None), ERR_NULL),
+    (dict(pos=None), ERR_NULL),
+    (dict(k_new=None), ERR_NULL),
+    (dict(q=FAKE + 8), ERR_ALIGN),
+    (dict(pos=FAKE + 2), ERR_ALIGN),
+])
+def test_rope_append_rejects(lib, kw, code):
+    assert _rope(lib, **kw) == code
+
+
+def test_rope_append_scale_one_needs_no_ramp(lib):
+    # plain RoPE: the ramp bounds are not used, and nothing is launched for T = 0
+    assert _rope(lib, scale=1.0, bf=1.0, bs=1.0, T=0) == OK
+    assert _rope(lib, T=0) == OK
+
+
 def test_append_empty_enqueues_nothing(lib):
     assert _append(lib, T=0) == OK
     assert _append(lib, B=0, T=0) == OK
