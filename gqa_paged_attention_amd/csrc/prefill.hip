@@ -612,8 +612,9 @@ __device__ __forceinline__ void exact_block(WaveState<D> &w, const uint16_t *kt,
 // a lazy maximum (raised only when a block's maximum exceeds it by more than
 // kRescaleSlack, so weights stay below 2^kRescaleSlack), which spares the
 // rescale of the accumulators on almost every block.  The block holds keys
-// k0 .. k0+31; the wave's rows sit at positions wpf + 32 rb + (0 .. 31), and
-// a row block to which every key is visible skips the band mask.
+// k0 .. k0+31; the wave's rows sit at positions wpf + 32 rb + (0 .. 31); a
+// row block that sees none of the keys skips the block, and one that sees
+// all of them skips the band mask.
 template <int D>
 __device__ __forceinline__ void window_block(WaveState<D> &w, const uint16_t *kt,
                                              const uint16_t *vt, int thr, int window, int k0,
@@ -624,8 +625,11 @@ __device__ __forceinline__ void window_block(WaveState<D> &w, const uint16_t *kt
     read_v<D>(vop, vt, 0, lane);
 #pragma unroll
     for (int rb = 0; rb < Cfg<D>::kNRB; ++rb) {
-        f32x16_t s = qk_mfma<D>(w.qop[rb], kop);
         const int p_first = wpf + 32 * rb;
+        // no key of the block in any row's window: nothing to do
+        if (k0 > p_first + 31 || k0 + kKB - 1 < p_first - window + 1)
+            continue;
+        f32x16_t s = qk_mfma<D>(w.qop[rb], kop);
         if (!(k0 + kKB - 1 <= p_first && k0 >= p_first + 31 - window + 1))
             apply_band(s, thr + 32 * rb, window);
         const float bm = block_max(s, scale_log2);
