@@ -93,7 +93,7 @@ bool multi_packed(int group, int head_dim, int max_q_len)
 {
     const int rows = group * max_q_len;
     return group > 0 && max_q_len >= 1 &&
-           rows <= (head_dim == 64 ? attn::kMultiRowsD64 : attn::kMultiRowsD128);
+           rows <= attn::kMultiRowsMax;
 }
 
 int check_common(int dtype, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

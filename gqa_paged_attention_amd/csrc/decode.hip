@@ -387,9 +387,9 @@ __device__ __forceinline__ void store_final(const SplitArgs &a, const WaveState<
 // t_lo on, of segment (b, g); the result goes to `slot`, or, when kFinal (the
 // piece is the whole sequence, one query token), straight to the output.
 // q_first / q_len: the sequence's query rows (q_len new tokens, the last
-// ones of its L keys).
+// ones of its L keys); the wave takes the packed rows row0 .. row0 + 16 NCB - 1.
 template <int D, int NCB, bool kFinal = false>
-__device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int t_begin,
+__device__ __forceinline__ void run_piece(const SplitArgs &a, int row0, int b, int g, int t_begin,
                                           int t_lo, int t_end, int L, int q_first, int q_len,
                                           long long slot, int n, int lg, u32x4_t *klds)
 {
@@ -409,7 +409,7 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int 
     int col_end[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-        const int row = 16 * cb + n, tok = row / a.group;
+        const int row = row0 + 16 * cb + n, tok = row / a.group;
         col_end[cb] = L - q_len + tok + 1;
         if (tok < q_len) {
             const uint16_t *qrow =
@@ -514,7 +514,7 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int b, int g, int 
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         const float lsum = group4_sum(st.lsum[cb]);
-        const int row = 16 * cb + n, tok = row / a.group;
+        const int row = row0 + 16 * cb + n, tok = row / a.group;
         if (tok < q_len) {
             // partial-result row: (slot, query token, query head)
             const size_t prow = ((size_t)slot * a.q_max + tok) * a.num_q_heads +
@@ -543,6 +543,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16(SplitArgs a)
     if (g >= a.num_kv_heads)
         return;  // the last head group may be partial (waves are independent)
     const int w = blockIdx.x;
+    const int row0 = 16 * NCB * blockIdx.z;  // this layer's packed rows
     // per-wave K staging buffer: one 32-token block of K (dynamic LDS,
     // heads_per_wg * 64 * D bytes)
     extern __shared__ u32x4_t s_k[];
@@ -573,7 +574,7 @@ __global__ __launch_bounds__(512) void decode_split_bf16(SplitArgs a)
             q_first = load_scalar(a.cu_seqlens_q, b);
             q_len = load_scalar(a.cu_seqlens_q, b + 1) - q_first;
         }
-        run_piece<D, NCB>(a, b, g, t_begin, oldest_key(L, a.window), t_end, L, q_first, q_len,
+        run_piece<D, NCB>(a, row0, b, g, t_begin, oldest_key(L, a.window), t_end, L, q_first, q_len,
                           (long long)b + w, n, lg, klds);
         u = piece_end;
         if (u < u_stop) {
@@ -600,7 +601,7 @@ __global__ __launch_bounds__(64) void decode_direct_bf16(SplitArgs a)
     extern __shared__ u32x4_t s_k[];
     const int L = load_scalar(a.seq_lens, b);
     const int t_lo = oldest_key(L, a.window);
-    run_piece<D, 1, true>(a, b, g, first_unit(L, a.window) * kUnitTokens, t_lo, L, L, b, 1, 0, n,
+    run_piece<D, 1, true>(a, 0, b, g, first_unit(L, a.window) * kUnitTokens, t_lo, L, L, b, 1, 0, n,
                           lg, s_k);
 }
 
@@ -757,27 +758,29 @@ hipError_t launch_split_d(const DecodeLaunch &p)
     a.cu_seqlens_q = p.cu_seqlens_q;
     a.q_max = p.q_max;
     a.scale_log2 = p.scale * kLog2e;
-    const dim3 grid(p.num_wgs, (p.num_kv_heads + p.heads_per_wg - 1) / p.heads_per_wg);
+    // row groups of 16 NCB packed rows each, one per grid layer
+    const int rows = a.group * p.q_max;
+    const unsigned groups = (unsigned)((rows + 16 * NCB - 1) / (16 * NCB));
+    const dim3 grid(p.num_wgs, (p.num_kv_heads + p.heads_per_wg - 1) / p.heads_per_wg, groups);
     const size_t lds = (size_t)p.heads_per_wg * 2 * 16 * (D / 8) * sizeof(u32x4_t);
     hipLaunchKernelGGL((decode_split_bf16<D, NCB>), grid, dim3(64 * p.heads_per_wg), lds,
                        p.stream, a);
     return hipGetLastError();
 }
 
-// Column blocks of packed query rows: G * (query rows per sequence) <= 16 NCB.
+// Column blocks of packed query rows, G * (query rows per sequence) of them:
+// up to NCB blocks of 16 share each wave's K/V reads (NCB <= 4 at d = 64, 1 at
+// d = 128, where more would not fit the registers next to the K/V ring); more
+// rows take further grid layers, which read the K/V again.
 template <int D>
 hipError_t launch_split_rows(const DecodeLaunch &p)
 {
     const int rows = (p.num_q_heads / p.num_kv_heads) * p.q_max;
-    if (rows <= 16)
+    if (rows <= 16 || D != 64)
         return launch_split_d<D, 1>(p);
-    if constexpr (D == 64) {
-        if (rows <= 32)
-            return launch_split_d<D, 2>(p);
-        if (rows <= 64)
-            return launch_split_d<D, 4>(p);
-    }
-    return hipErrorInvalidValue;  // the host checks keep such shapes away
+    if (rows <= 32)
+        return launch_split_d<D, 2>(p);
+    return launch_split_d<D, 4>(p);
 }
 
 template <int D>

@@ -46,10 +46,9 @@ struct PrefillLaunch {
 };
 
 // The most packed query rows (G times query tokens per sequence) the
-// multi-token decode handles per KV head: 64 at d = 64, 16 at d = 128 (one
-// column block; more would not fit the registers next to the K/V ring).
-constexpr int kMultiRowsD64 = 64;
-constexpr int kMultiRowsD128 = 16;
+// multi-token decode takes per KV head (in layers of up to 64 rows at d = 64
+// and of 16 at d = 128); beyond that the prefill kernel runs.
+constexpr int kMultiRowsMax = 128;
 
 // Decode split pass: up to 4 KV heads (waves) per workgroup; the grid gives
 // every one of MI355X's 256 CUs the same number of workgroups, with at least

@@ -304,8 +304,11 @@ def test_multi_workspace_bytes(lib):
         if q == 1:
             assert got == one
     # shapes that run the prefill kernel need no workspace
-    assert ga.attn_sinks_decode_multi_workspace_bytes(64, 64, 8, 64, 8192, 9) == 0   # 72 rows
-    assert ga.attn_sinks_decode_multi_workspace_bytes(4, 64, 4, 128, 9000, 2) == 0   # 32 rows
+    assert ga.attn_sinks_decode_multi_workspace_bytes(64, 64, 8, 64, 8192, 17) == 0  # 136 rows
+    assert ga.attn_sinks_decode_multi_workspace_bytes(4, 64, 4, 128, 9000, 9) == 0   # 144 rows
+    # up to 128 packed rows take the split passes, in layers
+    assert ga.attn_sinks_decode_multi_workspace_bytes(64, 64, 8, 64, 8192, 9) > 0    # 72 rows
+    assert ga.attn_sinks_decode_multi_workspace_bytes(4, 64, 4, 128, 9000, 8) > 0    # 128 rows
     assert ga.attn_sinks_decode_multi_workspace_bytes(4, 64, 8, 96, 9000, 2) == 0    # head_dim
 
 
