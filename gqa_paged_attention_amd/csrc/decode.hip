@@ -480,6 +480,17 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int row0, int b, i
                 compute_block<D, NCB, false>(st, b2, qop, t0 + 64, t_lo, t_end, col_end,
                                              a.scale_log2, lg, klds);
             }
+        } else if constexpr (D == 128 && NCB > 1) {
+            // two column blocks of packed rows leave no registers for a
+            // second block: one block at a time (the many waves of the
+            // layers keep the memory busy)
+            for (int ib = 0; ib < nfull; ++ib) {
+                Block<D> b0;
+                load_block<D, true>(b0, a.k_cache, a.v_cache, bt, at(ib), t_end, g,
+                                    a.num_kv_heads, n, lg);
+                compute_block<D, NCB, false>(st, b0, qop, t_begin + kUnitTokens * ib, t_lo,
+                                             t_end, col_end, a.scale_log2, lg, klds);
+            }
         } else {
             Block<D> b0, b1;
             load_block<D, true>(b0, a.k_cache, a.v_cache, bt, at(0), t_end, g, a.num_kv_heads, n,
@@ -769,18 +780,22 @@ hipError_t launch_split_d(const DecodeLaunch &p)
 }
 
 // Column blocks of packed query rows, G * (query rows per sequence) of them:
-// up to NCB blocks of 16 share each wave's K/V reads (NCB <= 4 at d = 64, 1 at
-// d = 128, where more would not fit the registers next to the K/V ring); more
-// rows take further grid layers, which read the K/V again.
+// up to NCB blocks of 16 share each wave's K/V reads (NCB <= 4 at d = 64, 2 at
+// d = 128, where more would not fit the registers); more rows take further
+// grid layers, which read the K/V again.
 template <int D>
 hipError_t launch_split_rows(const DecodeLaunch &p)
 {
     const int rows = (p.num_q_heads / p.num_kv_heads) * p.q_max;
-    if (rows <= 16 || D != 64)
+    if (rows <= 16)
         return launch_split_d<D, 1>(p);
-    if (rows <= 32)
+    if constexpr (D == 64) {
+        if (rows <= 32)
+            return launch_split_d<D, 2>(p);
+        return launch_split_d<D, 4>(p);
+    } else {
         return launch_split_d<D, 2>(p);
-    return launch_split_d<D, 4>(p);
+    }
 }
 
 template <int D>

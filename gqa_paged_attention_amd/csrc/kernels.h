@@ -47,7 +47,7 @@ struct PrefillLaunch {
 
 // The most packed query rows (G times query tokens per sequence) the
 // multi-token decode takes per KV head (in layers of up to 64 rows at d = 64
-// and of 16 at d = 128); beyond that the prefill kernel runs.
+// and of 32 at d = 128); beyond that the prefill kernel runs.
 constexpr int kMultiRowsMax = 128;
 
 // Decode split pass: up to 4 KV heads (waves) per workgroup; the grid gives

@@ -342,7 +342,7 @@ int attn_sinks_prefill_append(int dtype, int num_seqs, int num_q_heads, int num_
  * causal among the new tokens, sink in every row); the difference is the
  * kernel.  The split-KV decode passes run with the query rows of each KV
  * head packed GQA-style into the matrix columns (G x Lq rows share each K
- * and V block read, in layers of up to 64 rows at head_dim 64 and 16 at
+ * and V block read, in layers of up to 64 rows at head_dim 64 and 32 at
  * head_dim 128; each further layer reads the blocks again), when
  *     dtype is bf16 and G * max_q_len <= 128;
  * other shapes run attn_sinks_prefill and need no workspace.

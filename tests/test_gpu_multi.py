@@ -3,7 +3,7 @@ sequence, as when speculative or MTP drafts are verified) against the
 oracle, which computes it as a causal chunk at the end of each sequence.
 
 Cases cover every packed width (G x Lq query rows per KV head: one, two and
-four 16-column blocks at d = 64, one at d = 128), shapes that need several
+four 16-column blocks at d = 64, one and two at d = 128), shapes that need several
 grid layers of such blocks (up to 128 rows), sequences with fewer new
 tokens than the batch's maximum, sequences shorter than a 32-token block or
 whose new tokens straddle block and page boundaries, and the shapes that
@@ -45,9 +45,10 @@ CASES = [
     ("d64_g16_lq4", "bf16", [9, 777], [4, 4], 32, 2, 64, True),
     ("d128_g8_lq2", "bf16", [2, 129, 1500], [2, 2, 1], 16, 2, 128, True),
     ("d128_g16_lq1", "bf16", [300, 33], [1, 1], 32, 2, 128, True),
-    ("d128_g16_lq2_two_layers", "bf16", [50, 600], [2, 2], 32, 2, 128, True),
-    ("d128_g16_lq4_four_layers", "bf16", [4, 33, 2000], [4, 3, 4], 64, 4, 128, True),
-    ("d128_g16_lq8_eight_layers", "bf16", [8, 1025], [8, 7], 32, 2, 128, True),
+    ("d128_g16_lq2_two_blocks", "bf16", [50, 600], [2, 2], 32, 2, 128, True),
+    ("d128_g8_lq3_two_blocks", "bf16", [3, 70, 1000], [3, 2, 3], 16, 2, 128, True),
+    ("d128_g16_lq4_two_layers", "bf16", [4, 33, 2000], [4, 3, 4], 64, 4, 128, True),
+    ("d128_g16_lq8_four_layers", "bf16", [8, 1025], [8, 7], 32, 2, 128, True),
     ("d64_g8_lq9_two_layers", "bf16", [9, 200], [9, 9], 16, 2, 64, True),
     ("d64_g16_lq8_two_layers", "bf16", [8, 3000, 70], [8, 8, 2], 32, 2, 64, True),
     ("d64_g16_lq9_fallback", "bf16", [9, 200], [9, 9], 32, 2, 64, False),
