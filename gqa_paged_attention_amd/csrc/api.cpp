@@ -241,11 +241,13 @@ int check_append(int dtype, int num_seqs, int num_kv_heads, int head_dim, int pa
 
 int elem_bytes(int dtype) { return dtype == ATTN_DTYPE_F32 ? 4 : 2; }
 
-// bf16 decode of one token per sequence: the direct kernel for a short window
-// that cuts some sequence (max_seq_len > window), else split + merge.
+// bf16 decode of one token per sequence: the direct kernel when every
+// sequence's visible keys are few (a short window that cuts some sequence,
+// or a length bound within the same limit), else split + merge.
 int run_decode_bf16(const attn::DecodeLaunch &p, int max_seq_len)
 {
-    if (p.window > 0 && p.window <= attn::kDirectWindowMax && p.window < max_seq_len)
+    if ((p.window > 0 && p.window <= attn::kDirectWindowMax && p.window < max_seq_len) ||
+        max_seq_len <= attn::kDirectWindowMax)
         return attn::launch_decode_direct_bf16(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
     if (attn::launch_decode_split_bf16(p) != hipSuccess)
         return ATTN_ERR_HIP;

@@ -63,8 +63,9 @@ hipError_t launch_decode_split_bf16(const DecodeLaunch &p);
 // write out in p.dtype.
 hipError_t launch_decode_merge(const DecodeLaunch &p);
 // Direct decode (bf16, one query token, 0 < window <= kDirectWindowMax and
-// window < the length bound): one wave per (sequence, KV head) over the
-// visible keys, sink folded, output written; no workspace, no merge.
+// window < the length bound, or a length bound <= kDirectWindowMax): one wave
+// per (sequence, KV head) over the visible keys, sink folded, output
+// written; no workspace, no merge.
 constexpr int kDirectWindowMax = 512;
 hipError_t launch_decode_direct_bf16(const DecodeLaunch &p);
 hipError_t launch_prefill_bf16(const PrefillLaunch &p);

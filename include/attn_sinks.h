@@ -126,7 +126,10 @@ int attn_sinks_decode(int dtype, int num_seqs, int num_q_heads, int num_kv_heads
 /*
  * The two passes of attn_sinks_decode, callable on their own (bf16 only for
  * the first pass).  attn_sinks_decode is exactly partials followed by merge
- * on the same stream with the same sizes.  Running them separately lets a
+ * on the same stream with the same sizes, except for bf16 calls with
+ * max_seq_len <= 512: those run one direct pass (one wave per sequence and
+ * KV head over all its keys, no workspace touched), whose results meet the
+ * same tolerance but need not equal the two passes' bits.  Running them separately lets a
  * caller time or overlap the passes, or combine partial results computed
  * elsewhere (for example over a KV range held by another device), since the
  * merge reads nothing but the workspace.

@@ -248,6 +248,27 @@ def test_stage_entry_points_equal_decode():
     assert torch.equal(out32.to(torch.bfloat16).view(torch.int16), ref.view(torch.int16))
 
 
+def test_short_contexts_take_the_direct_pass():
+    """With max_seq_len <= 512 attn_sinks_decode runs one direct pass; its
+    results meet the bar against the oracle and against the two stage
+    entry points on the same inputs."""
+    for d, L in ((64, [1, 31, 32, 33, 500, 512]), (128, [7, 200, 512])):
+        b = wl.small_batch(410 + d, "bf16", L, [1] * len(L), 32, 2, d, sink_mode="normal")
+        note(f"short-context decode d={d} L={L}")
+        got = run_decode(b)
+        compare(got, oracle_full(b), "bf16", f"direct decode d={d}")
+        g = b.to("cuda")
+        ws = torch.empty(ga.attn_sinks_decode_workspace_bytes(g.num_seqs, g.num_q_heads,
+                                                              g.num_kv_heads, d, b.max_seq_len),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(g.q)
+        ga.attn_sinks_decode_partials(g.q, g.k_cache, g.v_cache, g.block_table, g.seq_lens,
+                                      g.scale, ws, b.max_seq_len)
+        ga.attn_sinks_decode_merge(g.seq_lens, g.sinks, ws, out, g.num_kv_heads, b.max_seq_len)
+        torch.cuda.synchronize()
+        compare(got, out.cpu().double().numpy(), "bf16", f"direct vs stages d={d}")
+
+
 def test_empty_sequences_give_zero():
     b = wl.small_batch(95, "bf16", [1, 40], [1, 1], 8, 2, 64)
     b = replace(b, seq_lens=torch.tensor([0, 40], dtype=torch.int32))
