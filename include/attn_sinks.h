@@ -100,7 +100,10 @@ size_t attn_sinks_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_
  * ("GPT-OSS on day 0", section "Sink Attention": online softmax with a
  * running max and scale, parallel over heads and over the KV length), and
  * the sink is folded in once, in the final merge of the splits, so it is
- * counted exactly once however the KV range was split.
+ * counted exactly once however the KV range was split.  bf16 calls with
+ * max_seq_len <= 512 take one direct pass instead (one wave per sequence and
+ * KV head over all its keys, the sink folded at its end); the workspace is
+ * still checked but then not touched.
  *
  *   q            [num_seqs][num_q_heads][head_dim]          dtype
  *   k_cache      [num_pages][num_kv_heads][page_size][head_dim] dtype
