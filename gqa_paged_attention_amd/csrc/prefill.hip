@@ -80,6 +80,10 @@ struct Cfg {
     static constexpr int kLdsBytes = 2 * kStages * kTileElems * 2;
 };
 
+// Blocks after which the LDS stage pattern repeats.
+template <int D>
+constexpr int kLdsCycle = Cfg<D>::kBPT * Cfg<D>::kStages;
+
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
@@ -340,6 +344,57 @@ __device__ __forceinline__ void read_v(u32x4_t (&vop)[D / 32][2], const uint16_t
         }
 }
 
+// Per-lane LDS element offsets of read_k's and read_v's reads within a
+// 32-key block (read_k: one per 16-dim slice; read_v: one per 32-dim block,
+// the 16-key halves and the +8 rows being constant offsets from it, as the V
+// swizzle depends on key % 4 only).  With a block address the compiler knows,
+// every read is one of these plus an immediate.
+template <int D>
+struct LdsLanes {
+    int k[D / 16];
+    int v[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ LdsLanes<D> lds_lanes(int lane)
+{
+    const int r32 = lane & 31, half = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
+    const int src_key = 4 * half + (i16 >> 2);
+    const int src_dim = 16 * (g16 & 1) + 4 * (i16 & 3);
+    LdsLanes<D> l;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        l.k[kk] = Swz<D>::k_at(r32, 2 * kk + half);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+        l.v[db] = Swz<D>::v_at(src_key, (32 * db + src_dim) >> 2);
+    return l;
+}
+
+// read_k and read_v (key0 = 0) through precomputed lane offsets.
+template <int D>
+__device__ __forceinline__ void read_k_at(u32x4_t (&kop)[D / 16], const uint16_t *kt,
+                                          const LdsLanes<D> &l)
+{
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        kop[kk] = *(const u32x4_t *)(kt + l.k[kk]);
+}
+
+template <int D>
+__device__ __forceinline__ void read_v_at(u32x4_t (&vop)[D / 32][2], const uint16_t *vt,
+                                          const LdsLanes<D> &l)
+{
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const u32x2_t lo = lds_read_tr(vt + l.v[db] + 16 * ks * D);
+            const u32x2_t hi = lds_read_tr(vt + l.v[db] + (16 * ks + 8) * D);
+            vop[db][ks] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
+}
+
 template <int D>
 __device__ __forceinline__ f32x16_t qk_mfma(const u32x4_t (&qop)[D / 16],
                                             const u32x4_t (&kop)[D / 16])
@@ -454,19 +509,29 @@ __device__ __forceinline__ void qk_all(f32x16_t (&s)[Cfg<D>::kNRB], const WaveSt
 // relative to the reference maxima (set from the block itself when kFirst,
 // masked when kMasked).  A row sum too close to overflow (or not finite)
 // marks the lane in `bad`; such a wave is recomputed exactly after the loop
-// (exact_rows), so the loop itself has no rescale branch.
-template <int D, bool kQK, bool kPV, bool kMasked, bool kFirst>
+// (exact_rows), so the loop itself has no rescale branch.  kPhase >= 0: b is
+// known to be kPhase modulo the LDS cycle (BPT * S blocks), so the operands'
+// LDS addresses are compile-time constants.
+template <int D, bool kQK, bool kPV, bool kMasked, bool kFirst, int kPhase = -1>
 __device__ __forceinline__ void step(WaveState<D> &w, const Smem<D> &sm, int b,
                                      f32x16_t (&s_cur)[Cfg<D>::kNRB],
                                      f32x16_t (&s_next)[Cfg<D>::kNRB], int thr0, float scale_log2,
-                                     int lane, bool &bad, int rb_step)
+                                     int lane, bool &bad, int rb_step,
+                                     const LdsLanes<D> *lanes = nullptr)
 {
     constexpr int NRB = Cfg<D>::kNRB;
     u32x4_t kop[D / 16], vop[D / 32][2];
-    if (kQK)
-        read_k<D>(kop, k_block<D>(sm, b + 1), 0, lane);
-    if (kPV)
-        read_v<D>(vop, v_block<D>(sm, b - 1), 0, lane);
+    if constexpr (kPhase >= 0) {
+        if (kQK)
+            read_k_at<D>(kop, k_block<D>(sm, kPhase + 1), *lanes);
+        if (kPV)
+            read_v_at<D>(vop, v_block<D>(sm, kPhase - 1 + kLdsCycle<D>), *lanes);
+    } else {
+        if (kQK)
+            read_k<D>(kop, k_block<D>(sm, b + 1), 0, lane);
+        if (kPV)
+            read_v<D>(vop, v_block<D>(sm, b - 1), 0, lane);
+    }
     if (kQK)
         qk_all<D>(s_next, w, kop);
     if (kPV) {
@@ -888,6 +953,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     const int bm = (wpf + 1) / kKB;
     const int thr = wpf + row_step * r32 - 4 * half;  // minus the block start
     const float sl2 = a.scale_log2;
+    const LdsLanes<D> lane_ofs = lds_lanes<D>(lane);
     // S^T of the block whose weights are next, and of the one after: two
     // register sets that trade roles every step (the steady loop is unrolled
     // twice so that no copy is needed)
@@ -915,22 +981,63 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     // Steps 1 .. nb-2: all three stages, in pairs (sb then sa holds the
     // current S^T), so that no register copy is needed; step 0 left S^T of
     // block 1 in sb and every pair leaves the next one there.  An odd count
-    // starts with one single step that moves its next S^T into sb.  The
-    // pairs that reach the diagonal run the masked variant (a block with no
+    // ends with one single step that moves its next S^T into sb.  The pairs
+    // that reach the diagonal run the masked variant (a block with no
     // invisible key is unchanged by it).
     int j = 1;
-    if (nb >= 3 && (nb & 1)) {
-        tile_start(1);
-        if (bm <= 1)
-            step<D, true, true, true, false>(w, sm, 1, sb, sa, thr - kKB, sl2, lane, bad, rbs);
-        else
-            step<D, true, true, false, false>(w, sm, 1, sb, sa, 0, sl2, lane, bad, rbs);
+    const int steady_end = min(bm, nb - 1);
+    if constexpr (kLdsCycle<D> == 8) {
+        // The steady pairs in runs of four.  The pairs start at block 1, so
+        // every run starts at a block that is 1 modulo the LDS cycle: its LDS
+        // addresses are compile-time constants (no address arithmetic per
+        // step).
+        for (; j + 7 < steady_end; j += 8) {
+            const int jj = (j & ~7) | 1;  // == j, with its low bits visible
+            // the lane offsets hidden from the compiler for this run, so that
+            // it folds each read's constant block address into the read
+            // instead of keeping eight sets of sums live across the run
+            LdsLanes<D> lr = lane_ofs;
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-            sb[rb] = sa[rb];
-        j = 2;
+            for (int kk = 0; kk < D / 16; ++kk)
+                asm volatile("" : "+v"(lr.k[kk]));
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                asm volatile("" : "+v"(lr.v[db]));
+            tile_start(jj);
+            step<D, true, true, false, false, 1>(w, sm, jj, sb, sa, 0, sl2, lane, bad, rbs,
+                                                &lr);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_start(jj + 1);
+            step<D, true, true, false, false, 2>(w, sm, jj + 1, sa, sb, 0, sl2, lane, bad, rbs,
+                                                &lr);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_start(jj + 2);
+            step<D, true, true, false, false, 3>(w, sm, jj + 2, sb, sa, 0, sl2, lane, bad, rbs,
+                                                &lr);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_start(jj + 3);
+            step<D, true, true, false, false, 4>(w, sm, jj + 3, sa, sb, 0, sl2, lane, bad, rbs,
+                                                &lr);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_start(jj + 4);
+            step<D, true, true, false, false, 5>(w, sm, jj + 4, sb, sa, 0, sl2, lane, bad, rbs,
+                                                &lr);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_start(jj + 5);
+            step<D, true, true, false, false, 6>(w, sm, jj + 5, sa, sb, 0, sl2, lane, bad, rbs,
+                                                &lr);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_start(jj + 6);
+            step<D, true, true, false, false, 7>(w, sm, jj + 6, sb, sa, 0, sl2, lane, bad, rbs,
+                                                &lr);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_start(jj + 7);
+            step<D, true, true, false, false, 0>(w, sm, jj + 7, sa, sb, 0, sl2, lane, bad, rbs,
+                                                &lr);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-    for (; j + 1 < min(bm, nb - 1); j += 2) {
+    for (; j + 1 < steady_end; j += 2) {
         tile_start(j);
         step<D, true, true, false, false>(w, sm, j, sb, sa, 0, sl2, lane, bad, rbs);
         tile_start(j + 1);
@@ -942,6 +1049,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
         tile_start(j + 1);
         step<D, true, true, true, false>(w, sm, j + 1, sa, sb, thr - kKB * (j + 1), sl2, lane,
                                          bad, rbs);
+    }
+    // an odd count of full steps leaves one, which moves its next S^T into sb
+    // (the masked variant leaves a block with no invisible key unchanged)
+    if (j < nb - 1) {
+        tile_start(j);
+        step<D, true, true, true, false>(w, sm, j, sb, sa, thr - kKB * j, sl2, lane, bad, rbs);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+            sb[rb] = sa[rb];
+        ++j;
     }
     // step nb-1: weights of the last block (S^T in sb), P*V of the one before
     if (nb > 1) {
