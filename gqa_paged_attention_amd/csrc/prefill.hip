@@ -212,10 +212,14 @@ struct LoadLanes {
     int key[Cfg<D>::kChunksPerWave];  // key of this lane's row within the tile, per chunk
     int kc[Cfg<D>::kChunksPerWave];   // K chunk (elements) within the row
     int vc[Cfg<D>::kChunksPerWave];   // V chunk (elements) within the row
+    // byte offsets of this lane's K and V chunks in a tile that lies wholly
+    // inside the sequence: from the chunk's page slab (paged), or from the
+    // tile's first key row (contiguous rows kv_stride apart)
+    uint32_t ko[Cfg<D>::kChunksPerWave], vo[Cfg<D>::kChunksPerWave];
 };
 
-template <int D>
-__device__ __forceinline__ LoadLanes<D> load_lanes(int wave, int lane)
+template <int D, bool kContig>
+__device__ __forceinline__ LoadLanes<D> load_lanes(int wave, int lane, int kv_stride)
 {
     using C = Cfg<D>;
     constexpr int kChunks = D / 8;  // 16-byte chunks per key row
@@ -228,6 +232,9 @@ __device__ __forceinline__ LoadLanes<D> load_lanes(int wave, int lane)
         ll.key[i] = key;
         ll.kc[i] = 8 * (slot ^ Swz<D>::ksw(key));
         ll.vc[i] = 8 * (slot ^ (Swz<D>::vsw(key) >> 1));
+        const uint32_t row = kContig ? (uint32_t)key * (uint32_t)kv_stride : (key & 15) * D;
+        ll.ko[i] = 2 * (row + ll.kc[i]);
+        ll.vo[i] = 2 * (row + ll.vc[i]);
     }
     return ll;
 }
@@ -273,6 +280,7 @@ __device__ __forceinline__ ChunkPages chunk_pages(const int32_t *__restrict__ bt
 // Issue this wave's direct loads of tile t (keys t*BN ..) into stage t % S.
 // Rows past the sequence repeat its last row (finite; the causal mask hides
 // them); their page index is clamped to the last page, which holds that row.
+// A tile wholly inside the sequence takes the lanes' precomputed offsets.
 // kContig: K/V rows are contiguous [tokens][Hkv][d] and kv_off is the element
 // offset of the sequence's key 0 for this KV head (the 16-byte chunks of one
 // load then come from R rows kv_stride apart).  Paged: kv_off is the head's
@@ -285,6 +293,17 @@ __device__ __forceinline__ void load_tile(const Smem<D> &sm, const PrefillArgs &
     using C = Cfg<D>;
     const int kv0 = t * C::kBN;
     const int stage = t % C::kStages;
+    if (kv0 + C::kBN <= L) {
+#pragma unroll
+        for (int i = 0; i < C::kChunksPerWave; ++i) {
+            const int j = wave + kWaves * i;
+            const size_t base = kContig ? kv_off + (size_t)kv0 * a.kv_stride
+                                        : (size_t)cp.p[i] * a.num_kv_heads * 16 * D + kv_off;
+            dma16(a.k_cache + base, ll.ko[i], sm.k(stage) + 512 * j);
+            dma16(a.v_cache + base, ll.vo[i], sm.v(stage) + 512 * j);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < C::kChunksPerWave; ++i) {
         const int j = wave + kWaves * i;
@@ -910,7 +929,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
 
     // tiles 0 and 1 in flight before the loop; tile T+2 is issued when the
     // wave starts reading tile T
-    const LoadLanes<D> ll = load_lanes<D>(wave, lane);
+    const LoadLanes<D> ll = load_lanes<D, kContig>(wave, lane, a.kv_stride);
     auto pages = [&](int t) {
         if constexpr (kContig)
             return ChunkPages{{0, 0}};
