@@ -747,6 +747,176 @@ __global__ __launch_bounds__(1024) void decode_merge(MergeArgs a)
     }
 }
 
+// The merge with one wave per (sequence, KV head, query token), taking all G
+// query heads of the group: fewer waves than decode_merge's one per head
+// (the multi-token decode has G x tokens rows per KV head, which as single
+// waves would not fit on the chip at once), in the same arithmetic and order
+// (so the two give the same bits).  After the unit scan that places the
+// sequence's pieces, the lanes take one piece each (64 at a time) for the
+// common maximum of every head (sink included); then, 32 pieces at a time,
+// each piece's weight 2^(m_p - M) and sum l_p go to LDS, and every lane takes
+// its (head, 4-dim chunk) items through the pieces in order: denominator from
+// the sink term on plus f_p l_p, values f_p acc_p, kPB pieces' loads in
+// flight at a time.  Workgroups without a unit wrote nothing; they count
+// with weight 0 and are not read.
+template <int D, bool kBf16Out>
+__global__ __launch_bounds__(64) void decode_merge_group(MergeArgs a)
+{
+    constexpr int kMaxG = 16;
+    constexpr int kChunks = D / 4;                // float4 chunks of a head's row
+    constexpr int kItems = kMaxG * kChunks / 64;  // items per lane at G = 16
+    constexpr int kPB = D == 64 ? 4 : 2;          // pieces whose loads are in flight together
+    constexpr int kPiecesPerPass = 32;
+    __shared__ float wf[kPiecesPerPass * kMaxG], wl[kPiecesPerPass * kMaxG];
+    const int b = blockIdx.x, g = blockIdx.y, tok = blockIdx.z, lane = threadIdx.x;
+    int q_first = b, q_len = 1;
+    if (a.cu_seqlens_q) {
+        q_first = a.cu_seqlens_q[b];
+        q_len = a.cu_seqlens_q[b + 1] - q_first;
+    }
+    if (tok >= q_len)
+        return;
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int h0 = g * G;
+    const int L = a.seq_lens[b];
+    const long long nblk = units_of(L, a.window);
+    int w_lo = 0, w_hi = -1;
+    long long U = 0;
+    if (nblk > 0) {
+        long long before = 0, total = 0;
+        for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
+            const int bi = b0 + lane;
+            const long long u = bi < a.num_seqs ? units_of(a.seq_lens[bi], a.window) : 0;
+            total += u;
+            before += bi < b ? u : 0;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            total += __shfl_xor(total, off, 64);
+            before += __shfl_xor(before, off, 64);
+        }
+        U = total;
+        w_lo = wave_of_unit(before, U, a.num_wgs);
+        w_hi = wave_of_unit(before + nblk - 1, U, a.num_wgs);
+    }
+    auto live = [&](int w) {
+        return wave_first_unit(w, U, a.num_wgs) < wave_first_unit(w + 1, U, a.num_wgs);
+    };
+    // partial-result row of piece w for the group's first head
+    auto row = [&](int w) {
+        return ((size_t)(b + w) * a.q_max + tok) * a.num_q_heads + h0;
+    };
+
+    float M[kMaxG];
+#pragma unroll
+    for (int hh = 0; hh < kMaxG; ++hh)
+        M[hh] = (hh < G && a.sinks) ? a.sinks[h0 + hh] * kLog2e : kNegInf;
+    for (int w0 = w_lo; w0 <= w_hi; w0 += 64) {
+        const int w = w0 + lane;
+        if (w <= w_hi && live(w)) {
+            const float *ml = a.part_ml + row(w) * 2;
+#pragma unroll
+            for (int hh = 0; hh < kMaxG; ++hh)
+                if (hh < G)
+                    M[hh] = fmaxf(M[hh], ml[2 * hh]);
+        }
+    }
+#pragma unroll
+    for (int hh = 0; hh < kMaxG; ++hh)
+        if (hh < G)
+            M[hh] = wave_max(M[hh]);
+
+    // this lane's items: head hi[k], chunk ci[k]; den from the sink term
+    int hi[kItems], ci[kItems];
+    float den[kItems];
+    f32x4_t acc[kItems];
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        const int i = lane + 64 * k;
+        hi[k] = i / kChunks;
+        ci[k] = i % kChunks;
+        acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        den[k] = 0.f;
+    }
+#pragma unroll
+    for (int hh = 0; hh < kMaxG; ++hh) {
+        if (hh < G) {
+            const float sink2 = a.sinks ? a.sinks[h0 + hh] * kLog2e : kNegInf;
+            const float d0 = sink2 == kNegInf ? 0.f : exp2_fast(sink2 - M[hh]);
+#pragma unroll
+            for (int k = 0; k < kItems; ++k)
+                if (hi[k] == hh)
+                    den[k] = d0;
+        }
+    }
+    for (int w0 = w_lo; w0 <= w_hi; w0 += kPiecesPerPass) {
+        const int w = w0 + lane;
+        if (lane < kPiecesPerPass) {
+            const bool ok = w <= w_hi && live(w);
+#pragma unroll
+            for (int hh = 0; hh < kMaxG; ++hh) {
+                if (hh < G) {
+                    float f = 0.f, l = 0.f;
+                    if (ok) {
+                        const float2 ml = *(const float2 *)(a.part_ml + (row(w) + hh) * 2);
+                        f = ml.x == kNegInf ? 0.f : exp2_fast(ml.x - M[hh]);
+                        l = ml.y;
+                    }
+                    wf[lane * kMaxG + hh] = f;
+                    wl[lane * kMaxG + hh] = l;
+                }
+            }
+        }
+        __syncthreads();
+        const int cnt = min(kPiecesPerPass, w_hi - w0 + 1);
+        for (int j0 = 0; j0 < cnt; j0 += kPB) {
+            f32x4_t v[kItems][kPB];
+            float fj[kItems][kPB], lj[kItems][kPB];
+#pragma unroll
+            for (int k = 0; k < kItems; ++k) {
+                const bool item = hi[k] < G;
+#pragma unroll
+                for (int jj = 0; jj < kPB; ++jj) {
+                    const int j = j0 + jj;
+                    const bool in = item && j < cnt;
+                    const float f = in ? wf[j * kMaxG + hi[k]] : 0.f;
+                    fj[k][jj] = f;
+                    lj[k][jj] = in ? wl[j * kMaxG + hi[k]] : 0.f;
+                    v[k][jj] = f != 0.f ? *(const f32x4_t *)(a.part_acc +
+                                                              (row(w0 + j) + hi[k]) * D +
+                                                              4 * ci[k])
+                                        : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kItems; ++k)
+#pragma unroll
+                for (int jj = 0; jj < kPB; ++jj) {
+                    den[k] += fj[k][jj] * lj[k][jj];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[k][e] += fj[k][jj] * v[k][jj][e];
+                }
+        }
+        __syncthreads();
+    }
+    const size_t o = (size_t)(q_first + tok) * a.num_q_heads + h0;
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        if (hi[k] < G) {
+            const float inv = den[k] > 0.f ? 1.f / den[k] : 0.f;
+            const size_t e0 = (o + hi[k]) * D + 4 * ci[k];
+            if constexpr (kBf16Out) {
+                *(u32x2_t *)((uint16_t *)a.out + e0) =
+                    u32x2_t{pack_bf16(acc[k][0] * inv, acc[k][1] * inv),
+                            pack_bf16(acc[k][2] * inv, acc[k][3] * inv)};
+            } else {
+                *(f32x4_t *)((float *)a.out + e0) = acc[k] * inv;
+            }
+        }
+    }
+}
+
 template <int D, int NCB>
 hipError_t launch_split_d(const DecodeLaunch &p)
 {
@@ -815,6 +985,14 @@ hipError_t launch_merge_d(const DecodeLaunch &p)
     m.cu_seqlens_q = p.cu_seqlens_q;
     m.q_max = p.q_max;
     const dim3 grid(p.num_seqs, p.num_kv_heads, p.q_max);
+    if (p.q_max > 1) {
+        // multi-token decode: one wave per (sequence, KV head, token)
+        if (p.dtype == 1)
+            hipLaunchKernelGGL((decode_merge_group<D, true>), grid, dim3(64), 0, p.stream, m);
+        else
+            hipLaunchKernelGGL((decode_merge_group<D, false>), grid, dim3(64), 0, p.stream, m);
+        return hipGetLastError();
+    }
     const dim3 block(64 * (p.num_q_heads / p.num_kv_heads));
     if (p.dtype == 1)
         hipLaunchKernelGGL((decode_merge<D, true>), grid, block, 0, p.stream, m);
