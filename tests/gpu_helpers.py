@@ -4,7 +4,10 @@ from __future__ import annotations
 
 import sys
 
+from dataclasses import replace
+
 import numpy as np
+
 import torch
 
 import gqa_paged_attention_amd as ga
@@ -120,3 +123,32 @@ def check_sampled(got: torch.Tensor, batch_cpu, n_rows: int, seed: int, what: st
     ref = oracle.attention_rows(batch_cpu, toks, heads, threads=ORACLE_THREADS, window=window)
     return compare(got[torch.as_tensor(toks), torch.as_tensor(heads.astype(np.int64))], ref,
                    batch_cpu.dtype, what)
+
+
+def scale_keys(b, first_token, factor):
+    """Multiply the stored K rows of tokens >= first_token of every sequence by
+    `factor` (the oracle reads the same stored values)."""
+    k = b.k_cache.clone()
+    for s in range(b.num_seqs):
+        for t in range(first_token, int(b.seq_lens[s])):
+            page = int(b.block_table[s, t // 16])
+            k[page, :, t % 16, :] = (k[page, :, t % 16, :].float() * factor).to(k.dtype)
+    return replace(b, k_cache=k)
+
+
+def aligned_scores(b, seed, q_norm, k_norm):
+    """Every query of KV head g is q_norm u_g (+ noise 0.1) and every stored
+    key of it is -k_norm u_g (+ noise 0.5), u_g a random unit vector: all
+    logits near -scale q_norm k_norm, spread by a few units."""
+    gen = torch.Generator().manual_seed(seed)
+    G = b.num_q_heads // b.num_kv_heads
+    u = torch.randn(b.num_kv_heads, b.head_dim, generator=gen)
+    u = u / u.norm(dim=1, keepdim=True)
+    q = (q_norm * u.repeat_interleave(G, dim=0)[None] +
+         0.1 * torch.randn(b.q.shape, generator=gen)).to(b.q.dtype)
+    k = b.k_cache.float().clone()
+    for s_ in range(b.num_seqs):
+        for t in range(int(b.seq_lens[s_])):
+            page = int(b.block_table[s_, t // 16])
+            k[page, :, t % 16, :] = -k_norm * u + 0.5 * torch.randn(u.shape, generator=gen)
+    return replace(b, q=q, k_cache=k.to(b.k_cache.dtype))

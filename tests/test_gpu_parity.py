@@ -15,7 +15,8 @@ import torch
 import gqa_paged_attention_amd as ga
 import oracle
 from gqa_paged_attention_amd import workloads as wl
-from tests.gpu_helpers import (check_sampled, compare, note, oracle_full, run_decode,
+from tests.gpu_helpers import (aligned_scores as _aligned_scores, check_sampled, compare, note,
+                               oracle_full, run_decode, scale_keys as _scale_keys,
                                run_prefill)
 
 pytestmark = pytest.mark.gpu
@@ -106,17 +107,6 @@ def test_null_sinks_equal_neginf_sinks():
                        run_prefill(replace(p, sinks=None)).view(torch.int16))
 
 
-def _scale_keys(b, first_token, factor):
-    """Multiply the stored K rows of tokens >= first_token of every sequence by
-    `factor` (the oracle reads the same stored values)."""
-    k = b.k_cache.clone()
-    for s in range(b.num_seqs):
-        for t in range(first_token, int(b.seq_lens[s])):
-            page = int(b.block_table[s, t // 16])
-            k[page, :, t % 16, :] = (k[page, :, t % 16, :].float() * factor).to(k.dtype)
-    return replace(b, k_cache=k)
-
-
 @pytest.mark.parametrize("d,L,Lq", [(64, 300, 300), (64, 700, 190), (128, 400, 400)])
 def test_prefill_large_late_logits(d, L, Lq):
     """Keys after the first 64 get logits far above every early one (std ~100
@@ -129,24 +119,6 @@ def test_prefill_large_late_logits(d, L, Lq):
     note(f"decode large late logits d={d} L={L}")
     dec = replace(b, cu_seqlens_q=torch.tensor([0, 1], dtype=torch.int32), q=b.q[-1:].contiguous())
     compare(run_decode(dec), oracle_full(dec), "bf16", f"decode large late logits d={d}")
-
-
-def _aligned_scores(b, seed, q_norm, k_norm):
-    """Every query of KV head g is q_norm u_g (+ noise 0.1) and every stored
-    key of it is -k_norm u_g (+ noise 0.5), u_g a random unit vector: all
-    logits near -scale q_norm k_norm, spread by a few units."""
-    gen = torch.Generator().manual_seed(seed)
-    G = b.num_q_heads // b.num_kv_heads
-    u = torch.randn(b.num_kv_heads, b.head_dim, generator=gen)
-    u = u / u.norm(dim=1, keepdim=True)
-    q = (q_norm * u.repeat_interleave(G, dim=0)[None] +
-         0.1 * torch.randn(b.q.shape, generator=gen)).to(b.q.dtype)
-    k = b.k_cache.float().clone()
-    for s_ in range(b.num_seqs):
-        for t in range(int(b.seq_lens[s_])):
-            page = int(b.block_table[s_, t // 16])
-            k[page, :, t % 16, :] = -k_norm * u + 0.5 * torch.randn(u.shape, generator=gen)
-    return replace(b, q=q, k_cache=k.to(b.k_cache.dtype))
 
 
 @pytest.mark.parametrize("d,L,Lq", [(64, 300, 300), (64, 700, 190), (128, 400, 400)])

@@ -9,12 +9,14 @@ sequences shorter than the window, chunks over cached prefixes, both head
 dims and fp32, plus the full-size gpt-oss shapes at W = 128.
 """
 import zlib
+from dataclasses import replace
 
 import pytest
 import torch
 
 from gqa_paged_attention_amd import workloads as wl
-from tests.gpu_helpers import check_sampled, compare, note, oracle_full, run_decode, run_prefill
+from tests.gpu_helpers import (aligned_scores, check_sampled, compare, note, oracle_full,
+                               run_decode, run_prefill, scale_keys)
 
 pytestmark = pytest.mark.gpu
 
@@ -88,6 +90,36 @@ def test_window_runs_are_deterministic():
     note("window determinism")
     assert torch.equal(_bits(run_decode(d, window=128)), _bits(run_decode(d, window=128)))
     assert torch.equal(_bits(run_prefill(p, window=128)), _bits(run_prefill(p, window=128)))
+
+
+@pytest.mark.parametrize("d,L,Lq", [(64, 700, 700), (128, 500, 300)])
+def test_window_large_late_logits(d, L, Lq):
+    """Keys from position 200 on get logits far above the earlier ones (std
+    ~100 in natural units): rows whose window holds both kinds must raise
+    their maximum well past the lazy slack and rescale.  Prefill at W = 128;
+    decode at W = 600, whose window spans both kinds (the split passes)."""
+    b = wl.small_batch(600 + d + L, "bf16", [L], [Lq], 8, 2, d)
+    b = scale_keys(b, 200, 100.0)
+    note(f"window prefill large late logits d={d} L={L} Lq={Lq}")
+    compare(run_prefill(b, window=128), oracle_full(b, window=128), "bf16",
+            f"window prefill large late logits d={d}")
+    dec = replace(b, cu_seqlens_q=torch.tensor([0, 1], dtype=torch.int32),
+                  q=b.q[-1:].contiguous())
+    note(f"window decode large late logits d={d} L={L}")
+    compare(run_decode(dec, window=600), oracle_full(dec, window=600), "bf16",
+            f"window decode large late logits d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_window_prefill_logits_far_below_zero(d):
+    """Every logit near -150 (natural units) and no sink: weights against a
+    zero reference would underflow to 0; each row's maximum has to come from
+    its own first visible block."""
+    b = wl.small_batch(700 + d, "bf16", [600], [600], 8, 2, d, sink_mode="none")
+    b = aligned_scores(b, 9 + d, 30.0, 150.0 / (30.0 * b.scale))
+    note(f"window prefill logits near -150, no sink, d={d}")
+    compare(run_prefill(b, window=128), oracle_full(b, window=128), "bf16",
+            f"window prefill low logits d={d}")
 
 
 def test_full_gptoss_decode_window128():
