@@ -2,6 +2,8 @@
 sequence, "Fast embeddings on GPUs": ragged inputs and no KV cache) with
 and without the causal mask, and of the row LSE it reports, against the
 oracle (which reads the same values laid out in pages)."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -9,7 +11,7 @@ import torch
 import gqa_paged_attention_amd as ga
 import oracle
 from gqa_paged_attention_amd import workloads as wl
-from tests.gpu_helpers import ORACLE_THREADS, compare, note, require_gpu
+from tests.gpu_helpers import ORACLE_THREADS, compare, note, require_gpu, scale_keys
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +60,29 @@ def test_ragged(case, causal):
                                     causal=causal)
     compare(out, ref, "bf16", f"ragged {name} causal={causal}")
     check_lse(lse, ref_lse, f"ragged {name} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "unmasked"])
+def test_ragged_large_late_logits(causal):
+    """Keys from position 64 on get logits far above the earlier ones (std ~100
+    in natural units): weights against the reference taken from the first
+    keys cannot hold them, so the exact recompute runs; its outputs and LSE
+    meet the bar.  The contiguous K rows and the oracle's paged copy are
+    scaled alike."""
+    r = wl.ragged_batch(503 + int(causal), "bf16", [300, 700], [300, 190], 8, 2, 64,
+                        sink_mode="normal")
+    k = r.k.clone()
+    cu = r.cu_seqlens_kv
+    for s in range(len(cu) - 1):
+        lo, hi = int(cu[s]) + 64, int(cu[s + 1])
+        k[lo:hi] = (k[lo:hi].float() * 100.0).to(k.dtype)
+    r = replace(r, k=k, paged=scale_keys(r.paged, 64, 100.0))
+    note(f"ragged large late logits causal={causal}")
+    out, lse = run_ragged(r, causal)
+    ref, ref_lse = oracle.attention(r.paged, threads=ORACLE_THREADS, with_lse=True,
+                                    causal=causal)
+    compare(out, ref, "bf16", f"ragged large late logits causal={causal}")
+    check_lse(lse, ref_lse, f"ragged large late logits causal={causal}")
 
 
 def test_ragged_unmasked_more_rows_than_keys_and_empty_sequences():
