@@ -456,11 +456,11 @@ int attn_sinks_rope_append(int dtype, int num_seqs, int num_q_heads, int num_kv_
                       max_pages_per_seq, max_seq_len);
     if (rc != ATTN_OK)
         return rc;
-    if (!(std::isfinite(rope_base) && rope_base > 0.f && std::isfinite(rope_scale) &&
-          rope_scale > 0.f && orig_ctx > 0))
+    if (!(std::isfinite(rope_base) && rope_base > 0.f && rope_base != 1.f &&
+          std::isfinite(rope_scale) && rope_scale > 0.f && orig_ctx > 0))
         return ATTN_ERR_SHAPE;
     if (rope_scale != 1.f && !(std::isfinite(beta_fast) && std::isfinite(beta_slow) &&
-                               beta_fast > beta_slow))
+                               beta_fast > beta_slow && beta_slow > 0.f))
         return ATTN_ERR_SHAPE;
     if (num_seqs == 0 || total_new == 0)
         return ATTN_OK;
@@ -468,22 +468,26 @@ int attn_sinks_rope_append(int dtype, int num_seqs, int num_q_heads, int num_kv_
         return ATTN_ERR_NULL;
     if (!aligned16(q) || !aligned4(positions))
         return ATTN_ERR_ALIGN;
-    // YaRN frequencies: pair i turns at base^(-2i/d); pairs that turn fewer
-    // than beta_slow times in the original context are interpolated by the
-    // scale, pairs that turn more than beta_fast times are kept, linearly
-    // blended in between; q and k are multiplied by 0.1 ln(scale) + 1.
+    // YaRN frequencies: pair i turns at theta_i = base^(-2i/d).  The pair
+    // that turns beta times within the original context sits at the
+    // fractional index c(beta) = (d/2) ln(orig_ctx / (2 pi beta)) / ln(base);
+    // pairs below c(beta_fast) keep theta_i, pairs above c(beta_slow) turn at
+    // theta_i / scale, and the blend is linear in the pair index in between.
+    // q and k are multiplied by 0.1 ln(scale) + 1.
     double freq[64];
     const double s = rope_scale;
+    const double half = head_dim / 2.0, ln_base = std::log((double)rope_base);
+    const double lo = half * std::log(orig_ctx / (2.0 * M_PI * beta_fast)) / ln_base;
+    const double hi = half * std::log(orig_ctx / (2.0 * M_PI * beta_slow)) / ln_base;
     for (int i = 0; i < head_dim / 2; ++i) {
         const double theta = std::pow((double)rope_base, -2.0 * i / head_dim);
         if (s == 1.0) {
             freq[i] = theta;
             continue;
         }
-        const double turns = orig_ctx * theta / (2.0 * M_PI);
-        double ramp = (turns - beta_slow) / ((double)beta_fast - beta_slow);
+        double ramp = (i - lo) / (hi - lo);
         ramp = ramp < 0.0 ? 0.0 : (ramp > 1.0 ? 1.0 : ramp);
-        freq[i] = (1.0 - ramp) * theta / s + ramp * theta;
+        freq[i] = (1.0 - ramp) * theta + ramp * theta / s;
     }
     const float mscale = s > 1.0 ? (float)(0.1 * std::log(s) + 1.0) : 1.f;
     return attn::launch_rope_append(elem_bytes(dtype), num_seqs, num_q_heads, num_kv_heads,

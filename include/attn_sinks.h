@@ -275,12 +275,15 @@ int attn_sinks_append_kv(int dtype, int num_seqs, int num_kv_heads, int head_dim
  * 1 / RopeScale, beta_fast 32, beta_slow 1; section 4.1; section 11: the
  * positions come as an explicit array).  The notes give those parameters,
  * not the formula; the formula is YaRN's ("NTK-by-parts" interpolation with
- * attention scaling):
+ * attention scaling) in the form that takes beta_fast and beta_slow, the
+ * arguments the notes' RoPEEx call names: the pair that turns beta times
+ * within orig_ctx sits at the fractional index c(beta), and the blend is
+ * linear in the pair index between c(beta_fast) and c(beta_slow):
  *
  *   theta_i = rope_base^(-2 i / head_dim)              i = 0 .. head_dim/2 - 1
- *   r_i     = orig_ctx * theta_i / (2 pi)              turns within orig_ctx
- *   gamma_i = clamp((r_i - beta_slow) / (beta_fast - beta_slow), 0, 1)
- *   f_i     = (1 - gamma_i) theta_i / rope_scale + gamma_i theta_i
+ *   c(beta) = (head_dim / 2) ln(orig_ctx / (2 pi beta)) / ln(rope_base)
+ *   ramp_i  = clamp((i - c(beta_fast)) / (c(beta_slow) - c(beta_fast)), 0, 1)
+ *   f_i     = (1 - ramp_i) theta_i + ramp_i theta_i / rope_scale
  *   c       = 0.1 ln(rope_scale) + 1  (1 when rope_scale <= 1)
  *
  * and a row x at position p becomes, for every pair (i, i + head_dim/2):
@@ -297,8 +300,9 @@ int attn_sinks_append_kv(int dtype, int num_seqs, int num_kv_heads, int head_dim
  *   q              [total_new][num_q_heads][head_dim] dtype, read and written
  *   positions      [total_new] int32 rotary position of each new token
  *                  (usually its cache position; any value is accepted)
- *   rope_base      > 0; rope_scale > 0; orig_ctx > 0; when rope_scale != 1,
- *                  beta_fast > beta_slow (all finite), else ATTN_ERR_SHAPE
+ *   rope_base      > 0 and != 1; rope_scale > 0; orig_ctx > 0; when
+ *                  rope_scale != 1, beta_fast > beta_slow > 0 (all finite),
+ *                  else ATTN_ERR_SHAPE
  *   the rest       as for attn_sinks_append_kv (num_q_heads as for decode)
  * The new K rows in k_new are read only.  Device preconditions as for
  * attn_sinks_append_kv.

@@ -15,15 +15,19 @@ the published one:
   by the angle p * theta_i.  NeoX pairing: element i pairs with element
   i + d/2 (not with 2i+1).
 * YaRN (Peng et al., "YaRN: Efficient Context Window Extension of Large
-  Language Models", "NTK-by-parts" interpolation and attention scaling):
-  with scale s (= RopeScale), original context L0 and the pair's wavelength
-  lambda_i = 2 pi / theta_i, let r_i = L0 / lambda_i and
-      gamma(r) = 0 if r < beta_slow,  1 if r > beta_fast,
-                 (r - beta_slow) / (beta_fast - beta_slow) otherwise;
-  the pair's frequency becomes (1 - gamma) theta_i / s + gamma theta_i
-  (slow pairs are interpolated by s, fast pairs kept), and both q and k are
-  multiplied by sqrt(1/t) = 0.1 ln(s) + 1 (1 when s <= 1), so the logits
-  carry the paper's temperature.  s = 1 gives plain RoPE.
+  Language Models", "NTK-by-parts" interpolation and attention scaling),
+  in the form that takes beta_fast and beta_slow as arguments, as the notes'
+  RoPEEx call does: a pair that turns `beta` times within the original
+  context L0 (L0 theta_i / (2 pi) = beta) sits at the fractional pair index
+      c(beta) = (d/2) ln(L0 / (2 pi beta)) / ln(base);
+  pairs below lo = c(beta_fast) turn more often and keep theta_i, pairs
+  above hi = c(beta_slow) are interpolated to theta_i / s, and in between
+  the blend is linear in the pair index:
+      ramp_i = clamp((i - lo) / (hi - lo), 0, 1),
+      f_i = (1 - ramp_i) theta_i + ramp_i theta_i / s.
+  The bounds are used as they are, not rounded to whole pairs.  Both q and
+  k are multiplied by sqrt(1/t) = 0.1 ln(s) + 1 (1 when s <= 1), so the
+  logits carry the paper's temperature.  s = 1 gives plain RoPE.
 """
 from __future__ import annotations
 
@@ -33,6 +37,11 @@ import numpy as np
 import torch
 
 
+def correction_index(head_dim: int, base: float, orig_ctx: float, turns: float) -> float:
+    """Fractional pair index whose pair turns `turns` times within orig_ctx."""
+    return (head_dim / 2.0) * math.log(orig_ctx / (2.0 * math.pi * turns)) / math.log(base)
+
+
 def yarn_frequencies(head_dim: int, base: float, scale: float, orig_ctx: int,
                      beta_fast: float, beta_slow: float) -> np.ndarray:
     """Per-pair angular frequencies [head_dim / 2] in fp64."""
@@ -40,9 +49,10 @@ def yarn_frequencies(head_dim: int, base: float, scale: float, orig_ctx: int,
     theta = np.array([base ** (-2.0 * i / head_dim) for i in range(half)], dtype=np.float64)
     if scale == 1.0:
         return theta
-    r = orig_ctx * theta / (2.0 * math.pi)  # rotations of the pair within L0
-    gamma = np.clip((r - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)
-    return (1.0 - gamma) * theta / scale + gamma * theta
+    lo = correction_index(head_dim, base, orig_ctx, beta_fast)
+    hi = correction_index(head_dim, base, orig_ctx, beta_slow)
+    ramp = np.clip((np.arange(half, dtype=np.float64) - lo) / (hi - lo), 0.0, 1.0)
+    return (1.0 - ramp) * theta + ramp * theta / scale
 
 
 def yarn_mscale(scale: float) -> float:

@@ -253,6 +253,9 @@ def _rope(lib, **kw):
     (dict(orig=0), ERR_SHAPE),
     (dict(bf=1.0, bs=1.0), ERR_SHAPE),        # empty ramp with scale != 1
     (dict(bf=float("nan")), ERR_SHAPE),
+    (dict(bs=0.0), ERR_SHAPE),                # no pair turns zero times
+    (dict(bf=-1.0, bs=-2.0), ERR_SHAPE),
+    (dict(base=1.0), ERR_SHAPE),              # ln(base) = 0
     (dict(q=None), ERR_NULL),
     (dict(pos=None), ERR_NULL),
     (dict(k_new=None), ERR_NULL),

@@ -14,9 +14,14 @@ against what the mathematics fixes rather than against a retyped copy of it:
   the original context, divides by s those that turn fewer than beta_slow
   times, and blends monotonically in between; the rotation applies exactly
   those frequencies;
+* inside the blend, the frequencies of a hand-worked case
+  (tests/golden/yarn_ramp.json) and a blend weight that is affine in the
+  pair index (its second differences vanish);
 * the fused append writes V as the plain append does and K rotated.
 """
+import json
 import math
+import os
 import types
 
 import numpy as np
@@ -120,8 +125,34 @@ def pin_fused_append(impl):
     assert torch.equal(vc.view(torch.int16), vplain.view(torch.int16))
 
 
+GOLDEN_YARN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "yarn_ramp.json")
+
+
+def pin_yarn_golden(impl):
+    g = json.load(open(GOLDEN_YARN))
+    p = g["params"]
+    f = impl.yarn_frequencies(p["head_dim"], p["base"], p["scale"], p["orig_ctx"],
+                              p["beta_fast"], p["beta_slow"])
+    for i, want in g["frequencies"].items():
+        assert math.isclose(f[int(i)], want, rel_tol=g["tolerance_rel"]), (i, f[int(i)], want)
+
+
+def pin_yarn_ramp_affine(impl):
+    # the blend weight w_i = (1 - f_i / theta_i) / (1 - 1/s) of the pairs
+    # strictly inside the blend is affine in i, at several bases and heads
+    for d, base, s, ctx in ((64, BASE, 32.0, ORIG), (128, 500000.0, 8.0, 8192),
+                            (64, 150000.0, 32.0, ORIG)):
+        f = impl.yarn_frequencies(d, base, s, ctx, BF, BS)
+        theta = np.power(base, -np.arange(d // 2) * 2.0 / d)
+        w = (1.0 - f / theta) / (1.0 - 1.0 / s)
+        inner = np.nonzero((w > 1e-12) & (w < 1 - 1e-12))[0]
+        assert len(inner) >= 4, (d, base, inner)
+        assert np.all(np.diff(inner) == 1)
+        np.testing.assert_allclose(np.diff(w[inner], 2), 0.0, atol=1e-12)
+
+
 PINS = [pin_complex_form, pin_identity_at_zero, pin_norms, pin_relative_position,
-        pin_yarn_regions, pin_fused_append]
+        pin_yarn_regions, pin_yarn_golden, pin_yarn_ramp_affine, pin_fused_append]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -140,15 +171,25 @@ MUTANTS = {
                       "x1, x2 = x[..., 0::2], x[..., 1::2]"),
     "rotation turned the other way": ("x1 * c - x2 * s, x1 * s + x2 * c",
                                       "x1 * c + x2 * s, x2 * c - x1 * s"),
-    "ramp reversed": ("(1.0 - gamma) * theta / scale + gamma * theta",
-                      "gamma * theta / scale + (1.0 - gamma) * theta"),
-    "ramp bounds swapped": ("np.clip((r - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)",
-                            "np.clip((r - beta_fast) / (beta_slow - beta_fast), 0.0, 1.0)"),
+    "ramp reversed": ("(1.0 - ramp) * theta + ramp * theta / scale",
+                      "ramp * theta + (1.0 - ramp) * theta / scale"),
+    "ramp bounds swapped": ("(np.arange(half, dtype=np.float64) - lo) / (hi - lo)",
+                            "(np.arange(half, dtype=np.float64) - hi) / (lo - hi)"),
+    "ramp linear in the pair's turns, not its index": (
+        "np.clip((np.arange(half, dtype=np.float64) - lo) / (hi - lo), 0.0, 1.0)",
+        "1.0 - np.clip((orig_ctx * theta / (2.0 * math.pi) - beta_slow) / "
+        "(beta_fast - beta_slow), 0.0, 1.0)"),
+    "correction bounds rounded outward to whole pairs": (
+        "ramp = np.clip((np.arange(half, dtype=np.float64) - lo)",
+        "lo, hi = math.floor(lo), math.ceil(hi)\n"
+        "    ramp = np.clip((np.arange(half, dtype=np.float64) - lo)"),
+    "correction index without the factor d/2": (
+        "return (head_dim / 2.0) * math.log(", "return math.log("),
     "YaRN factor dropped": ("axis=-1) * mscale", "axis=-1)"),
     "frequency exponent halved": ("base ** (-2.0 * i / head_dim)", "base ** (-1.0 * i / head_dim)"),
     "positions off by one": ("ang = pos[:, None] * freqs[None, :]",
                              "ang = (pos[:, None] + 1) * freqs[None, :]"),
-    "slow pairs not interpolated": ("theta / scale + gamma", "theta + gamma"),
+    "slow pairs not interpolated": ("ramp * theta / scale", "ramp * theta"),
 }
 
 
