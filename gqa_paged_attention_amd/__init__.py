@@ -57,6 +57,8 @@ def library():
     lib.attn_sinks_prefill.restype = I
     lib.attn_sinks_decode_window.argtypes = [I] * 9 + [P] * 6 + [F, I, P, P, Z, P]
     lib.attn_sinks_decode_window.restype = I
+    lib.attn_sinks_decode_noalloc.argtypes = [I] * 9 + [P] * 6 + [F, I, P, P]
+    lib.attn_sinks_decode_noalloc.restype = I
     lib.attn_sinks_prefill_window.argtypes = [I] * 11 + [P] * 7 + [F, I, P, P]
     lib.attn_sinks_prefill_window.restype = I
     lib.attn_sinks_append_kv.argtypes = [I] * 9 + [P] * 7 + [P]
@@ -147,8 +149,18 @@ def attn_sinks_decode_window(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
             workspace, max_seq_len, stream)
 
 
+def attn_sinks_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              block_table: torch.Tensor, seq_lens: torch.Tensor,
+                              sinks: Optional[torch.Tensor], scale: float, window: int,
+                              out: torch.Tensor, max_seq_len: int, stream=None) -> None:
+    """Enqueue attn_sinks_decode_noalloc: attn_sinks_decode_window with the
+    partial results in the library's fixed per-GPU scratch (no workspace)."""
+    _decode(int(window), q, k_cache, v_cache, block_table, seq_lens, sinks, scale, out, None,
+            max_seq_len, stream, noalloc=True)
+
+
 def _decode(window, q, k_cache, v_cache, block_table, seq_lens, sinks, scale, out, workspace,
-            max_seq_len, stream):
+            max_seq_len, stream, noalloc=False):
     dt = _DTYPE_CODE.get(q.dtype)
     if dt is None:
         raise ValueError(f"unsupported dtype {q.dtype}")
@@ -168,6 +180,10 @@ def _decode(window, q, k_cache, v_cache, block_table, seq_lens, sinks, scale, ou
     head = (dt, B, Hq, Hkv, d, P, num_pages, block_table.shape[1], int(max_seq_len),
             _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(sinks),
             ctypes.c_float(scale))
+    if noalloc:
+        _raise(library().attn_sinks_decode_noalloc(*head, window, _ptr(out),
+                                                   _stream_handle(stream)))
+        return
     tail = (_ptr(out), _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(stream))
     if window is None:
         status = library().attn_sinks_decode(*head, *tail)

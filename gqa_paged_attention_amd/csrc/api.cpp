@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cstddef>
 #include <cmath>
 #include <cstdlib>
 #include <mutex>
@@ -254,6 +255,37 @@ int run_decode_bf16(const attn::DecodeLaunch &p, int max_seq_len)
     return attn::launch_decode_merge(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+// Fixed scratch of attn_sinks_decode_noalloc, for callers that cannot
+// allocate: the split pass's partial results go here instead of into a
+// caller workspace.  Every device the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address comes from hipGetSymbolAddress, once
+// per device with that device current, and only that address is used.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`.
+int scratch_address(void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return ATTN_ERR_HIP;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev])
+        return ATTN_ERR_HIP;
+    *ptr = g_scratch_ptr[dev];
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -303,6 +335,42 @@ int attn_sinks_decode_window(int dtype, int num_seqs, int num_q_heads, int num_k
                                              out, p.stream);
         return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
     }
+    return run_decode_bf16(p, max_seq_len);
+}
+
+int attn_sinks_decode_noalloc(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                              int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                              int max_seq_len, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *block_table,
+                              const int32_t *seq_lens, const float *sinks, float scale,
+                              int window, void *out, void *stream)
+{
+    // Every check of attn_sinks_decode_window first, against the fixed
+    // scratch's size (a stand-in address: nothing is dereferenced here).
+    attn::DecodeLaunch p;
+    void *const stand_in = reinterpret_cast<void *>((uintptr_t)256);
+    int rc = prepare_decode(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                            num_pages, max_pages_per_seq, max_seq_len, q, k_cache, v_cache,
+                            block_table, seq_lens, sinks, scale, window, out, stand_in,
+                            kScratchBytes, stream, true, true, &p);
+    if (rc == ATTN_ERR_WORKSPACE)
+        return ATTN_ERR_SCRATCH;
+    if (rc != ATTN_OK || num_seqs == 0)
+        return rc;
+    if (dtype == ATTN_DTYPE_F32) {
+        hipError_t e = attn::launch_rows_f32(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             max_pages_per_seq, num_seqs, q, k_cache, v_cache,
+                                             block_table, seq_lens, nullptr, sinks, scale, window,
+                                             out, p.stream);
+        return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    }
+    void *ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc != ATTN_OK)
+        return rc;
+    const ptrdiff_t acc_offset = p.part_acc - p.part_ml;
+    p.part_ml = static_cast<float *>(ws);
+    p.part_acc = p.part_ml + acc_offset;
     return run_decode_bf16(p, max_seq_len);
 }
 
@@ -702,6 +770,9 @@ const char *attn_sinks_status_string(int status)
     case ATTN_ERR_WORKSPACE: return "decode workspace is smaller than required";
     case ATTN_ERR_ALIGN: return "a pointer is not aligned as required";
     case ATTN_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case ATTN_ERR_SCRATCH:
+        return "the call needs more than the 32 MiB fixed scratch of attn_sinks_decode_noalloc "
+               "(attn_sinks_decode_workspace_bytes gives the size it needs)";
     default: return "unknown status";
     }
 }

@@ -42,7 +42,8 @@
  *   - stream is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously; the caller keeps every buffer alive until the stream
  *     has passed the call.  The library allocates nothing, frees nothing and
- *     keeps no pointer after returning, never synchronises and never copies
+ *     keeps no pointer after returning (attn_sinks_decode_noalloc uses a
+ *     fixed scratch of its own instead), never synchronises and never copies
  *     device data to the host, so calls can be captured into a HIP graph.
  *   - Arguments are checked on the host before anything is enqueued; a
  *     nonzero return value means nothing was enqueued, except ATTN_ERR_HIP,
@@ -52,7 +53,8 @@
  *     non-decreasing from 0 to total_q.  Violations are undefined behaviour.
  *   - Faults of the device work surface at the caller's next synchronisation.
  *   - Calls are re-entrant; the library's only state is a read-once cache of
- *     debug environment settings.
+ *     debug environment settings and, for attn_sinks_decode_noalloc only,
+ *     a fixed device scratch array per GPU (see there).
  */
 #ifndef ATTN_SINKS_H
 #define ATTN_SINKS_H
@@ -76,7 +78,9 @@ enum attn_status {
     ATTN_ERR_UNSUPPORTED = 3, /* dtype / head_dim / page_size / group size      */
     ATTN_ERR_WORKSPACE = 4,   /* decode workspace smaller than required         */
     ATTN_ERR_ALIGN = 5,       /* a pointer is not aligned as required          */
-    ATTN_ERR_HIP = 6          /* the HIP runtime rejected a launch              */
+    ATTN_ERR_HIP = 6,         /* the HIP runtime rejected a launch              */
+    ATTN_ERR_SCRATCH = 7      /* needs more than attn_sinks_decode_noalloc's
+                                 fixed scratch                                 */
 };
 
 /* Supported: head_dim 64 or 128; page_size 16; Hq % Hkv == 0 with
@@ -230,6 +234,36 @@ int attn_sinks_decode_window(int dtype, int num_seqs, int num_q_heads, int num_k
                              const void *v_cache, const int32_t *block_table,
                              const int32_t *seq_lens, const float *sinks, float scale, int window,
                              void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_sinks_decode_noalloc -- attn_sinks_decode_window without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * The split pass's partial results go to a fixed scratch array inside the
+ * library instead: 32 MiB of device memory per GPU the library runs on,
+ * held until the process ends.  The call itself allocates and frees
+ * nothing; its first call on a device looks up that device's copy of the
+ * array (the current device, hipGetDevice; the stream must belong to it).
+ *
+ * Arguments, results, checks and errors are those of
+ * attn_sinks_decode_window (window 0: attn_sinks_decode), with the same bits.
+ * A call whose workspace size (attn_sinks_decode_workspace_bytes of its
+ * sizes) exceeds 32 MiB returns ATTN_ERR_SCRATCH with nothing enqueued; the
+ * limit admits, for instance, 1800 sequences at 64 q heads and head_dim 64,
+ * or 700 at 64 q heads and head_dim 128.  ATTN_ERR_HIP also reports a failed
+ * lookup of the scratch.
+ *
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls on one stream
+ * are ordered and safe, but two calls that may overlap on one GPU (different
+ * streams without ordering between them) race and give undefined results.
+ */
+int attn_sinks_decode_noalloc(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                              int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                              int max_seq_len, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *block_table,
+                              const int32_t *seq_lens, const float *sinks, float scale,
+                              int window, void *out, void *stream);
 
 int attn_sinks_prefill_window(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
                               int head_dim, int page_size, int num_pages, int max_pages_per_seq,

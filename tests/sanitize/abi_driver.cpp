@@ -70,6 +70,18 @@ int main()
                                                      at(F), ip(F), ip(F), nullptr, .125f, -1,
                                                      at(F), at(F), big, nullptr),
            ATTN_ERR_SHAPE);
+    expect("noalloc beyond the scratch",
+           attn_sinks_decode_noalloc(1, 2000, 64, 8, 64, 16, 1, 512, 8192, at(F), at(F), at(F),
+                                     ip(F), ip(F), nullptr, .125f, 0, at(F), nullptr),
+           ATTN_ERR_SCRATCH);
+    expect("noalloc window", attn_sinks_decode_noalloc(1, 2, 8, 2, 64, 16, 8, 4, 64, at(F),
+                                                       at(F), at(F), ip(F), ip(F), nullptr,
+                                                       .125f, -1, at(F), nullptr),
+           ATTN_ERR_SHAPE);
+    expect("noalloc empty", attn_sinks_decode_noalloc(1, 0, 8, 2, 64, 16, 8, 4, 64, at(F), at(F),
+                                                      at(F), ip(F), ip(F), nullptr, .125f, 0,
+                                                      at(F), nullptr),
+           ATTN_OK);
     expect("partials dtype", attn_sinks_decode_partials(0, 2, 8, 2, 64, 16, 8, 4, 64, at(F),
                                                         at(F), at(F), ip(F), ip(F), .125f, at(F),
                                                         big, nullptr),

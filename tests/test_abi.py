@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn_sinks.h")
 
 # status codes as the header defines them
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP, ERR_SCRATCH = range(8)
 
 
 def declared_functions():
@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(7):
+    for code in range(8):
         s = ga.attn_sinks_status_string(code)
         assert isinstance(s, str) and s
     assert ga.attn_sinks_status_string(99) == "unknown status"
@@ -382,3 +382,40 @@ def test_ragged_rejects(lib, kw, code):
 def test_ragged_noncausal_allows_more_rows_than_keys(lib):
     assert _ragged(lib, causal=0, mq=40, mk=30, B=0) == OK
     assert _ragged(lib, Tq=0, mq=0) == OK
+
+
+def _noalloc(lib, **kw):
+    args = dict(dtype=1, B=2, Hq=8, Hkv=2, d=64, P=16, pages=8, max_pages=4, max_len=64,
+                q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, sinks=None, scale=0.125, window=0,
+                out=FAKE)
+    args.update(kw)
+    return lib.attn_sinks_decode_noalloc(
+        args["dtype"], args["B"], args["Hq"], args["Hkv"], args["d"], args["P"], args["pages"],
+        args["max_pages"], args["max_len"], args["q"], args["k"], args["v"], args["bt"],
+        args["sl"], args["sinks"], ctypes.c_float(args["scale"]), args["window"], args["out"],
+        None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), ERR_UNSUPPORTED),
+    (dict(d=96), ERR_UNSUPPORTED),
+    (dict(Hkv=3), ERR_SHAPE),
+    (dict(max_len=65), ERR_SHAPE),
+    (dict(window=-1), ERR_SHAPE),
+    (dict(scale=float("nan")), ERR_SHAPE),
+    (dict(q=None), ERR_NULL),
+    (dict(out=FAKE + 8), ERR_ALIGN),
+    # more partial results than the fixed 32 MiB scratch holds
+    (dict(B=2000, Hq=64, Hkv=8, pages=1, max_pages=512, max_len=8192), ERR_SCRATCH),
+    (dict(B=0), OK),
+])
+def test_noalloc_rejects(lib, kw, code):
+    assert _noalloc(lib, **kw) == code
+
+
+def test_noalloc_limit_is_the_workspace_size(lib):
+    # the call takes exactly the sizes whose decode workspace fits 32 MiB
+    limit = 32 << 20
+    assert ga.attn_sinks_decode_workspace_bytes(1800, 64, 8, 64, 8192) <= limit
+    assert ga.attn_sinks_decode_workspace_bytes(700, 64, 4, 128, 32768) <= limit
+    assert ga.attn_sinks_decode_workspace_bytes(2000, 64, 8, 64, 8192) > limit
