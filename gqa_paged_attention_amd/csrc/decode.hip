@@ -182,44 +182,43 @@ __device__ __forceinline__ int k_swizzle(int r)
 
 // Load one 32-token block starting at token t0.  kFull: both slabs lie inside
 // the range (no branch, so the compiler can keep several blocks in flight).
-// Otherwise the second slab is loaded only when it holds a token < t_end.
+// Otherwise a slab is loaded only when it holds a token of [t_lo, t_end):
+// the second only when t0 + 16 < t_end, and the first only when t0 + 16 >
+// t_lo (under a sliding window the block that holds the oldest visible key
+// may begin with a whole page below the window, whose table entry is then
+// never read).  Slabs not loaded are zero.
 template <int D, bool kFull>
 __device__ __forceinline__ void load_block(Block<D> &blk, const uint16_t *__restrict__ kc,
                                            const uint16_t *__restrict__ vc,
                                            const int32_t *__restrict__ bt, int t0, int t_end,
-                                           int g, int num_kv_heads, int n, int lg)
+                                           int g, int num_kv_heads, int n, int lg, int t_lo = 0)
 {
     using VRow = typename VRowT<D>::type;
     constexpr size_t slab = 16 * D;
     const int lane = lg * 16 + n;
     const int pg = uniform(t0 >> 4);
-    const int page0 = load_scalar(bt, pg);
-    const size_t base0 = ((size_t)page0 * num_kv_heads + g) * slab;
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j)
-        blk.k[0][j] = __builtin_nontemporal_load((const u32x4_t *)(kc + base0 + (j * 64 + lane) * 8));
+    for (int s = 0; s < 2; ++s) {
+        const bool live = kFull || (s == 0 ? t0 + 16 > t_lo : t0 + 16 < t_end);
+        if (live) {
+            const int page = load_scalar(bt, pg + s);
+            const size_t base = ((size_t)page * num_kv_heads + g) * slab;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        blk.v[i] = __builtin_nontemporal_load(
-            (const VRow *)(vc + base0 + (4 * lg + i) * D + n * (D / 16)));
-    if (kFull || t0 + 16 < t_end) {
-        const int page1 = load_scalar(bt, pg + 1);
-        const size_t base1 = ((size_t)page1 * num_kv_heads + g) * slab;
+            for (int j = 0; j < D / 32; ++j)
+                blk.k[s][j] = __builtin_nontemporal_load(
+                    (const u32x4_t *)(kc + base + (j * 64 + lane) * 8));
 #pragma unroll
-        for (int j = 0; j < D / 32; ++j)
-            blk.k[1][j] =
-                __builtin_nontemporal_load((const u32x4_t *)(kc + base1 + (j * 64 + lane) * 8));
+            for (int i = 0; i < 4; ++i)
+                blk.v[4 * s + i] = __builtin_nontemporal_load(
+                    (const VRow *)(vc + base + (4 * lg + i) * D + n * (D / 16)));
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            blk.v[4 + i] = __builtin_nontemporal_load(
-                (const VRow *)(vc + base1 + (4 * lg + i) * D + n * (D / 16)));
-    } else {
+            for (int j = 0; j < D / 32; ++j)
+                blk.k[s][j] = u32x4_t{0, 0, 0, 0};
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-            blk.k[1][kk] = u32x4_t{0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            blk.v[4 + i] = VRow{};
+            for (int i = 0; i < 4; ++i)
+                blk.v[4 * s + i] = VRow{};
+        }
     }
 }
 
@@ -438,7 +437,7 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int row0, int b, i
         // the block that holds the oldest key of a sliding window
         Block<D> head;
         load_block<D, false>(head, a.k_cache, a.v_cache, bt, t_begin, t_end, g, a.num_kv_heads,
-                             n, lg);
+                             n, lg, t_lo);
         compute_block<D, NCB, true>(st, head, qop, t_begin, t_lo, t_end, col_end, a.scale_log2,
                                     lg, klds);
         t_begin += kUnitTokens;

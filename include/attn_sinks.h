@@ -227,6 +227,12 @@ int attn_sinks_prefill(int dtype, int num_seqs, int num_q_heads, int num_kv_head
  * KV head) over them and writes the output directly (the workspace is then
  * not touched).  Prefill with 0 < W < max_seq_len runs a kernel of its own in which each
  * wave streams the few blocks its rows need straight from the paged cache.
+ *
+ * Pages a window no longer reaches may be released: with W > 0, the page
+ * table entries of sequence b below entry (L_b - Lq_b - W + 1) / 16 (decode:
+ * (L_b - W) / 16; integer division, negative meaning none) are never read,
+ * nor the pages they name, so they may hold any value, invalid page ids
+ * included.  The fp32 path reads only the keys each row sees as well.
  */
 int attn_sinks_decode_window(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
                              int head_dim, int page_size, int num_pages, int max_pages_per_seq,

@@ -134,3 +134,57 @@ def test_full_gptoss_prefill_window128():
     note("full gpt-oss prefill, window 128 (sampled rows)")
     check_sampled(run_prefill(b, window=128), b, 3000, 5, "gpt-oss prefill window 128",
                   window=128)
+
+
+def _redirect_below(b, first_page):
+    """The batch with every table entry of sequence s below page first_page[s]
+    pointing at a spare (NaN-filled, never referenced) page: a cache that
+    has released the pages a window no longer reaches."""
+    used = set(b.block_table[b.block_table >= 0].tolist())
+    spare = next(p for p in range(b.k_cache.shape[0]) if p not in used)
+    assert torch.isnan(b.k_cache[spare].float()).all(), "spare pages hold NaN"
+    bt = b.block_table.clone()
+    moved = 0
+    for s, p in enumerate(first_page):
+        if p > 0:
+            bt[s, :p] = spare
+            moved += p
+    assert moved > 0
+    return replace(b, block_table=bt)
+
+
+WINDOW_PAGE_CASES = [
+    # id, seq_lens, Hq, Hkv, d, window: the oldest visible key of some
+    # sequence sits at offset >= 16 of its 32-token block, so that block
+    # begins with a page wholly below the window
+    ("d64_w80", [1000, 300, 2049, 97], 16, 2, 64, 80),
+    ("d64_w590_split", [2049, 1300, 3000], 16, 2, 64, 590),
+    ("d128_w100", [1000, 517, 2049], 32, 2, 128, 100),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_PAGE_CASES, ids=[c[0] for c in WINDOW_PAGE_CASES])
+def test_decode_window_reads_no_page_below_it(case):
+    name, L, Hq, Hkv, d, w = case
+    b = wl.small_batch(zlib.crc32(name.encode()) % 1000 + 29, "bf16", L, [1] * len(L), Hq, Hkv,
+                       d, sink_mode="normal")
+    assert any((l - w) % 32 >= 16 for l in L if l > w)
+    moved = _redirect_below(b, [max(l - w, 0) // 16 for l in L])
+    note(f"decode window {w}, pages below the window redirected, {name}: L={L} d={d}")
+    got = run_decode(moved, window=w)
+    compare(got, oracle_full(b, window=w), "bf16", f"decode {name}, released pages")
+    same = run_decode(b, window=w)
+    assert torch.equal(got.view(torch.int16), same.view(torch.int16))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_window_reads_no_page_below_it(d):
+    L, Lq, w = [1400, 700, 3000], [300, 200, 1000], 100
+    b = wl.small_batch(71 + d, "bf16", L, Lq, 16, 2, d, sink_mode="normal")
+    first = [max(l - lq - w + 1, 0) // 16 for l, lq in zip(L, Lq)]
+    moved = _redirect_below(b, first)
+    note(f"prefill window {w}, pages below every row's window redirected: L={L} Lq={Lq} d={d}")
+    got = run_prefill(moved, window=w)
+    compare(got, oracle_full(b, window=w), "bf16", f"prefill d={d}, released pages")
+    same = run_prefill(b, window=w)
+    assert torch.equal(got.view(torch.int16), same.view(torch.int16))
