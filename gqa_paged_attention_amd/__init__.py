@@ -79,6 +79,8 @@ def library():
     lib.attn_sinks_status_string.restype = ctypes.c_char_p
     lib.attn_sinks_version.argtypes = []
     lib.attn_sinks_version.restype = I
+    lib.attn_sinks_set_debug.argtypes = [I, I]
+    lib.attn_sinks_set_debug.restype = I
     _lib = lib
     return lib
 
@@ -89,6 +91,16 @@ def attn_sinks_status_string(status: int) -> str:
 
 def attn_sinks_version() -> int:
     return int(library().attn_sinks_version())
+
+
+ATTN_DEBUG_PREFILL_ONE_HEAD = 0
+ATTN_DEBUG_PREFILL_WAIT_ALL = 1
+
+
+def attn_sinks_set_debug(setting: int, value: int) -> int:
+    """Set a debug setting for the launches that follow; returns the previous
+    value (-1: unknown setting).  Every setting gives the same results."""
+    return int(library().attn_sinks_set_debug(int(setting), int(value)))
 
 
 def attn_sinks_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,

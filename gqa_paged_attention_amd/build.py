@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -46,12 +47,40 @@ COMMON_FLAGS = [
 ]
 
 
+# Kernels whose waits for their direct global-to-LDS tile loads are counted
+# by hand (s_waitcnt vmcnt(N) leaves the next tile's loads in flight): that
+# count is right only while those loads are the wave's only vector-memory
+# operations in the loop, so a register spill (scratch traffic) there would
+# let a wave read an LDS stage before it lands.  The build refuses them with
+# any scratch.
+NO_SCRATCH_KERNELS = ("prefill_bf16I",)
+
+
+def check_no_scratch(remarks: str, src: str) -> None:
+    """Parse -Rpass-analysis=kernel-resource-usage remarks; raise if a kernel
+    of NO_SCRATCH_KERNELS uses scratch."""
+    name = None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and any(k in name for k in NO_SCRATCH_KERNELS) and int(m.group(1)):
+            raise RuntimeError(
+                f"{src}: kernel {name} uses {m.group(1)} bytes/lane of scratch; its hand-counted "
+                "waits for the direct tile loads assume no other vector-memory operation in its "
+                "loop (reduce its register use)")
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    check_no_scratch(res.stderr, src)
     return obj
 
 

@@ -4,10 +4,12 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cstddef>
 #include <cmath>
 #include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 #include "kernels.h"
@@ -52,6 +54,20 @@ int heads_override()
         value = env_int("ATTN_SINKS_DECODE_HEADS_PER_WG", 1, attn::kDecodeMaxHeadsPerWg);
     });
     return value;
+}
+
+// Debug settings: environment defaults read once, then attn_sinks_set_debug.
+std::atomic<int> g_debug[attn::kDebugSettings];
+std::once_flag g_debug_once;
+
+void debug_init()
+{
+    std::call_once(g_debug_once, [] {
+        const char *k = std::getenv("ATTN_SINKS_PREFILL_ONE_HEAD");
+        g_debug[attn::kDebugPrefillOneHead] = (k && std::strcmp(k, "1") == 0) ? 1 : 0;
+        const char *w = std::getenv("ATTN_SINKS_PREFILL_WAIT_ALL");
+        g_debug[attn::kDebugPrefillWaitAll] = (w && std::strcmp(w, "1") == 0) ? 1 : 0;
+    });
 }
 
 struct DecodeShape {
@@ -287,6 +303,12 @@ int scratch_address(void **ptr)
 }
 
 }  // namespace
+
+int attn::debug_setting(int id)
+{
+    debug_init();
+    return (id >= 0 && id < attn::kDebugSettings) ? g_debug[id].load() : 0;
+}
 
 extern "C" {
 
@@ -778,5 +800,13 @@ const char *attn_sinks_status_string(int status)
 }
 
 int attn_sinks_version(void) { return kVersion; }
+
+int attn_sinks_set_debug(int setting, int value)
+{
+    if (setting < 0 || setting >= attn::kDebugSettings)
+        return -1;
+    debug_init();
+    return g_debug[setting].exchange(value != 0 ? 1 : 0);
+}
 
 }  // extern "C"

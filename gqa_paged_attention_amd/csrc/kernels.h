@@ -45,6 +45,16 @@ struct PrefillLaunch {
     hipStream_t stream;
 };
 
+// Debug settings (attn_sinks_set_debug; environment defaults read once):
+// kDebugPrefillOneHead gives every prefill workgroup one query head where it
+// would take four (ATTN_SINKS_PREFILL_ONE_HEAD=1), kDebugPrefillWaitAll makes
+// the prefill tile waits take every load in flight
+// (ATTN_SINKS_PREFILL_WAIT_ALL=1).  Every setting gives the same results.
+constexpr int kDebugPrefillOneHead = 0;
+constexpr int kDebugPrefillWaitAll = 1;
+constexpr int kDebugSettings = 2;
+int debug_setting(int id);
+
 // The most packed query rows (G times query tokens per sequence) the
 // multi-token decode takes per KV head (in layers of up to 64 rows at d = 64
 // and of 32 at d = 128); beyond that the prefill kernel runs.

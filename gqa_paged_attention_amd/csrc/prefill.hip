@@ -201,32 +201,33 @@ struct Smem {
     }
 };
 
-// Per-lane parts of this wave's direct loads (constant over tiles).  The wave
-// loads 1 KiB chunks j = wave + 4i (i < kChunksPerWave) of each K and V tile;
-// chunk j holds
+// Per-lane parts of this wave's direct loads (constant over tiles).  With NW
+// waves sharing the loads, the wave loads 1 KiB chunks j = wave + NW i
+// (i < kChunks / NW) of each K and V tile; chunk j holds
 // key rows R*j .. R*j+R-1 (R = 1024 / (2 d)), all inside one 16-token page,
 // and lane l fetches the 16-byte chunk that belongs in slot l % (d/8) of row
 // R*j + l / (d/8) of the swizzled tile.
-template <int D>
+template <int D, int NW = kWaves>
 struct LoadLanes {
-    int key[Cfg<D>::kChunksPerWave];  // key of this lane's row within the tile, per chunk
-    int kc[Cfg<D>::kChunksPerWave];   // K chunk (elements) within the row
-    int vc[Cfg<D>::kChunksPerWave];   // V chunk (elements) within the row
+    static constexpr int kPer = Cfg<D>::kChunks / NW;  // chunks per wave and tensor
+    int key[kPer];  // key of this lane's row within the tile, per chunk
+    int kc[kPer];   // K chunk (elements) within the row
+    int vc[kPer];   // V chunk (elements) within the row
     // byte offsets of this lane's K and V chunks in a tile that lies wholly
     // inside the sequence: from the chunk's page slab (paged), or from the
     // tile's first key row (contiguous rows kv_stride apart)
-    uint32_t ko[Cfg<D>::kChunksPerWave], vo[Cfg<D>::kChunksPerWave];
+    uint32_t ko[kPer], vo[kPer];
 };
 
-template <int D, bool kContig>
-__device__ __forceinline__ LoadLanes<D> load_lanes(int wave, int lane, int kv_stride)
+template <int D, bool kContig, int NW = kWaves>
+__device__ __forceinline__ LoadLanes<D, NW> load_lanes(int wave, int lane, int kv_stride)
 {
     using C = Cfg<D>;
     constexpr int kChunks = D / 8;  // 16-byte chunks per key row
-    LoadLanes<D> ll;
+    LoadLanes<D, NW> ll;
 #pragma unroll
-    for (int i = 0; i < C::kChunksPerWave; ++i) {
-        const int j = wave + kWaves * i;
+    for (int i = 0; i < LoadLanes<D, NW>::kPer; ++i) {
+        const int j = wave + NW * i;
         const int key = C::kRowsPerLoad * j + lane / kChunks;
         const int slot = lane % kChunks;
         ll.key[i] = key;
@@ -255,7 +256,7 @@ __device__ __forceinline__ void dma16(const uint16_t *gbase, uint32_t voff, cons
                  : "memory");
 }
 
-// Page ids of this wave's load chunks of tile t (chunk j = wave + 4i starts
+// Page ids of this wave's load chunks of tile t (chunk j = wave + NW i starts
 // at key t*BN + R*j).  Page indices past the sequence's last page are
 // clamped to it.  Read one tile before the loads that use them, so that the
 // scalar-load latency stays off the tile start.
@@ -263,7 +264,7 @@ struct ChunkPages {
     int p[2];
 };
 
-template <int D>
+template <int D, int NW = kWaves>
 __device__ __forceinline__ ChunkPages chunk_pages(const int32_t *__restrict__ bt, int t,
                                                   int last_page, int wave)
 {
@@ -271,9 +272,9 @@ __device__ __forceinline__ ChunkPages chunk_pages(const int32_t *__restrict__ bt
     ChunkPages cp;
     cp.p[1] = 0;
 #pragma unroll
-    for (int i = 0; i < C::kChunksPerWave; ++i)
+    for (int i = 0; i < LoadLanes<D, NW>::kPer; ++i)
         cp.p[i] = load_scalar(
-            bt, min((t * C::kBN + C::kRowsPerLoad * (wave + kWaves * i)) >> 4, last_page));
+            bt, min((t * C::kBN + C::kRowsPerLoad * (wave + NW * i)) >> 4, last_page));
     return cp;
 }
 
@@ -285,18 +286,19 @@ __device__ __forceinline__ ChunkPages chunk_pages(const int32_t *__restrict__ bt
 // offset of the sequence's key 0 for this KV head (the 16-byte chunks of one
 // load then come from R rows kv_stride apart).  Paged: kv_off is the head's
 // offset inside a page (g * 16 * d).
-template <int D, bool kContig>
+template <int D, bool kContig, int NW = kWaves>
 __device__ __forceinline__ void load_tile(const Smem<D> &sm, const PrefillArgs &a, const ChunkPages &cp,
                                           int t, int L, size_t kv_off, int wave,
-                                          const LoadLanes<D> &ll)
+                                          const LoadLanes<D, NW> &ll)
 {
     using C = Cfg<D>;
+    constexpr int kPer = LoadLanes<D, NW>::kPer;
     const int kv0 = t * C::kBN;
     const int stage = t % C::kStages;
     if (kv0 + C::kBN <= L) {
 #pragma unroll
-        for (int i = 0; i < C::kChunksPerWave; ++i) {
-            const int j = wave + kWaves * i;
+        for (int i = 0; i < kPer; ++i) {
+            const int j = wave + NW * i;
             const size_t base = kContig ? kv_off + (size_t)kv0 * a.kv_stride
                                         : (size_t)cp.p[i] * a.num_kv_heads * 16 * D + kv_off;
             dma16(a.k_cache + base, ll.ko[i], sm.k(stage) + 512 * j);
@@ -305,8 +307,8 @@ __device__ __forceinline__ void load_tile(const Smem<D> &sm, const PrefillArgs &
         return;
     }
 #pragma unroll
-    for (int i = 0; i < C::kChunksPerWave; ++i) {
-        const int j = wave + kWaves * i;
+    for (int i = 0; i < kPer; ++i) {
+        const int j = wave + NW * i;
         if constexpr (kContig) {
             const int tok = min(kv0 + ll.key[i], L - 1);
             const uint32_t row = (uint32_t)tok * (uint32_t)a.kv_stride;
@@ -609,20 +611,25 @@ struct RawBlock {
 
 // k0 is a multiple of 32, so a block spans two pages, whose ids the wave
 // reads once (scalar loads); chunk i lies on the first when i < kPer / 2.
+// k_lo: the oldest key any row of the wave sees.  When the block's first page
+// lies wholly below it (a sliding window), that page's table entry is not
+// read and its chunks are zero (every row masks those keys).
 template <int D, bool kContig = false>
 __device__ __forceinline__ void fetch_block(RawBlock<D> &rb, const PrefillArgs &a,
                                             const int32_t *__restrict__ bt, int L,
-                                            size_t kv_off, int k0, int lane)
+                                            size_t kv_off, int k0, int lane, int k_lo = 0)
 {
     constexpr int kChunks = D / 8;
     constexpr int kPer = RawBlock<D>::kPer;
     static_assert(kPer % 2 == 0, "half of the chunks on each page");
+    const bool first_live = kContig || k0 + 16 > k_lo;
     size_t slab[2] = {0, 0};  // element offsets of the two pages' head slabs
     if constexpr (!kContig) {
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-            slab[s] = (size_t)load_scalar(bt, min(k0 + 16 * s, L - 1) >> 4) * a.num_kv_heads *
-                          16 * D + kv_off;
+            if (s == 1 || first_live)
+                slab[s] = (size_t)load_scalar(bt, min(k0 + 16 * s, L - 1) >> 4) *
+                              a.num_kv_heads * 16 * D + kv_off;
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -634,8 +641,12 @@ __device__ __forceinline__ void fetch_block(RawBlock<D> &rb, const PrefillArgs &
             off = kv_off + (size_t)tok * a.kv_stride + 8 * chunk;
         else
             off = slab[i < kPer / 2 ? 0 : 1] + (size_t)(tok & 15) * D + 8 * chunk;
-        rb.k[i] = *(const u32x4_t *)(a.k_cache + off);
-        rb.v[i] = *(const u32x4_t *)(a.v_cache + off);
+        if (i < kPer / 2 && !first_live) {
+            rb.k[i] = rb.v[i] = u32x4_t{0, 0, 0, 0};
+        } else {
+            rb.k[i] = *(const u32x4_t *)(a.k_cache + off);
+            rb.v[i] = *(const u32x4_t *)(a.v_cache + off);
+        }
     }
 }
 
@@ -765,16 +776,19 @@ __device__ void exact_rows(WaveState<D> &w, uint16_t *lds_wave, const PrefillArg
     }
 }
 
-// Workgroup -> (sequence, KV head, query head, query tile): all workgroups of
-// one (sequence, KV head) land on one XCD (workgroups are dispatched to XCDs
-// round-robin), heaviest query tiles first.
+// Workgroup -> (sequence, KV head, first query head, query tile): all
+// workgroups of one (sequence, KV head) land on one XCD (workgroups are
+// dispatched to XCDs round-robin), heaviest query tiles first.  A workgroup
+// takes HPW consecutive query heads of the KV head.
 struct TileCoords {
     int b, g, h, qt;
 };
 
+template <int HPW>
 __device__ __forceinline__ TileCoords tile_of(const PrefillArgs &a)
 {
-    const int per_group = a.group * a.num_q_tiles;
+    const int hgroups = a.group / HPW;
+    const int per_group = hgroups * a.num_q_tiles;
     const int id = blockIdx.x;
     int grp, r;
     const int main_ids = a.xcd_groups * per_group;
@@ -789,8 +803,8 @@ __device__ __forceinline__ TileCoords tile_of(const PrefillArgs &a)
     TileCoords tc;
     tc.b = grp / a.num_kv_heads;
     tc.g = grp % a.num_kv_heads;
-    tc.qt = a.num_q_tiles - 1 - r / a.group;
-    tc.h = tc.g * a.group + r % a.group;
+    tc.qt = a.num_q_tiles - 1 - r / hgroups;
+    tc.h = tc.g * a.group + HPW * (r % hgroups);
     return tc;
 }
 
@@ -877,23 +891,33 @@ __device__ __forceinline__ void store_rows(const WaveState<D> &w, uint16_t *stag
 }
 
 // kContig: ragged cache-free attention over contiguous K/V rows (with or
-// without the causal mask); otherwise the paged cache.
-template <int D, bool kContig>
+// without the causal mask); otherwise the paged cache.  kWaitAll: the tile
+// waits take every load of the wave (vmcnt(0)) instead of leaving the next
+// tile's in flight (a debug setting; same results).  HPW: query heads per
+// workgroup.  With HPW = 1 the 4 waves take consecutive row blocks of one
+// head (BM rows); with HPW = 4 they take the same 32 NRB rows of 4 heads of
+// one KV head, so every wave sees the same keys, masks and block count (no
+// wave waits at the tile barriers for the others' extra diagonal blocks) and
+// the causal range of a workgroup's tiles is 4 times finer.
+template <int D, bool kContig, bool kWaitAll, int HPW>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
 {
     using C = Cfg<D>;
     constexpr int NRB = C::kNRB;
-    const TileCoords tc = tile_of(a);
-    const int b = tc.b, g = tc.g, h = tc.h, qt = tc.qt;
+    constexpr int kWavesPerHead = kWaves / HPW;
+    constexpr int kRowsPerWg = 32 * NRB * kWavesPerHead;
+    const TileCoords tc = tile_of<HPW>(a);
+    const int b = tc.b, g = tc.g, qt = tc.qt;
 
     const int q0 = a.cu_seqlens_q[b];
     const int q_len = a.cu_seqlens_q[b + 1] - q0;
-    const int row0 = qt * C::kBM;
+    const int row0 = qt * kRowsPerWg;
     if (row0 >= q_len)
         return;  // uniform over the workgroup
     const int kv_first = kContig ? a.cu_seqlens_kv[b] : 0;
     const int L = kContig ? a.cu_seqlens_kv[b + 1] - kv_first : a.seq_lens[b];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = tc.h + wave / kWavesPerHead;
     const int lane = threadIdx.x & 63;
     const int r32 = lane & 31, half = lane >> 5;
     // Position of query row i: shift + i (causal, aligned to the end of the
@@ -905,10 +929,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     const int rbs = 32 * row_step;  // position step between row blocks
 
     // this wave's rows: row_w + 32 rb + r32
-    const int row_w = row0 + 32 * NRB * wave;
+    const int row_w = row0 + 32 * NRB * (wave % kWavesPerHead);
 
     // keys needed by the workgroup (tiles) and by this wave (blocks)
-    const int last_row = min(row0 + C::kBM, q_len) - 1;
+    const int last_row = min(row0 + kRowsPerWg, q_len) - 1;
     const int kv_end = causal ? min(shift + last_row + 1, L) : L;
     const int ntiles = (kv_end + C::kBN - 1) / C::kBN;
     const int wave_last = min(row_w + 32 * NRB - 1, q_len - 1);
@@ -960,7 +984,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
         if ((step + 1) % C::kBPT == 0) {
             const int t = (step + 1) / C::kBPT;
             if (t < ntiles) {
-                wait_loads_and_sync<2 * C::kChunksPerWave>(t + 1 >= ntiles);
+                wait_loads_and_sync<2 * C::kChunksPerWave>(kWaitAll || t + 1 >= ntiles);
                 if (t + 2 < ntiles) {
                     load_tile<D, kContig>(sm, a, next_pages, t + 2, L, kv_off, wave, ll);
                     next_pages = pages(t + 3);
@@ -1119,7 +1143,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_window_bf16(PrefillArgs a
 {
     using C = Cfg<D>;
     constexpr int NRB = C::kNRB;
-    const TileCoords tc = tile_of(a);
+    const TileCoords tc = tile_of<1>(a);
     const int q0 = a.cu_seqlens_q[tc.b];
     const int q_len = a.cu_seqlens_q[tc.b + 1] - q0;
     const int row0 = tc.qt * C::kBM;
@@ -1134,7 +1158,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_window_bf16(PrefillArgs a
     const int wpf = shift + row_w;  // position of the wave's first row
     const int wave_last = min(row_w + 32 * NRB - 1, q_len - 1);
     const int nb = row_w < q_len ? (min(shift + wave_last + 1, L) + kKB - 1) / kKB : 0;
-    const int b_lo = max(wpf - a.window + 1, 0) / kKB;
+    const int b_lo = max(wpf - a.window + 1, 0) / kKB;  // the block of the oldest key
 
     extern __shared__ __align__(16) uint16_t lds[];
     uint16_t *kt = lds + wave * (2 * kKB * D);
@@ -1151,15 +1175,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_window_bf16(PrefillArgs a
     // each block is fetched when its turn comes)
     constexpr bool kAhead = D == 64;
     RawBlock<D> raw;
+    const int k_lo = max(wpf - a.window + 1, 0);  // the oldest key a row of the wave sees
     if (kAhead && b_lo < nb)
-        fetch_block<D>(raw, a, bt, L, head_off, kKB * b_lo, lane);
+        fetch_block<D>(raw, a, bt, L, head_off, kKB * b_lo, lane, k_lo);
     for (int blk = b_lo; blk < nb; ++blk) {
         const int k0 = kKB * blk;
         if (!kAhead)
-            fetch_block<D>(raw, a, bt, L, head_off, k0, lane);
+            fetch_block<D>(raw, a, bt, L, head_off, k0, lane, k_lo);
         stash_block<D>(raw, kt, vt, lane);
         if (kAhead && blk + 1 < nb)
-            fetch_block<D>(raw, a, bt, L, head_off, k0 + kKB, lane);
+            fetch_block<D>(raw, a, bt, L, head_off, k0 + kKB, lane, k_lo);
         window_block<D>(w, kt, vt, thr - k0, a.window, k0, wpf, a.scale_log2, lane);
     }
     // the staging area of the epilogue is the wave's own K tile and more:
@@ -1169,6 +1194,41 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_window_bf16(PrefillArgs a
 
 template <int D>
 constexpr int kWindowLdsBytes = kWaves * 2 * kKB * D * 2;
+
+bool prefill_one_head() { return debug_setting(kDebugPrefillOneHead) != 0; }
+bool prefill_wait_all() { return debug_setting(kDebugPrefillWaitAll) != 0; }
+
+// more than 64 KiB of LDS (d = 128) has to be allowed once per kernel
+template <int D, bool kContig, bool kWaitAll, int HPW>
+hipError_t launch_causal(const PrefillArgs &a, long long wgs, hipStream_t stream)
+{
+    constexpr int kLds = Cfg<D>::kLdsBytes;
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void *)prefill_bf16<D, kContig, kWaitAll, HPW>,
+        hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (attr != hipSuccess)
+        return attr;
+    hipLaunchKernelGGL((prefill_bf16<D, kContig, kWaitAll, HPW>), dim3((unsigned)wgs),
+                       dim3(kThreads), kLds, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, int HPW>
+hipError_t launch_causal_hpw(PrefillArgs a, const PrefillLaunch &p)
+{
+    constexpr int kRows = 32 * Cfg<D>::kNRB * (kWaves / HPW);
+    a.num_q_tiles = (p.max_q_len + kRows - 1) / kRows;
+    const long long wgs =
+        (long long)p.num_seqs * p.num_kv_heads * (a.group / HPW) * a.num_q_tiles;
+    if (wgs > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    const bool contig = p.cu_seqlens_kv != nullptr, wait_all = prefill_wait_all();
+    if (contig)
+        return wait_all ? launch_causal<D, true, true, HPW>(a, wgs, p.stream)
+                        : launch_causal<D, true, false, HPW>(a, wgs, p.stream);
+    return wait_all ? launch_causal<D, false, true, HPW>(a, wgs, p.stream)
+                    : launch_causal<D, false, false, HPW>(a, wgs, p.stream);
+}
 
 template <int D>
 hipError_t launch_d(const PrefillLaunch &p)
@@ -1212,25 +1272,10 @@ hipError_t launch_d(const PrefillLaunch &p)
                            kWindowLdsBytes<D>, p.stream, a);
         return hipGetLastError();
     }
-    // more than 64 KiB of LDS (d = 128) has to be allowed once per kernel
-    if (p.cu_seqlens_kv) {
-        static const hipError_t cattr = hipFuncSetAttribute(
-            (const void *)prefill_bf16<D, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-            C::kLdsBytes);
-        if (cattr != hipSuccess)
-            return cattr;
-        hipLaunchKernelGGL((prefill_bf16<D, true>), dim3((unsigned)wgs), dim3(kThreads),
-                           C::kLdsBytes, p.stream, a);
-        return hipGetLastError();
-    }
-    static const hipError_t attr = hipFuncSetAttribute(
-        (const void *)prefill_bf16<D, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-        C::kLdsBytes);
-    if (attr != hipSuccess)
-        return attr;
-    hipLaunchKernelGGL((prefill_bf16<D, false>), dim3((unsigned)wgs), dim3(kThreads),
-                       C::kLdsBytes, p.stream, a);
-    return hipGetLastError();
+    // four query heads per workgroup where the group allows it (d = 64)
+    if (D == 64 && a.group % 4 == 0 && !prefill_one_head())
+        return launch_causal_hpw<D, 4>(a, p);
+    return launch_causal_hpw<D, 1>(a, p);
 }
 
 }  // namespace

@@ -455,6 +455,28 @@ int attn_sinks_ragged(int dtype, int num_seqs, int num_q_heads, int num_kv_heads
 /* Static English text for a status code (never NULL). */
 const char *attn_sinks_status_string(int status);
 
+/*
+ * Debug settings, for diagnostics and tests; every setting gives the same
+ * results, bit for bit.  Defaults come from the environment, read once:
+ *   ATTN_DEBUG_PREFILL_ONE_HEAD  bf16 causal prefill at head_dim 64 with a
+ *                                group size divisible by 4 gives each
+ *                                workgroup one query head (256 rows) instead
+ *                                of four (64 rows each)
+ *                                (ATTN_SINKS_PREFILL_ONE_HEAD=1)
+ *   ATTN_DEBUG_PREFILL_WAIT_ALL  the prefill's waits for its direct K/V tile
+ *                                loads take every load in flight instead of
+ *                                leaving the next tile's loads outstanding
+ *                                (ATTN_SINKS_PREFILL_WAIT_ALL=1)
+ * attn_sinks_set_debug sets one (value 0 or nonzero) for the launches that
+ * follow and returns its previous value, or -1 for an unknown setting.  Not
+ * meant to be changed while other threads enqueue calls.
+ */
+enum attn_debug_setting {
+    ATTN_DEBUG_PREFILL_ONE_HEAD = 0,
+    ATTN_DEBUG_PREFILL_WAIT_ALL = 1
+};
+int attn_sinks_set_debug(int setting, int value);
+
 /* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
 int attn_sinks_version(void);
 

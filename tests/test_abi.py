@@ -419,3 +419,14 @@ def test_noalloc_limit_is_the_workspace_size(lib):
     assert ga.attn_sinks_decode_workspace_bytes(1800, 64, 8, 64, 8192) <= limit
     assert ga.attn_sinks_decode_workspace_bytes(700, 64, 4, 128, 32768) <= limit
     assert ga.attn_sinks_decode_workspace_bytes(2000, 64, 8, 64, 8192) > limit
+
+
+def test_debug_settings(lib):
+    # set returns the previous value; unknown settings give -1 and change nothing
+    for s in (ga.ATTN_DEBUG_PREFILL_ONE_HEAD, ga.ATTN_DEBUG_PREFILL_WAIT_ALL):
+        before = ga.attn_sinks_set_debug(s, 1)
+        assert before in (0, 1)
+        assert ga.attn_sinks_set_debug(s, 0) == 1
+        assert ga.attn_sinks_set_debug(s, before) == 0
+    assert ga.attn_sinks_set_debug(2, 1) == -1
+    assert ga.attn_sinks_set_debug(-1, 1) == -1
