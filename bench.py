@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of paged GQA attention with per-head sinks on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode|all|next]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--only all|decode|prefill|mixed|next|qwen]
 
 One step is one decode pass (split pass + merge pass) of the gpt-oss-20b-shaped
 decode workload: 64 sequences x 1 query token, 64 q / 8 KV heads, head_dim 64,
@@ -12,16 +13,18 @@ timed events.  The headline value is decode KV-read GB/s; the same line also
 carries the causal prefill (TFLOP/s), the Qwen3-235B-shaped decode, the
 mixed batch and the sliding-window, multi-token, ragged, KV-append and
 RoPE-append legs, each against its own roofline, plus the fp64 CPU oracle
-timed on the host cores (a baseline, not a target).  The RoPE-append leg
+timed on the host cores (a baseline, not a target).  Every leg reports the
+mean step time with the median and minimum beside it.  The RoPE-append leg
 rotates the same q in place every step: its values drift, its work does not.
 
 Modes used to make the committed profiles:
-    --profile-run            every leg but the mixed batch and the Qwen decode,
-                             no oracle (run under rocprofv3); with --only next
-                             the same
+    --profile-run            the selected legs (--only; default every leg),
+                             no oracle, no warm pass (run under rocprofv3)
     --summarize-trace DIR NAME              kernel durations -> profiles/NAME.txt
     --summarize-traffic FDIR WDIR KERNEL NAME
                                             FETCH/WRITE_SIZE -> HBM bytes per launch
+    --summarize-counters DIR KERNEL NAME    any --pmc counters -> per-dispatch
+                                            averages and derived busy fractions
 """
 from __future__ import annotations
 
@@ -42,7 +45,17 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, TFLOP/s (256 CU x 2.4 GHz x 4096)
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "decode_split_bf16_gptoss_decode_traffic.txt")
+PREFILL_TRAFFIC_FILE = os.path.join(PROFILES, "prefill_bf16_gptoss_prefill_traffic.txt")
+PREFILL_COUNTER_FILE = os.path.join(PROFILES, "prefill_bf16_gptoss_prefill_counters.txt")
 DECODE_SOURCES = ["gqa_paged_attention_amd/csrc/decode.hip", "gqa_paged_attention_amd/csrc/common.h"]
+PREFILL_SOURCES = ["gqa_paged_attention_amd/csrc/prefill.hip",
+                   "gqa_paged_attention_amd/csrc/common.h"]
+
+
+def kernel_sources(kernel: str):
+    """The source files a profiled kernel is built from (for the hash that
+    ties a committed counter summary to the code it measured)."""
+    return PREFILL_SOURCES if "prefill" in kernel else DECODE_SOURCES
 
 
 def log(*a):
@@ -162,8 +175,37 @@ class Timer:
         return {"stage_ms": {k: sum(v) / len(v) for k, v in per_stage.items()},
                 "stage_ms_min": {k: min(v) for k, v in per_stage.items()},
                 "step_ms": sum(totals) / len(totals),
-                "step_ms_median": sorted(totals)[len(totals) // 2],
+                "step_ms_median": _median(totals),
+                "step_ms_min": min(totals),
                 "wall_s": walls[0]}
+
+
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def spread(r) -> dict:
+    """Median and minimum step time beside the mean (ms)."""
+    return {"ms_median": round(r["step_ms_median"], 4), "ms_min": round(r["step_ms_min"], 4)}
+
+
+class leg_range:
+    """A named range around one leg (roctx through torch), so that a
+    rocprofv3 --marker-trace run can attribute each kernel dispatch to its
+    leg; the GPU is synchronised before the range closes."""
+
+    def __init__(self, torch, name):
+        self.torch, self.name = torch, name
+
+    def __enter__(self):
+        self.torch.cuda.synchronize()
+        self.torch.cuda.nvtx.range_push(self.name)
+
+    def __exit__(self, *exc):
+        self.torch.cuda.synchronize()
+        self.torch.cuda.nvtx.range_pop()
 
 
 # --------------------------------------------------------------- workloads
@@ -198,6 +240,7 @@ def bench_decode(torch, ga, timer, batch_cpu, steps, warmup, label, with_warm=Tr
         "workload": label,
         "algorithmic_bytes": nbytes,
         "ms": round(cold["step_ms"], 4),
+        **spread(cold),
         "GB_per_s": round(gbs, 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "split_ms": round(cold["stage_ms"]["decode_split"], 4),
@@ -219,7 +262,8 @@ def bench_prefill(torch, ga, timer, batch_cpu, steps, warmup, label):
     flops = prefill_flops(batch_cpu)
     tf = flops / (r["step_ms"] * 1e-3) / 1e12
     return {"workload": label, "algorithmic_flops": flops, "ms": round(r["step_ms"], 4),
-            "TFLOP_per_s": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}, out
+            **spread(r), "TFLOP_per_s": round(tf, 1),
+            "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}, out
 
 
 def bench_window(torch, ga, timer, steps, warmup, wl, window=128):
@@ -380,24 +424,37 @@ def bench_ragged(torch, ga, timer, steps, warmup, wl):
 
 
 def bench_mixed(torch, ga, timer, steps, warmup, wl):
+    """The mixed batch: the decode rows (split + merge) and the two prefill
+    chunks, one after the other on one stream.  The decode half and the
+    prefill half are each timed on their own as well as the whole step, with
+    events only around what is timed (none between its launches)."""
     full, dec, pre = wl.mixed(0)
     gd, gp = dec.to("cuda"), pre.to("cuda")
     out_d, out_p = torch.empty_like(gd.q), torch.empty_like(gp.q)
     ws = decode_workspace(torch, ga, gd)
-    stages = decode_stages(ga, gd, out_d, ws) + [("prefill", lambda: ga.attn_sinks_prefill(
+    dstages = decode_stages(ga, gd, out_d, ws)
+    pstage = [("prefill", lambda: ga.attn_sinks_prefill(
         gp.q, gp.k_cache, gp.v_cache, gp.block_table, gp.seq_lens, gp.cu_seqlens_q, gp.sinks,
         gp.scale, out_p, pre.max_q_len, pre.max_seq_len))]
-    r = timer.run(stages, steps, warmup, flush=True)
+    rd = timer.run(dstages, steps, warmup, flush=True)
+    rp = timer.run(pstage, steps, warmup, flush=True)
+    r = timer.run(dstages + pstage, steps, warmup, flush=True)
     nb, fl = decode_bytes(dec), prefill_flops(pre)
-    dec_ms = r["stage_ms"]["decode_split"] + r["stage_ms"]["decode_merge"]
+    dec_ms, pre_ms = rd["step_ms"], rp["step_ms"]
     bound_ms = (nb / (HBM_PEAK_GBS * 1e9) + fl / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
     return {"workload": "mixed: 32 decode seqs (ctx U[2048,16384]) + 2 prefill chunks of 2048 "
                         "on 8192-token prefixes, 64/8 heads, d=64, bf16, sinks N(0,2)",
-            "ms": round(r["step_ms"], 4),
+            "ms": round(r["step_ms"], 4), **spread(r),
             "decode_ms": round(dec_ms, 4),
+            "decode_split_ms": round(rd["stage_ms"]["decode_split"], 4),
+            "decode_merge_ms": round(rd["stage_ms"]["decode_merge"], 4),
+            "decode_algorithmic_bytes": nb,
             "decode_GB_per_s": round(nb / (dec_ms * 1e-3) / 1e9, 1),
-            "prefill_ms": round(r["stage_ms"]["prefill"], 4),
-            "prefill_TFLOP_per_s": round(fl / (r["stage_ms"]["prefill"] * 1e-3) / 1e12, 1),
+            "decode_hbm_frac": round(nb / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "prefill_ms": round(pre_ms, 4),
+            "prefill_algorithmic_flops": fl,
+            "prefill_TFLOP_per_s": round(fl / (pre_ms * 1e-3) / 1e12, 1),
+            "prefill_mfma_frac": round(fl / (pre_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "serial_bound_ms": round(bound_ms, 4),
             "frac_of_serial_bound": round(bound_ms / r["step_ms"], 4)}
 
@@ -445,21 +502,30 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def read_traffic():
-    """HBM traffic per split-pass launch from the committed counter summary,
-    or None when the summary is missing or the kernel changed since."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
+def _summary_fields(path):
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != source_hash(DECODE_SOURCES):
+    return kv
+
+
+def read_traffic(path, sources):
+    """HBM traffic per launch from a committed counter summary, or None when
+    the summary is missing or the kernel's sources changed since."""
+    return read_counter(path, sources, "traffic_bytes_per_launch")
+
+
+def read_counter(path, sources, field):
+    if not os.path.exists(path):
+        return None
+    kv = _summary_fields(path)
+    if kv.get("kernel_source_sha256_16") != source_hash(sources):
         return None
     try:
-        return float(kv["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
+        return float(kv[field].split()[0])
+    except (KeyError, ValueError, IndexError):
         return None
 
 
@@ -512,6 +578,28 @@ def summarize_trace(outdir: str, name: str, command: str):
             k, gx, gy, gz, bx, vg, ag, sc, lds = key
             lines.append(f"{k} | {gx}x{gy}x{gz} | {bx} | {vg} | {ag} | {sc} | {lds} | "
                          f"{len(ds)} | {sum(ds) / len(ds):.2f} | {min(ds):.2f}")
+    markers = glob.glob(os.path.join(outdir, "**", "*marker_api_trace.csv"), recursive=True)
+    if hits and markers:
+        # each dispatch attributed to the leg range (bench.py leg_range) that
+        # holds its start
+        ranges = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Message"])
+                  for r in _read_csv(markers[0]) if r.get("Message")]
+        legs = {}
+        for r in _read_csv(hits[0]):
+            t0 = int(r["Start_Timestamp"])
+            leg = next((m for a, b, m in ranges if a <= t0 <= b), None)
+            if leg is None or "FillFunctor" in r["Kernel_Name"] or "copyBuffer" in r["Kernel_Name"]:
+                continue
+            key = (leg, _short(r["Kernel_Name"]), r["Grid_Size_X"], r["Grid_Size_Y"],
+                   r["Grid_Size_Z"])
+            legs.setdefault(key, []).append((int(r["End_Timestamp"]) - t0) / 1e3)
+        lines += ["", "by leg (bench.py leg ranges; flush fills and copies left out):",
+                  "leg | kernel | grid (threads) | calls | avg_us | median_us | min_us"]
+        for key, ds in legs.items():
+            leg, k, gx, gy, gz = key
+            ds = sorted(ds)
+            lines.append(f"{leg} | {k} | {gx}x{gy}x{gz} | {len(ds)} | {sum(ds) / len(ds):.2f} | "
+                         f"{ds[len(ds) // 2]:.2f} | {ds[0]:.2f}")
     _write_profile(name, lines)
 
 
@@ -535,7 +623,7 @@ def summarize_traffic(fetch_dir: str, write_dir: str, kernel: str, name: str, co
     traffic = (fetch[0] * fetch[3] + write[0] * write[3]) * 1024.0
     lines = [f"# rocprofv3 HBM traffic summary: {name}", f"command: {command}",
              f"kernel: {kernel}",
-             f"kernel_source_sha256_16: {source_hash(DECODE_SOURCES)}",
+             f"kernel_source_sha256_16: {source_hash(kernel_sources(kernel))}",
              f"copy_calibration_bytes: {calib}",
              f"fetch_kib_copy: {fetch[2]:.1f}",
              f"fetch_scale: {fetch[3]:.4f}",
@@ -544,6 +632,64 @@ def summarize_traffic(fetch_dir: str, write_dir: str, kernel: str, name: str, co
              f"fetch_kib_per_dispatch: {fetch[0]:.1f}  ({fetch[1]} dispatches)",
              f"write_kib_per_dispatch: {write[0]:.1f}  ({write[1]} dispatches)",
              f"traffic_bytes_per_launch: {traffic:.0f}"]
+    _write_profile(name, lines)
+
+
+# MI355X: 8 XCDs of 32 CUs, 4 SIMDs per CU.
+XCDS, SIMDS = 8, 1024
+
+
+def summarize_counters(outdir: str, kernel: str, name: str, command: str):
+    """profiles/<name>.txt: per-dispatch averages of every counter collected
+    for `kernel` (rocprofv3 --pmc runs under DIR), with derived figures.
+
+    rocprofv3's csv gives each counter summed over its hardware instances.
+    GRBM_GUI_ACTIVE counts every XCD's busy cycles, so /8 is the kernel's span
+    in cycles; SQ_VALU_MFMA_BUSY_CYCLES counts each SIMD's matrix-core busy
+    cycles, so over (SIMDs x span) it is the matrix cores' busy fraction.  The
+    SQ_* wave counters (SQ_WAVE_CYCLES, SQ_ACTIVE_INST_*) count in units of 4
+    cycles, summed over waves."""
+    files = glob.glob(os.path.join(outdir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {outdir}")
+    vals, durs = {}, []
+    for f in files:
+        for r in _read_csv(f):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            durs.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    if not vals:
+        raise SystemExit(f"no dispatch of {kernel} under {outdir}")
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    dur_ns = sum(durs) / len(durs)
+    lines = [f"# rocprofv3 counter summary: {name}", f"command: {command}", f"kernel: {kernel}",
+             f"kernel_source_sha256_16: {source_hash(kernel_sources(kernel))}",
+             f"dispatch_avg_ns_under_counters: {dur_ns:.0f}", "",
+             "counter | per-dispatch average | dispatches"]
+    for k in sorted(avg):
+        lines.append(f"{k} | {avg[k]:.6g} | {len(vals[k])}")
+    lines.append("")
+    span = avg.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+    if span:
+        lines.append(f"span_cycles: {span:.0f}  (GRBM_GUI_ACTIVE / 8 XCDs)")
+        lines.append(f"implied_clock_ghz: {span / dur_ns:.3f}  (span / dispatch duration)")
+    if span and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        lines.append(f"mfma_busy_frac: {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (SIMDS * span):.4f}"
+                     "  (SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x span))")
+    if span and "SQ_ACTIVE_INST_VALU" in avg:
+        lines.append(f"valu_active_frac_per_simd: "
+                     f"{4 * avg['SQ_ACTIVE_INST_VALU'] / (SIMDS * span):.4f}"
+                     "  (4 x SQ_ACTIVE_INST_VALU / (1024 SIMDs x span); summed over the "
+                     "SIMD's waves, MFMA issue included)")
+    if span and "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+        lines.append(f"valu_mfma_coexec_frac: "
+                     f"{avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / (SIMDS * span):.4f}"
+                     "  (SQ_VALU_MFMA_COEXEC_CYCLES / (1024 SIMDs x span))")
+    if "SQ_INSTS_VALU" in avg and avg.get("SQ_INSTS_MFMA"):
+        lines.append(f"valu_insts_per_mfma_inst: "
+                     f"{(avg['SQ_INSTS_VALU'] - avg['SQ_INSTS_MFMA']) / avg['SQ_INSTS_MFMA']:.2f}"
+                     "  ((SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA)")
     _write_profile(name, lines)
 
 
@@ -556,18 +702,23 @@ def _write_profile(name, lines):
 
 # -------------------------------------------------------------------- main
 
+LEGS = ("decode", "prefill", "mixed", "next", "qwen")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["decode", "all", "next"], default="all",
-                    help="decode: the headline only; next (with --profile-run): also the "
-                         "window, multi-token, ragged, KV-append and RoPE-append legs")
+    ap.add_argument("--only", choices=["all", *LEGS], default="all",
+                    help="run only the headline decode plus this leg (with --profile-run: "
+                         "only this leg); next = the window, multi-token, ragged, KV-append "
+                         "and RoPE-append legs")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "NAME"))
     ap.add_argument("--summarize-traffic", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "KERNEL", "NAME"))
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("DIR", "KERNEL", "NAME"))
     ap.add_argument("--command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
 
@@ -576,6 +727,9 @@ def main():
         return 0
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.command)
+        return 0
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.command)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library's path runs on a single MI355X "
@@ -594,53 +748,71 @@ def main():
     flush_buf = torch.empty(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB
     timer = Timer(torch, flush_buf)
     K, W = args.steps, args.warmup
+    legs = set(LEGS) if args.only == "all" else {args.only}
+    # the headline decode always runs, except in a profile run of another leg
+    run_headline = not args.profile_run or args.only in ("all", "decode")
 
-    log("generating gpt-oss decode workload")
-    dec = wl.gptoss_decode(0)
     label = ("gpt-oss-20b-shaped decode, bf16: 64 seqs x 1 token, 64 q / 8 KV heads, "
              "head_dim 64, ctx U[1024,8192], 16-token HND pages, random page table, "
              "q/k/v/sinks N(0,1), seed 0")
-    log("timing decode")
-    d_res, d_out, _ = bench_decode(torch, ga, timer, dec, K, W, label,
-                                   with_warm=not args.profile_run)
-    log(json.dumps(d_res))
+    d_res = d_out = dec = None
+    if run_headline:
+        log("generating gpt-oss decode workload")
+        dec = wl.gptoss_decode(0)
+        log("timing decode")
+        with leg_range(torch, "gptoss_decode"):
+            d_res, d_out, _ = bench_decode(torch, ga, timer, dec, K, W, label,
+                                           with_warm=not args.profile_run)
+        log(json.dumps(d_res))
 
     extra = {}
-    if args.only == "all" or args.profile_run:
+    if "prefill" in legs:
         log("generating gpt-oss prefill workload")
         pre = wl.gptoss_prefill(0)
-        p_res, _ = bench_prefill(torch, ga, timer, pre, K, W,
-                                 "gpt-oss-shaped causal prefill, bf16: 8 seqs x 4096 tokens, "
-                                 "64 q / 8 KV heads, head_dim 64, sinks N(0,1), seed 0")
+        with leg_range(torch, "gptoss_prefill"):
+            p_res, _ = bench_prefill(torch, ga, timer, pre, K, W,
+                                     "gpt-oss-shaped causal prefill, bf16: 8 seqs x 4096 "
+                                     "tokens, 64 q / 8 KV heads, head_dim 64, sinks N(0,1), "
+                                     "seed 0")
+        del pre
         log(json.dumps(p_res))
         extra["prefill"] = p_res
-    if args.only == "all" and not args.profile_run:
+    if "mixed" in legs:
         log("generating mixed workload")
-        extra["mixed"] = bench_mixed(torch, ga, timer, K, W, wl)
+        with leg_range(torch, "mixed"):
+            extra["mixed"] = bench_mixed(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["mixed"]))
-    if args.only == "all" or args.only == "next":
+    if "next" in legs:
         log("sliding-window legs (window 128)")
-        extra["sliding_window"] = bench_window(torch, ga, timer, K, W, wl)
+        with leg_range(torch, "window128"):
+            extra["sliding_window"] = bench_window(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["sliding_window"]))
         log("multi-token decode leg")
-        extra["multi_token_decode"] = bench_multi(torch, ga, timer, K, W, wl)
+        with leg_range(torch, "multi_token_decode"):
+            extra["multi_token_decode"] = bench_multi(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["multi_token_decode"]))
         log("ragged cache-free legs")
-        extra["ragged"] = bench_ragged(torch, ga, timer, K, W, wl)
+        with leg_range(torch, "ragged"):
+            extra["ragged"] = bench_ragged(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["ragged"]))
         log("KV append legs")
-        extra["kv_append"] = bench_append(torch, ga, timer, K, W, wl)
+        with leg_range(torch, "kv_append"):
+            extra["kv_append"] = bench_append(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["kv_append"]))
         log("RoPE + KV append leg")
-        extra["rope_append"] = bench_rope(torch, ga, timer, K, W, wl)
+        with leg_range(torch, "rope_append"):
+            extra["rope_append"] = bench_rope(torch, ga, timer, K, W, wl)
         log(json.dumps(extra["rope_append"]))
-    if args.only == "all" and not args.profile_run:
+    if "qwen" in legs:
         log("generating qwen decode workload (about a minute)")
         qw = wl.qwen_decode(0)
-        q_res, _, keep = bench_decode(torch, ga, timer, qw, max(K // 2, 3), max(W // 2, 1),
-                                      "Qwen3-235B-shaped decode, bf16: 128 seqs x 1 token, "
-                                      "64 q / 4 KV heads, head_dim 128, ctx U[4096,32768], "
-                                      "sinks -inf, seed 0")
+        with leg_range(torch, "qwen_decode"):
+            q_res, _, keep = bench_decode(torch, ga, timer, qw, max(K // 2, 3),
+                                          max(W // 2, 1),
+                                          "Qwen3-235B-shaped decode, bf16: 128 seqs x 1 token, "
+                                          "64 q / 4 KV heads, head_dim 128, ctx "
+                                          "U[4096,32768], sinks -inf, seed 0",
+                                          with_warm=not args.profile_run)
         del keep, qw
         extra["qwen_decode"] = q_res
         log(json.dumps(q_res))
@@ -664,7 +836,7 @@ def main():
         print("GPU decode output does not match the oracle; refusing to report", file=sys.stderr)
         return 1
 
-    traffic = read_traffic()
+    traffic = read_traffic(TRAFFIC_FILE, DECODE_SOURCES)
     split_launch_bytes = d_res["algorithmic_bytes"]
     achieved = d_res["split_GB_per_s"]
     line = {
@@ -682,6 +854,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": label, "parallelism": "single GPU",
                    "hbm_frac": d_res["hbm_frac"], "warm_GB_per_s": d_res["warm_GB_per_s"],
+                   "ms_median": d_res["ms_median"], "ms_min": d_res["ms_min"],
                    "split_ms": d_res["split_ms"], "merge_ms": d_res["merge_ms"]},
         "roofline": {"bound": "hbm", "kernel": "decode_split_bf16<64>",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -693,9 +866,11 @@ def main():
     }
     if "prefill" in extra:
         p = extra["prefill"]
-        line["prefill_roofline"] = {"bound": "mfma", "kernel": "prefill_bf16<64>",
-                                    "achieved": p["TFLOP_per_s"], "peak": MFMA_BF16_PEAK_TFLOPS,
-                                    "unit": "TFLOP/s", "frac": p["mfma_frac"], "traffic": None}
+        line["prefill_roofline"] = {
+            "bound": "mfma", "kernel": "prefill_bf16<64>", "achieved": p["TFLOP_per_s"],
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": p["mfma_frac"],
+            "traffic": read_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SOURCES),
+            "mfma_busy": read_counter(PREFILL_COUNTER_FILE, PREFILL_SOURCES, "mfma_busy_frac")}
     print(json.dumps(line), flush=True)
     return 0
 
