@@ -95,6 +95,7 @@ def attn_sinks_version() -> int:
 
 ATTN_DEBUG_PREFILL_ONE_HEAD = 0
 ATTN_DEBUG_PREFILL_WAIT_ALL = 1
+ATTN_DEBUG_PREFILL_WINDOW_STREAMED = 2
 
 
 def attn_sinks_set_debug(setting: int, value: int) -> int:

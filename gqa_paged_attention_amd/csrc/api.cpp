@@ -67,6 +67,8 @@ void debug_init()
         g_debug[attn::kDebugPrefillOneHead] = (k && std::strcmp(k, "1") == 0) ? 1 : 0;
         const char *w = std::getenv("ATTN_SINKS_PREFILL_WAIT_ALL");
         g_debug[attn::kDebugPrefillWaitAll] = (w && std::strcmp(w, "1") == 0) ? 1 : 0;
+        const char *ws = std::getenv("ATTN_SINKS_PREFILL_WINDOW_STREAMED");
+        g_debug[attn::kDebugPrefillWindowStreamed] = (ws && std::strcmp(ws, "1") == 0) ? 1 : 0;
     });
 }
 

@@ -49,10 +49,14 @@ struct PrefillLaunch {
 // kDebugPrefillOneHead gives every prefill workgroup one query head where it
 // would take four (ATTN_SINKS_PREFILL_ONE_HEAD=1), kDebugPrefillWaitAll makes
 // the prefill tile waits take every load in flight
-// (ATTN_SINKS_PREFILL_WAIT_ALL=1).  Every setting gives the same results.
+// (ATTN_SINKS_PREFILL_WAIT_ALL=1), kDebugPrefillWindowStreamed runs the
+// windowed prefill in the kernel whose waves stream their own blocks
+// (ATTN_SINKS_PREFILL_WINDOW_STREAMED=1).  Every setting gives results within
+// the same bar (the first two the same bits).
 constexpr int kDebugPrefillOneHead = 0;
 constexpr int kDebugPrefillWaitAll = 1;
-constexpr int kDebugSettings = 2;
+constexpr int kDebugPrefillWindowStreamed = 2;
+constexpr int kDebugSettings = 3;
 int debug_setting(int id);
 
 // The most packed query rows (G times query tokens per sequence) the

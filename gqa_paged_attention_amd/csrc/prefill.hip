@@ -43,12 +43,16 @@
 // loop with the plain online softmax (exact block maxima, rescaling).  The
 // final division uses the same m, so the result does not depend on it.
 //
-// Pipeline.  Step b of a wave issues S^T of block b+1 and P*V of block b-1 on
-// the matrix cores (16 instructions at d = 64) while the vector ALU computes
-// the weights of block b from the S^T of the previous step.  No instruction
-// of a step waits for another of the same step, so one wave keeps both pipes
-// busy.  At the step that reads the first block of tile T, the wave waits for
-// tile T, meets the other waves and issues tile T+2.
+// Pipeline.  At d = 128, step b of a wave issues S^T of block b+1 and P*V of
+// block b-1 on the matrix cores while the vector ALU computes the weights of
+// block b from the S^T of the previous step; no instruction of a step waits
+// for another of the same step, so one wave keeps both pipes busy.  At d = 64
+// the two row blocks of a wave run half a step apart (skew_step): each
+// half-step pairs the weights of one row block with 8 matrix instructions of
+// the other, which needs one S^T register set per row block and leaves room
+// to read every LDS operand a step before its use.  At the step that first
+// reads tile T, the wave waits for tile T, meets the other waves and issues
+// tile T+2.
 #include "common.h"
 #include "kernels.h"
 
@@ -130,11 +134,15 @@ __device__ __forceinline__ void wait_loads_and_sync(bool all_landed)
 {
     static_assert(kLoadsPerTile == 2 || kLoadsPerTile == 4, "loads per tile");
     if (all_landed)
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     else if (kLoadsPerTile == 4)
-        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else
-        asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    // the LDS wait through the builtin, so that the compiler knows every
+    // earlier LDS read has landed and adds no wait for them later
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
 }
 
 struct PrefillArgs {
@@ -264,9 +272,14 @@ struct ChunkPages {
     int p[2];
 };
 
+// first_page: under a sliding window, the page of the oldest key the
+// workgroup sees; chunks on pages below it (wholly outside every window)
+// take that page instead, whose table entry is valid (their keys are masked
+// either way; load_tile keeps their rows inside the sequence, so the data
+// stays finite).
 template <int D, int NW = kWaves>
 __device__ __forceinline__ ChunkPages chunk_pages(const int32_t *__restrict__ bt, int t,
-                                                  int last_page, int wave)
+                                                  int last_page, int wave, int first_page = 0)
 {
     using C = Cfg<D>;
     ChunkPages cp;
@@ -274,7 +287,8 @@ __device__ __forceinline__ ChunkPages chunk_pages(const int32_t *__restrict__ bt
 #pragma unroll
     for (int i = 0; i < LoadLanes<D, NW>::kPer; ++i)
         cp.p[i] = load_scalar(
-            bt, min((t * C::kBN + C::kRowsPerLoad * (wave + NW * i)) >> 4, last_page));
+            bt, min(max((t * C::kBN + C::kRowsPerLoad * (wave + NW * i)) >> 4, first_page),
+                    last_page));
     return cp;
 }
 
@@ -282,6 +296,11 @@ __device__ __forceinline__ ChunkPages chunk_pages(const int32_t *__restrict__ bt
 // Rows past the sequence repeat its last row (finite; the causal mask hides
 // them); their page index is clamped to the last page, which holds that row.
 // A tile wholly inside the sequence takes the lanes' precomputed offsets.
+// first_page: the lower page clamp of chunk_pages.  A chunk it moved up
+// reads that page's row of the same slot, or the sequence's last row where
+// that slot lies past the end (the first page can be the last, partly
+// filled one; rows past the end of a page are not the sequence's data).  In
+// a tile wholly inside the sequence every row of the first page is inside it.
 // kContig: K/V rows are contiguous [tokens][Hkv][d] and kv_off is the element
 // offset of the sequence's key 0 for this KV head (the 16-byte chunks of one
 // load then come from R rows kv_stride apart).  Paged: kv_off is the head's
@@ -289,7 +308,7 @@ __device__ __forceinline__ ChunkPages chunk_pages(const int32_t *__restrict__ bt
 template <int D, bool kContig, int NW = kWaves>
 __device__ __forceinline__ void load_tile(const Smem<D> &sm, const PrefillArgs &a, const ChunkPages &cp,
                                           int t, int L, size_t kv_off, int wave,
-                                          const LoadLanes<D, NW> &ll)
+                                          const LoadLanes<D, NW> &ll, int first_page = 0)
 {
     using C = Cfg<D>;
     constexpr int kPer = LoadLanes<D, NW>::kPer;
@@ -316,7 +335,9 @@ __device__ __forceinline__ void load_tile(const Smem<D> &sm, const PrefillArgs &
             dma16(a.v_cache + kv_off, 2 * (row + ll.vc[i]), sm.v(stage) + 512 * j);
         } else {
             const size_t slab = (size_t)cp.p[i] * a.num_kv_heads * 16 * D + kv_off;
-            const int row = kv0 + ll.key[i] < L ? (ll.key[i] & 15) : ((L - 1) & 15);
+            // the token this lane's row stands for on the page it reads
+            const int tok = 16 * max((kv0 + ll.key[i]) >> 4, first_page) + (ll.key[i] & 15);
+            const int row = min(tok, L - 1) & 15;
             dma16(a.k_cache + slab, 2 * (row * D + ll.kc[i]), sm.k(stage) + 512 * j);
             dma16(a.v_cache + slab, 2 * (row * D + ll.vc[i]), sm.v(stage) + 512 * j);
         }
@@ -600,6 +621,158 @@ __device__ __forceinline__ void last_step(WaveState<D> &w, const Smem<D> &sm, in
         pv_mfma<D>(w.acc[rb], vop, w.pop[rb]);
 }
 
+// ---- skewed row blocks -----------------------------------------------------
+// The two row blocks of a wave run half a step apart, so that every half-step
+// pairs the vector work of one row block with matrix work of the other:
+//   half A of step b: weights of block b for row block 1, while S^T of block
+//                     b+1 for row block 0 and P*V of block b for row block 0
+//                     go to the matrix cores;
+//   half B of step b: weights of block b+1 for row block 0, while S^T of
+//                     block b+1 and P*V of block b for row block 1 do.
+// Each row block then needs one S^T register set (its weights are taken
+// before its next S^T is written), and each half-step has 8 matrix
+// instructions to overlap with about 50 vector ones.  The K operands of
+// block b+2 are read into the second K register set at the start of step b
+// (a whole step ahead), the V operands of block b+1 at its end.  Every row's
+// arithmetic is that of the plain order, so the results are the same bits.
+
+template <int D>
+__device__ __forceinline__ void qk_rb(f32x16_t &s, const u32x4_t (&qop)[D / 16],
+                                      const u32x4_t (&kop)[D / 16])
+{
+    s = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        s = mfma32x32x16(kop[kk], qop[kk], s);
+}
+
+// Weights of one row block (mask, reference maximum on the first block).
+template <bool kMasked, bool kFirst>
+__device__ __forceinline__ void weights_rb(float &m, float &lsum, u32x4_t (&pop)[2], f32x16_t &s,
+                                           int thr, float scale_log2, bool &bad)
+{
+    if (kMasked)
+        apply_mask(s, thr);
+    if (kFirst)
+        m = block_max(s, scale_log2);
+    lsum = block_weights(s, m, pop, scale_log2, lsum);
+    bad = bad || !(lsum <= kWeightSumLimit);
+    asm volatile("" ::"v"(pop[0]), "v"(pop[1]), "v"(lsum));
+}
+
+// Step b.  kNext: block b+1 exists (S^T of it, weights of it for row block
+// 0); kMasked: the weights need the causal mask; kFirst: b = 0 (row block 1
+// takes its reference maximum from it).  kcur: K of block b+1; knext:
+// receives K of block b+2 (kReadK); vop: V of block b, then of block b+1
+// (kReadV).  thr: the row's position minus 4 (lane / 32), for block 0.
+template <int D, bool kNext, bool kMasked, bool kFirst, bool kReadK, bool kReadV,
+          int kPhase = -1>
+__device__ __forceinline__ void skew_step(WaveState<D> &w, const Smem<D> &sm, int b,
+                                          f32x16_t (&s)[2], const u32x4_t (&kcur)[D / 16],
+                                          u32x4_t (&knext)[D / 16], u32x4_t (&vop)[D / 32][2],
+                                          int thr, int rbs, float sl2, int lane, bool &bad,
+                                          const LdsLanes<D> *lanes = nullptr)
+{
+    static_assert(Cfg<D>::kNRB == 2, "two row blocks");
+    if (kReadK) {
+        if constexpr (kPhase >= 0)
+            read_k_at<D>(knext, k_block<D>(sm, kPhase + 2), *lanes);
+        else
+            read_k<D>(knext, k_block<D>(sm, b + 2), 0, lane);
+    }
+    // half A
+    if (kNext)
+        qk_rb<D>(s[0], w.qop[0], kcur);
+    pv_mfma<D>(w.acc[0], vop, w.pop[0]);
+    weights_rb<kMasked, kFirst>(w.m[1], w.lsum[1], w.pop[1], s[1], thr - kKB * b + rbs, sl2,
+                                bad);
+    if (D == 64) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // half B
+    if (kNext)
+        qk_rb<D>(s[1], w.qop[1], kcur);
+    pv_mfma<D>(w.acc[1], vop, w.pop[1]);
+    if (kNext)
+        weights_rb<kMasked, false>(w.m[0], w.lsum[0], w.pop[0], s[0], thr - kKB * (b + 1), sl2,
+                                   bad);
+    if (kReadV) {
+        if constexpr (kPhase >= 0)
+            read_v_at<D>(vop, v_block<D>(sm, kPhase + 1), *lanes);
+        else
+            read_v<D>(vop, v_block<D>(sm, b + 1), 0, lane);
+    }
+    if (D == 64 && kNext) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+    }
+}
+
+// Weights of one row block under a sliding window: the band mask (keys
+// past the row or before its window) when `masked`; when `lazy`, a row that
+// has seen no key yet takes its reference maximum from this block (rows whose
+// window starts later still have none: their weights are 0).
+__device__ __forceinline__ void win_weights_rb(float &m, float &lsum, u32x4_t (&pop)[2],
+                                               f32x16_t &s, int thr, int window, bool masked,
+                                               bool lazy, float scale_log2, bool &bad)
+{
+    if (masked)
+        apply_band(s, thr, window);
+    if (lazy) {
+        const float bm = block_max(s, scale_log2);
+        m = m == kNegInf ? bm : m;
+    }
+    const float m_ref = m == kNegInf ? 0.f : m;
+    lsum = block_weights(s, m_ref, pop, scale_log2, lsum);
+    bad = bad || !(lsum <= kWeightSumLimit);
+    asm volatile("" ::"v"(pop[0]), "v"(pop[1]), "v"(lsum));
+}
+
+// skew_step under a sliding window (runtime mask and first-key flags; the
+// few blocks of a window do not repay compile-time variants).  Row block 0's
+// rows start at position p0; row block 1's at p0 + 32.
+template <int D>
+__device__ __forceinline__ void win_step(WaveState<D> &w, const Smem<D> &sm, int b, bool next,
+                                         f32x16_t (&s)[2], const u32x4_t (&kcur)[D / 16],
+                                         u32x4_t (&knext)[D / 16], u32x4_t (&vop)[D / 32][2],
+                                         int thr, int p0, int window, float sl2, int lane,
+                                         bool &bad)
+{
+    // a block needs the band mask unless every row of the row block sees
+    // all of its keys; a row block's rows have all seen a key after block
+    // (p + 32 - window) / 32 of its last row p
+    auto masked = [&](int blk, int p) {
+        return !(kKB * blk >= p + 32 - window && kKB * blk + kKB - 1 <= p);
+    };
+    auto lazy = [&](int blk, int p) { return kKB * blk <= max(p + 32 - window, 0); };
+    if (next)
+        read_k<D>(knext, k_block<D>(sm, b + 2), 0, lane);
+    if (next)
+        qk_rb<D>(s[0], w.qop[0], kcur);
+    pv_mfma<D>(w.acc[0], vop, w.pop[0]);
+    win_weights_rb(w.m[1], w.lsum[1], w.pop[1], s[1], thr - kKB * b + 32, window,
+                   masked(b, p0 + 32), lazy(b, p0 + 32), sl2, bad);
+    __builtin_amdgcn_sched_barrier(0);
+    if (next)
+        qk_rb<D>(s[1], w.qop[1], kcur);
+    pv_mfma<D>(w.acc[1], vop, w.pop[1]);
+    if (next) {
+        win_weights_rb(w.m[0], w.lsum[0], w.pop[0], s[0], thr - kKB * (b + 1), window,
+                       masked(b + 1, p0), lazy(b + 1, p0), sl2, bad);
+        read_v<D>(vop, v_block<D>(sm, b + 1), 0, lane);
+    }
+}
+
 // One 32-key block of K and V fetched straight from the paged cache: kPer
 // 16-byte chunks of each per lane (key c / (d/8), chunk c % (d/8) for c =
 // lane + 64 i).  Keys past the sequence repeat its last key (finite; masked).
@@ -613,7 +786,9 @@ struct RawBlock {
 // reads once (scalar loads); chunk i lies on the first when i < kPer / 2.
 // k_lo: the oldest key any row of the wave sees.  When the block's first page
 // lies wholly below it (a sliding window), that page's table entry is not
-// read and its chunks are zero (every row masks those keys).
+// read and its chunks take rows of the second page instead, kept inside the
+// sequence (that page may be its last, partly filled one): finite values
+// for keys every row masks.
 template <int D, bool kContig = false>
 __device__ __forceinline__ void fetch_block(RawBlock<D> &rb, const PrefillArgs &a,
                                             const int32_t *__restrict__ bt, int L,
@@ -622,31 +797,28 @@ __device__ __forceinline__ void fetch_block(RawBlock<D> &rb, const PrefillArgs &
     constexpr int kChunks = D / 8;
     constexpr int kPer = RawBlock<D>::kPer;
     static_assert(kPer % 2 == 0, "half of the chunks on each page");
-    const bool first_live = kContig || k0 + 16 > k_lo;
     size_t slab[2] = {0, 0};  // element offsets of the two pages' head slabs
+    // the first page below every window: its chunks stand for keys 16 on
+    const bool skip_first = !kContig && k0 + 16 <= k_lo;
     if constexpr (!kContig) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-            if (s == 1 || first_live)
-                slab[s] = (size_t)load_scalar(bt, min(k0 + 16 * s, L - 1) >> 4) *
-                              a.num_kv_heads * 16 * D + kv_off;
+        const size_t page_elems = (size_t)a.num_kv_heads * 16 * D;
+        slab[1] = (size_t)load_scalar(bt, min(k0 + 16, L - 1) >> 4) * page_elems + kv_off;
+        slab[0] = skip_first
+                      ? slab[1]
+                      : (size_t)load_scalar(bt, min(k0, L - 1) >> 4) * page_elems + kv_off;
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int c = lane + 64 * i;
         const int key = c / kChunks, chunk = c % kChunks;
-        const int tok = min(k0 + key, L - 1);
+        const int tok = min(k0 + key + (skip_first && i < kPer / 2 ? 16 : 0), L - 1);
         size_t off;
         if constexpr (kContig)
             off = kv_off + (size_t)tok * a.kv_stride + 8 * chunk;
         else
             off = slab[i < kPer / 2 ? 0 : 1] + (size_t)(tok & 15) * D + 8 * chunk;
-        if (i < kPer / 2 && !first_live) {
-            rb.k[i] = rb.v[i] = u32x4_t{0, 0, 0, 0};
-        } else {
-            rb.k[i] = *(const u32x4_t *)(a.k_cache + off);
-            rb.v[i] = *(const u32x4_t *)(a.v_cache + off);
-        }
+        rb.k[i] = *(const u32x4_t *)(a.k_cache + off);
+        rb.v[i] = *(const u32x4_t *)(a.v_cache + off);
     }
 }
 
@@ -753,7 +925,7 @@ __device__ __forceinline__ void window_block(WaveState<D> &w, const uint16_t *kt
 template <int D, bool kContig>
 __device__ void exact_rows(WaveState<D> &w, uint16_t *lds_wave, const PrefillArgs &a,
                            const int32_t *__restrict__ bt, int L, size_t kv_off, int nb,
-                           int wpf, int thr, int rb_step, int lane)
+                           int wpf, int thr, int rb_step, int lane, int window = 0, int j0 = 0)
 {
     constexpr int NRB = Cfg<D>::kNRB;
     uint16_t *kt = lds_wave;
@@ -766,13 +938,17 @@ __device__ void exact_rows(WaveState<D> &w, uint16_t *lds_wave, const PrefillArg
         for (int db = 0; db < D / 32; ++db)
             w.acc[rb][db] = f32x16_t{};
     }
-    for (int blk = 0; blk < nb; ++blk) {
+    const int k_lo = window > 0 ? max(wpf - window + 1, 0) : 0;
+    for (int blk = j0; blk < nb; ++blk) {
         const int k0 = kKB * blk;
         RawBlock<D> raw;
-        fetch_block<D, kContig>(raw, a, bt, L, kv_off, k0, lane);
+        fetch_block<D, kContig>(raw, a, bt, L, kv_off, k0, lane, k_lo);
         stash_block<D>(raw, kt, vt, lane);
-        exact_block<D, false>(w, kt, vt, k0 + kKB - 1 > wpf, thr - k0, 0, a.scale_log2, lane,
-                              rb_step);
+        if (window > 0)
+            exact_block<D, true>(w, kt, vt, true, thr - k0, window, a.scale_log2, lane, rb_step);
+        else
+            exact_block<D, false>(w, kt, vt, k0 + kKB - 1 > wpf, thr - k0, 0, a.scale_log2, lane,
+                                  rb_step);
     }
 }
 
@@ -899,9 +1075,10 @@ __device__ __forceinline__ void store_rows(const WaveState<D> &w, uint16_t *stag
 // one KV head, so every wave sees the same keys, masks and block count (no
 // wave waits at the tile barriers for the others' extra diagonal blocks) and
 // the causal range of a workgroup's tiles is 4 times finer.
-template <int D, bool kContig, bool kWaitAll, int HPW>
+template <int D, bool kContig, bool kWaitAll, int HPW, bool kWin = false>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
 {
+    static_assert(!kWin || (D == 64 && HPW == 4 && !kContig), "windowed layout");
     using C = Cfg<D>;
     constexpr int NRB = C::kNRB;
     constexpr int kWavesPerHead = kWaves / HPW;
@@ -950,21 +1127,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     // its offset inside a page
     const size_t kv_off = kContig ? (size_t)kv_first * a.kv_stride + (size_t)g * D
                                   : (size_t)g * 16 * D;
+    // Sliding window: the workgroup's rows (the same for its 4 waves) see
+    // keys from k_lo on; its tiles start at the tile of k_lo, its blocks at
+    // that tile's first block j0, and pages below k_lo's are never read.
+    const int window = kWin ? a.window : 0;
+    const int k_lo = kWin ? max(wpf - window + 1, 0) : 0;
+    const int t_lo = k_lo / C::kBN;
+    const int j0 = C::kBPT * t_lo;
 
-    // tiles 0 and 1 in flight before the loop; tile T+2 is issued when the
-    // wave starts reading tile T
+    // tiles t_lo and t_lo+1 in flight before the loop; tile T+2 is issued
+    // when the wave starts reading tile T
     const LoadLanes<D> ll = load_lanes<D, kContig>(wave, lane, a.kv_stride);
     auto pages = [&](int t) {
         if constexpr (kContig)
             return ChunkPages{{0, 0}};
         else
-            return chunk_pages<D>(bt, t, last_page, wave);
+            return chunk_pages<D>(bt, t, last_page, wave, k_lo >> 4);
     };
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-        if (t < ntiles)
-            load_tile<D, kContig>(sm, a, pages(t), t, L, kv_off, wave, ll);
-    ChunkPages next_pages = pages(2);
+        if (t_lo + t < ntiles)
+            load_tile<D, kContig>(sm, a, pages(t_lo + t), t_lo + t, L, kv_off, wave, ll,
+                                      k_lo >> 4);
+    ChunkPages next_pages = pages(t_lo + 2);
 
     // Q while the first tiles load; one wait covers both (the compiler then
     // knows the Q registers are ready and adds no waits inside the loops)
@@ -973,6 +1158,170 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
 
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
+    // blocks from bm on hold keys past the wave's first row: causal mask
+    const int bm = (wpf + 1) / kKB;
+    const int thr = wpf + row_step * r32 - 4 * half;  // minus the block start
+    bool bad = false;  // a row sum of this lane came too close to overflow
+    if constexpr (NRB == 2) {
+    // Step j reads K of block j+2 (tile (j+2)/BPT) and V of block j+1.  When
+    // block j+2 starts tile T, the wave first waits for tile T, meets the
+    // other waves and issues tile T+2 (steps -2 and -1 do this for tiles 0
+    // and 1).  Waves with fewer blocks keep doing so after their last step.
+    auto tile_start = [&](int step) {
+        if ((step + 2) % C::kBPT == 0) {
+            const int t = (step + 2) / C::kBPT;
+            if (t < ntiles) {
+                // the page ids of tile t+3 are read before the wait, which
+                // covers them: no scalar load is in flight afterwards, so the
+                // compiler can wait for LDS reads by count
+                const ChunkPages later = pages(t + 3);
+                wait_loads_and_sync<2 * C::kChunksPerWave>(kWaitAll || t + 1 >= ntiles);
+                if (t + 2 < ntiles)
+                    load_tile<D, kContig>(sm, a, next_pages, t + 2, L, kv_off, wave, ll,
+                                          k_lo >> 4);
+                next_pages = later;
+            }
+        }
+    };
+    const float sl2 = a.scale_log2;
+    const LdsLanes<D> lane_ofs = lds_lanes<D>(lane);
+    f32x16_t s[NRB];
+    u32x4_t ka[D / 16], kb[D / 16], vop[D / 32][2];
+    if constexpr (kWin) {
+        // blocks j0 .. nb-1 (a window's few blocks), masks and first-key
+        // references decided per block
+        tile_start(j0 - 2);
+        tile_start(j0 - 1);
+        read_k<D>(ka, k_block<D>(sm, j0), 0, lane);
+        qk_rb<D>(s[0], w.qop[0], ka);
+        qk_rb<D>(s[1], w.qop[1], ka);
+        read_k<D>(ka, k_block<D>(sm, j0 + 1), 0, lane);
+        read_v<D>(vop, v_block<D>(sm, j0), 0, lane);
+        win_weights_rb(w.m[0], w.lsum[0], w.pop[0], s[0], thr - kKB * j0, window, true, true, sl2,
+                       bad);
+        for (int j = j0; j < nb; j += 2) {
+            tile_start(j);
+            win_step<D>(w, sm, j, j + 1 < nb, s, ka, kb, vop, thr, wpf, window, sl2, lane, bad);
+            if (j + 1 < nb) {
+                tile_start(j + 1);
+                win_step<D>(w, sm, j + 1, j + 2 < nb, s, kb, ka, vop, thr, wpf, window, sl2, lane,
+                            bad);
+            }
+        }
+        for (int j = nb; j + 2 <= C::kBPT * ntiles; ++j)
+            tile_start(j);
+    } else {
+    tile_start(-2);
+    tile_start(-1);
+    if (nb > 0) {
+        // S^T of block 0 for both row blocks, weights of row block 0; the
+        // operands of step 0 (K of block 1, V of block 0)
+        read_k<D>(ka, k_block<D>(sm, 0), 0, lane);
+        qk_rb<D>(s[0], w.qop[0], ka);
+        qk_rb<D>(s[1], w.qop[1], ka);
+        read_k<D>(ka, k_block<D>(sm, 1), 0, lane);
+        read_v<D>(vop, v_block<D>(sm, 0), 0, lane);
+        if (bm == 0)
+            weights_rb<true, true>(w.m[0], w.lsum[0], w.pop[0], s[0], thr, sl2, bad);
+        else
+            weights_rb<false, true>(w.m[0], w.lsum[0], w.pop[0], s[0], thr, sl2, bad);
+    }
+    // step 0 (row block 1 takes its reference maximum from block 0)
+    tile_start(0);
+    if (nb > 1) {
+        if (bm <= 1)
+            skew_step<D, true, true, true, true, true>(w, sm, 0, s, ka, kb, vop, thr, rbs, sl2,
+                                                       lane, bad);
+        else
+            skew_step<D, true, false, true, true, true>(w, sm, 0, s, ka, kb, vop, thr, rbs, sl2,
+                                                        lane, bad);
+    } else if (nb == 1) {
+        skew_step<D, false, true, true, false, false>(w, sm, 0, s, ka, kb, vop, thr, rbs, sl2,
+                                                      lane, bad);
+    }
+    // Steps 1 .. nb-2 in pairs (odd steps take K from kb and read into ka,
+    // even ones the other way round); steps whose weights reach the diagonal
+    // run the masked variant.  Then the last step.
+    int j = 1;
+    const int steady_end = min(bm - 1, nb - 1);  // steps before it need no mask
+    if constexpr (kLdsCycle<D> == 8) {
+        for (; j + 7 < steady_end; j += 8) {
+            const int jj = (j & ~7) | 1;  // == j, with its low bits visible
+            LdsLanes<D> lr = lane_ofs;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+                asm volatile("" : "+v"(lr.k[kk]));
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                asm volatile("" : "+v"(lr.v[db]));
+            tile_start(jj);
+            skew_step<D, true, false, false, true, true, 1>(w, sm, jj, s, kb, ka, vop, thr, rbs,
+                                                            sl2, lane, bad, &lr);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_start(jj + 1);
+            skew_step<D, true, false, false, true, true, 2>(w, sm, jj + 1, s, ka, kb, vop, thr,
+                                                            rbs, sl2, lane, bad, &lr);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_start(jj + 2);
+            skew_step<D, true, false, false, true, true, 3>(w, sm, jj + 2, s, kb, ka, vop, thr,
+                                                            rbs, sl2, lane, bad, &lr);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_start(jj + 3);
+            skew_step<D, true, false, false, true, true, 4>(w, sm, jj + 3, s, ka, kb, vop, thr,
+                                                            rbs, sl2, lane, bad, &lr);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_start(jj + 4);
+            skew_step<D, true, false, false, true, true, 5>(w, sm, jj + 4, s, kb, ka, vop, thr,
+                                                            rbs, sl2, lane, bad, &lr);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_start(jj + 5);
+            skew_step<D, true, false, false, true, true, 6>(w, sm, jj + 5, s, ka, kb, vop, thr,
+                                                            rbs, sl2, lane, bad, &lr);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_start(jj + 6);
+            skew_step<D, true, false, false, true, true, 7>(w, sm, jj + 6, s, kb, ka, vop, thr,
+                                                            rbs, sl2, lane, bad, &lr);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_start(jj + 7);
+            skew_step<D, true, false, false, true, true, 0>(w, sm, jj + 7, s, ka, kb, vop, thr,
+                                                            rbs, sl2, lane, bad, &lr);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    for (; j + 1 < steady_end; j += 2) {
+        tile_start(j);
+        skew_step<D, true, false, false, true, true>(w, sm, j, s, kb, ka, vop, thr, rbs, sl2, lane,
+                                                     bad);
+        tile_start(j + 1);
+        skew_step<D, true, false, false, true, true>(w, sm, j + 1, s, ka, kb, vop, thr, rbs, sl2,
+                                                     lane, bad);
+    }
+    for (; j + 1 < nb - 1; j += 2) {
+        tile_start(j);
+        skew_step<D, true, true, false, true, true>(w, sm, j, s, kb, ka, vop, thr, rbs, sl2, lane,
+                                                    bad);
+        tile_start(j + 1);
+        skew_step<D, true, true, false, true, true>(w, sm, j + 1, s, ka, kb, vop, thr, rbs, sl2,
+                                                    lane, bad);
+    }
+    // an odd count of full steps leaves one (K of block j+1 in kb)
+    if (j < nb - 1) {
+        tile_start(j);
+        skew_step<D, true, true, false, true, true>(w, sm, j, s, kb, ka, vop, thr, rbs, sl2, lane,
+                                                    bad);
+        ++j;
+    }
+    // step nb-1: weights of block nb-1 for row block 1, P*V of block nb-1
+    // (no S^T or K operands left to take, so the K register set is moot)
+    if (nb > 1) {
+        tile_start(nb - 1);
+        skew_step<D, false, true, false, false, false>(w, sm, nb - 1, s, ka, kb, vop, thr, rbs,
+                                                       sl2, lane, bad);
+    }
+    for (j = max(nb, 1); j + 2 <= C::kBPT * ntiles; ++j)
+        tile_start(j);
+    }
+    } else {
     // Step j reads K of block j+1 (tile (j+1)/BPT) and V of block j-1.  When
     // block j+1 starts tile T, the wave first waits for tile T, meets the
     // other waves and issues tile T+2 (step -1 does this for tile 0).  Waves
@@ -992,16 +1341,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
             }
         }
     };
-    // blocks from bm on hold keys past the wave's first row: causal mask
-    const int bm = (wpf + 1) / kKB;
-    const int thr = wpf + row_step * r32 - 4 * half;  // minus the block start
     const float sl2 = a.scale_log2;
     const LdsLanes<D> lane_ofs = lds_lanes<D>(lane);
     // S^T of the block whose weights are next, and of the one after: two
     // register sets that trade roles every step (the steady loop is unrolled
     // twice so that no copy is needed)
     f32x16_t sa[NRB], sb[NRB];
-    bool bad = false;  // a row sum of this lane came too close to overflow
     tile_start(-1);
     if (nb > 0) {
         u32x4_t kop[D / 16];
@@ -1119,10 +1464,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     }
     for (j = max(nb + 1, 1); j <= C::kBPT * ntiles; ++j)
         tile_start(j);
+    }
     __syncthreads();  // every wave is past its last read of the stages
     if (__any(bad))
         exact_rows<D, kContig>(w, lds + wave * (C::kLdsBytes / 2 / kWaves), a, bt, L, kv_off, nb,
-                               wpf, thr, rbs, lane);
+                               wpf, thr, rbs, lane, window, j0);
 
     // Epilogue through this wave's part of the (now free) LDS.
     store_rows<D>(w, lds + wave * (C::kLdsBytes / 2 / kWaves), a, q0, q_len, row_w, h, lane);
@@ -1196,30 +1542,36 @@ template <int D>
 constexpr int kWindowLdsBytes = kWaves * 2 * kKB * D * 2;
 
 bool prefill_one_head() { return debug_setting(kDebugPrefillOneHead) != 0; }
+bool prefill_window_streamed() { return debug_setting(kDebugPrefillWindowStreamed) != 0; }
 bool prefill_wait_all() { return debug_setting(kDebugPrefillWaitAll) != 0; }
 
 // more than 64 KiB of LDS (d = 128) has to be allowed once per kernel
-template <int D, bool kContig, bool kWaitAll, int HPW>
+template <int D, bool kContig, bool kWaitAll, int HPW, bool kWin = false>
 hipError_t launch_causal(const PrefillArgs &a, long long wgs, hipStream_t stream)
 {
     constexpr int kLds = Cfg<D>::kLdsBytes;
     static const hipError_t attr = hipFuncSetAttribute(
-        (const void *)prefill_bf16<D, kContig, kWaitAll, HPW>,
+        (const void *)prefill_bf16<D, kContig, kWaitAll, HPW, kWin>,
         hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (attr != hipSuccess)
         return attr;
-    hipLaunchKernelGGL((prefill_bf16<D, kContig, kWaitAll, HPW>), dim3((unsigned)wgs),
+    hipLaunchKernelGGL((prefill_bf16<D, kContig, kWaitAll, HPW, kWin>), dim3((unsigned)wgs),
                        dim3(kThreads), kLds, stream, a);
     return hipGetLastError();
 }
 
 template <int D, int HPW>
-hipError_t launch_causal_hpw(PrefillArgs a, const PrefillLaunch &p)
+long long causal_grid(PrefillArgs &a, const PrefillLaunch &p)
 {
     constexpr int kRows = 32 * Cfg<D>::kNRB * (kWaves / HPW);
     a.num_q_tiles = (p.max_q_len + kRows - 1) / kRows;
-    const long long wgs =
-        (long long)p.num_seqs * p.num_kv_heads * (a.group / HPW) * a.num_q_tiles;
+    return (long long)p.num_seqs * p.num_kv_heads * (a.group / HPW) * a.num_q_tiles;
+}
+
+template <int D, int HPW>
+hipError_t launch_causal_hpw(PrefillArgs a, const PrefillLaunch &p)
+{
+    const long long wgs = causal_grid<D, HPW>(a, p);
     if (wgs > 0x7fffffffLL)
         return hipErrorInvalidValue;
     const bool contig = p.cu_seqlens_kv != nullptr, wait_all = prefill_wait_all();
@@ -1228,6 +1580,17 @@ hipError_t launch_causal_hpw(PrefillArgs a, const PrefillLaunch &p)
                         : launch_causal<D, true, false, HPW>(a, wgs, p.stream);
     return wait_all ? launch_causal<D, false, true, HPW>(a, wgs, p.stream)
                     : launch_causal<D, false, false, HPW>(a, wgs, p.stream);
+}
+
+// The windowed prefill on the causal kernel's pipeline (d = 64, paged, four
+// query heads per workgroup).
+hipError_t launch_window64(PrefillArgs a, const PrefillLaunch &p)
+{
+    const long long wgs = causal_grid<64, 4>(a, p);
+    if (wgs > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    return prefill_wait_all() ? launch_causal<64, false, true, 4, true>(a, wgs, p.stream)
+                              : launch_causal<64, false, false, 4, true>(a, wgs, p.stream);
 }
 
 template <int D>
@@ -1263,6 +1626,11 @@ hipError_t launch_d(const PrefillLaunch &p)
     if (p.window > 0 && p.window < p.max_seq_len) {
         // a window that leaves out some key of some row (otherwise the
         // causal kernel below computes exactly the same rows)
+        if constexpr (D == 64) {
+            if (a.group % 4 == 0 && !p.cu_seqlens_kv && !prefill_one_head() &&
+                !prefill_window_streamed())
+                return launch_window64(a, p);
+        }
         static const hipError_t wattr = hipFuncSetAttribute(
             (const void *)prefill_window_bf16<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
             kWindowLdsBytes<D>);
@@ -1273,8 +1641,10 @@ hipError_t launch_d(const PrefillLaunch &p)
         return hipGetLastError();
     }
     // four query heads per workgroup where the group allows it (d = 64)
-    if (D == 64 && a.group % 4 == 0 && !prefill_one_head())
-        return launch_causal_hpw<D, 4>(a, p);
+    if constexpr (D == 64) {
+        if (a.group % 4 == 0 && !prefill_one_head())
+            return launch_causal_hpw<D, 4>(a, p);
+    }
     return launch_causal_hpw<D, 1>(a, p);
 }
 

@@ -225,7 +225,9 @@ int attn_sinks_prefill(int dtype, int num_seqs, int num_q_heads, int num_kv_head
  * Decode reads only the blocks of each sequence that hold its last W keys;
  * bf16 with 0 < W <= 512 and W < max_seq_len runs one wave per (sequence,
  * KV head) over them and writes the output directly (the workspace is then
- * not touched).  Prefill with 0 < W < max_seq_len runs a kernel of its own in which each
+ * not touched).  bf16 prefill with 0 < W < max_seq_len at head_dim 64 and a
+ * group size divisible by 4 runs on the causal prefill's pipeline over the
+ * tiles its rows' windows reach; other shapes run a kernel in which each
  * wave streams the few blocks its rows need straight from the paged cache.
  *
  * Pages a window no longer reaches may be released: with W > 0, the page
@@ -456,8 +458,9 @@ int attn_sinks_ragged(int dtype, int num_seqs, int num_q_heads, int num_kv_heads
 const char *attn_sinks_status_string(int status);
 
 /*
- * Debug settings, for diagnostics and tests; every setting gives the same
- * results, bit for bit.  Defaults come from the environment, read once:
+ * Debug settings, for diagnostics and tests; the first two give the same
+ * results bit for bit, the third the same within rounding.  Defaults come
+ * from the environment, read once:
  *   ATTN_DEBUG_PREFILL_ONE_HEAD  bf16 causal prefill at head_dim 64 with a
  *                                group size divisible by 4 gives each
  *                                workgroup one query head (256 rows) instead
@@ -467,13 +470,21 @@ const char *attn_sinks_status_string(int status);
  *                                loads take every load in flight instead of
  *                                leaving the next tile's loads outstanding
  *                                (ATTN_SINKS_PREFILL_WAIT_ALL=1)
+ *   ATTN_DEBUG_PREFILL_WINDOW_STREAMED
+ *                                a windowed bf16 prefill that would run on
+ *                                the causal kernel's pipeline (head_dim 64,
+ *                                group size divisible by 4) runs the kernel
+ *                                whose waves stream their own blocks instead
+ *                                (ATTN_SINKS_PREFILL_WINDOW_STREAMED=1); its
+ *                                results differ in rounding only
  * attn_sinks_set_debug sets one (value 0 or nonzero) for the launches that
  * follow and returns its previous value, or -1 for an unknown setting.  Not
  * meant to be changed while other threads enqueue calls.
  */
 enum attn_debug_setting {
     ATTN_DEBUG_PREFILL_ONE_HEAD = 0,
-    ATTN_DEBUG_PREFILL_WAIT_ALL = 1
+    ATTN_DEBUG_PREFILL_WAIT_ALL = 1,
+    ATTN_DEBUG_PREFILL_WINDOW_STREAMED = 2
 };
 int attn_sinks_set_debug(int setting, int value);
 

@@ -423,10 +423,11 @@ def test_noalloc_limit_is_the_workspace_size(lib):
 
 def test_debug_settings(lib):
     # set returns the previous value; unknown settings give -1 and change nothing
-    for s in (ga.ATTN_DEBUG_PREFILL_ONE_HEAD, ga.ATTN_DEBUG_PREFILL_WAIT_ALL):
+    for s in (ga.ATTN_DEBUG_PREFILL_ONE_HEAD, ga.ATTN_DEBUG_PREFILL_WAIT_ALL,
+              ga.ATTN_DEBUG_PREFILL_WINDOW_STREAMED):
         before = ga.attn_sinks_set_debug(s, 1)
         assert before in (0, 1)
         assert ga.attn_sinks_set_debug(s, 0) == 1
         assert ga.attn_sinks_set_debug(s, before) == 0
-    assert ga.attn_sinks_set_debug(2, 1) == -1
+    assert ga.attn_sinks_set_debug(3, 1) == -1
     assert ga.attn_sinks_set_debug(-1, 1) == -1

@@ -14,6 +14,7 @@ from dataclasses import replace
 import pytest
 import torch
 
+import gqa_paged_attention_amd as ga
 from gqa_paged_attention_amd import workloads as wl
 from tests.gpu_helpers import (aligned_scores, check_sampled, compare, note, oracle_full,
                                run_decode, run_prefill, scale_keys)
@@ -53,13 +54,24 @@ PREFILL_CASES = [
 ]
 
 
+@pytest.fixture(params=[False, True], ids=["pipelined", "streamed"])
+def window_route(request):
+    """bf16 windowed prefill at d 64 with a group size divisible by 4 runs on
+    the causal kernel's pipeline; the debug setting sends it to the kernel
+    whose waves stream their own blocks, which every other shape takes."""
+    ga.attn_sinks_set_debug(ga.ATTN_DEBUG_PREFILL_WINDOW_STREAMED, int(request.param))
+    yield request.param
+    ga.attn_sinks_set_debug(ga.ATTN_DEBUG_PREFILL_WINDOW_STREAMED, 0)
+
+
 @pytest.mark.parametrize("case", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
-def test_prefill_window(case):
+def test_prefill_window(case, window_route):
     name, dt, L, Lq, Hq, Hkv, d, sm = case
     b = wl.small_batch(zlib.crc32(name.encode()) % 1000 + 11, dt, L, Lq, Hq, Hkv, d,
                        sink_mode=sm)
     for w in (1, 17, 32, 64, 128, 300):
-        note(f"prefill window {w} {name}: L={L} Lq={Lq} Hq={Hq} Hkv={Hkv} d={d} {dt}")
+        note(f"prefill window {w} {name} (streamed={window_route}): L={L} Lq={Lq} Hq={Hq} "
+             f"Hkv={Hkv} d={d} {dt}")
         compare(run_prefill(b, window=w), oracle_full(b, window=w), dt,
                 f"prefill {name} window {w}")
 
@@ -93,7 +105,7 @@ def test_window_runs_are_deterministic():
 
 
 @pytest.mark.parametrize("d,L,Lq", [(64, 700, 700), (128, 500, 300)])
-def test_window_large_late_logits(d, L, Lq):
+def test_window_large_late_logits(d, L, Lq, window_route):
     """Keys from position 200 on get logits far above the earlier ones (std
     ~100 in natural units): rows whose window holds both kinds must raise
     their maximum well past the lazy slack and rescale.  Prefill at W = 128;
@@ -111,7 +123,7 @@ def test_window_large_late_logits(d, L, Lq):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_window_prefill_logits_far_below_zero(d):
+def test_window_prefill_logits_far_below_zero(d, window_route):
     """Every logit near -150 (natural units) and no sink: weights against a
     zero reference would underflow to 0; each row's maximum has to come from
     its own first visible block."""
@@ -122,6 +134,25 @@ def test_window_prefill_logits_far_below_zero(d):
             f"window prefill low logits d={d}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_window_tail_on_partial_last_page(d, window_route):
+    """Chunks of a few rows at the very end of their sequence, whose windows
+    all start on the sequence's last, partly filled page: the pages below
+    are read as rows of that page, and those rows have to stay inside the
+    sequence (the rest of the page holds NaN).  Lengths put the oldest key
+    in either half of its 32-token block and in either block of a 64-key
+    tile; the windows are shorter than a page, one past a block's half,
+    and longer."""
+    L = [97, 100, 289, 310, 1000, 1007, 1010, 1025, 96, 1008]
+    Lq = [1, 4, 1, 8, 1, 8, 3, 2, 1, 9]
+    b = wl.small_batch(321 + d, "bf16", L, Lq, 16, 2, d, sink_mode="normal")
+    for w in (1, 2, 8, 9, 17, 40):
+        note(f"prefill window {w} tails on partial pages d={d} (streamed={window_route}): "
+             f"L={L} Lq={Lq}")
+        compare(run_prefill(b, window=w), oracle_full(b, window=w), "bf16",
+                f"prefill tails d={d} window {w}")
+
+
 def test_full_gptoss_decode_window128():
     b = wl.gptoss_decode(0)
     note("full gpt-oss decode, window 128 (every row)")
@@ -129,7 +160,7 @@ def test_full_gptoss_decode_window128():
             "gpt-oss decode window 128")
 
 
-def test_full_gptoss_prefill_window128():
+def test_full_gptoss_prefill_window128(window_route):
     b = wl.gptoss_prefill(0)
     note("full gpt-oss prefill, window 128 (sampled rows)")
     check_sampled(run_prefill(b, window=128), b, 3000, 5, "gpt-oss prefill window 128",
@@ -178,7 +209,7 @@ def test_decode_window_reads_no_page_below_it(case):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_prefill_window_reads_no_page_below_it(d):
+def test_prefill_window_reads_no_page_below_it(d, window_route):
     L, Lq, w = [1400, 700, 3000], [300, 200, 1000], 100
     b = wl.small_batch(71 + d, "bf16", L, Lq, 16, 2, d, sink_mode="normal")
     first = [max(l - lq - w + 1, 0) // 16 for l, lq in zip(L, Lq)]
