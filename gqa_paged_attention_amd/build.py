@@ -53,7 +53,7 @@ COMMON_FLAGS = [
 # operations in the loop, so a register spill (scratch traffic) there would
 # let a wave read an LDS stage before it lands.  The build refuses them with
 # any scratch.
-NO_SCRATCH_KERNELS = ("prefill_bf16I",)
+NO_SCRATCH_KERNELS = ("prefill_bf16I", "prefill_window_persistI")
 
 
 def check_no_scratch(remarks: str, src: str) -> None:
@@ -71,6 +71,44 @@ def check_no_scratch(remarks: str, src: str) -> None:
                 f"{src}: kernel {name} uses {m.group(1)} bytes/lane of scratch; its hand-counted "
                 "waits for the direct tile loads assume no other vector-memory operation in its "
                 "loop (reduce its register use)")
+
+
+# A vector instruction that writes a scalar register (v_readlane,
+# v_readfirstlane: spill restores among them) needs five wait states before a
+# vector-memory instruction reads that register.  The compiler inserts them
+# for its own instructions but does not look inside inline assembly, so the
+# direct tile loads carry them in their assembly; check_dma_hazards checks
+# the compiled assembly for any load that lacks them.
+_DMA = re.compile(r"global_load_lds_dwordx4\s+v\d+,\s+s\[(\d+):(\d+)\]")
+_VALU_SGPR_WRITE = re.compile(r"^(v_readlane_b32|v_readfirstlane_b32)\s+s(\d+)\b")
+_NOP = re.compile(r"^s_nop\s+(\d+)")
+
+
+def check_dma_hazards(asm: str) -> int:
+    """Raise if some global_load_lds reads a scalar base register that a
+    vector instruction wrote fewer than five wait states earlier (walking back
+    through the listing; s_nop N counts N + 1).  Returns the loads checked."""
+    lines = [l.strip() for l in asm.splitlines()]
+    checked = 0
+    for i, line in enumerate(lines):
+        m = _DMA.search(line)
+        if not m:
+            continue
+        checked += 1
+        regs = {int(m.group(1)), int(m.group(2))}
+        waits, k = 0, i - 1
+        while k >= 0 and waits < 5:
+            t = lines[k]
+            k -= 1
+            if not t or t[0] in ";." or t.endswith(":"):
+                continue
+            w = _VALU_SGPR_WRITE.match(t)
+            if w and int(w.group(2)) in regs:
+                raise RuntimeError(f"line {i + 1}: {line!r} reads s{w.group(2)}, written by "
+                                   f"{t!r} only {waits} wait states before")
+            n = _NOP.match(t)
+            waits += int(n.group(1)) + 1 if n else 1
+    return checked
 
 
 def _compile(src: str) -> str:

@@ -252,13 +252,17 @@ __device__ __forceinline__ LoadLanes<D, NW> load_lanes(int wave, int lane, int k
 // LDS byte address lds + 16 l.  Issued as inline assembly so that the
 // compiler does not tie its own LDS reads to these loads (it would wait for
 // every load in flight, the prefetches included); the kernel waits for them
-// explicitly (wait_loads_and_sync).  M0 holds the LDS address; one wait state
-// separates its write from the load that reads it.
+// explicitly (wait_loads_and_sync).  M0 holds the LDS address.  The
+// compiler does not look inside the assembly for hazards, so the assembly
+// opens with five wait states itself: a vector instruction that wrote the
+// base's scalar registers (v_readlane, as when they come back from a spill)
+// needs five before a vector-memory instruction reads them, and the write
+// of M0 needs one before the load that reads it.
 __device__ __forceinline__ void dma16(const uint16_t *gbase, uint32_t voff, const uint16_t *lds)
 {
     const uint32_t lds_addr =
         (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t *)lds;
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(voff), "s"(gbase), "{m0}"(lds_addr)
                  : "memory");
@@ -1008,21 +1012,29 @@ __device__ __forceinline__ void init_rows(WaveState<D> &w, const PrefillArgs &a,
     }
 }
 
-// Epilogue: fold the sink into each row's normalisation, then write the
-// wave's rows through its own LDS staging area (32 NRB rows of d bf16) so
-// that every global store covers whole 16-byte chunks of contiguous output
-// rows.  The staging rows are XOR-swizzled by 16-byte chunk (both the 8-byte
-// writes and the 16-byte reads are then free of bank conflicts).
+// The head's sink logit in base-2 units (-inf without sinks).  Read when a
+// wave starts, so that its latency overlaps the first loads instead of
+// delaying the epilogue.
+__device__ __forceinline__ float sink_log2(const PrefillArgs &a, int h)
+{
+    return a.sinks ? a.sinks[h] * kLog2e : kNegInf;
+}
+
+// Epilogue: fold the sink (sink2, from sink_log2) into each row's
+// normalisation, then write the wave's rows through its own LDS staging area
+// (32 NRB rows of d bf16) so that every global store covers whole 16-byte
+// chunks of contiguous output rows.  The staging rows are XOR-swizzled by
+// 16-byte chunk (both the 8-byte writes and the 16-byte reads are then free
+// of bank conflicts).
 template <int D>
 __device__ __forceinline__ void store_rows(const WaveState<D> &w, uint16_t *stage,
                                            const PrefillArgs &a, int q0, int q_len, int row_w,
-                                           int h, int lane)
+                                           int h, int lane, float sink2)
 {
     constexpr int NRB = Cfg<D>::kNRB;
     constexpr int kC16 = D / 8;  // 16-byte chunks per row
     const int r32 = lane & 31, half = lane >> 5;
     auto st_at = [&](int r, int c16) { return r * D + 8 * (c16 ^ (r & (kC16 - 1))); };
-    const float sink2 = a.sinks ? a.sinks[h] * kLog2e : kNegInf;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
         float lx, ly;
@@ -1095,6 +1107,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     const int L = kContig ? a.cu_seqlens_kv[b + 1] - kv_first : a.seq_lens[b];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = tc.h + wave / kWavesPerHead;
+    const float sink2 = sink_log2(a, h);
     const int lane = threadIdx.x & 63;
     const int r32 = lane & 31, half = lane >> 5;
     // Position of query row i: shift + i (causal, aligned to the end of the
@@ -1471,7 +1484,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
                                wpf, thr, rbs, lane, window, j0);
 
     // Epilogue through this wave's part of the (now free) LDS.
-    store_rows<D>(w, lds + wave * (C::kLdsBytes / 2 / kWaves), a, q0, q_len, row_w, h, lane);
+    store_rows<D>(w, lds + wave * (C::kLdsBytes / 2 / kWaves), a, q0, q_len, row_w, h, lane,
+                  sink2);
 }
 
 // Sliding-window prefill ("GPT OSS" model notes, section 4.1: even layers
@@ -1497,6 +1511,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_window_bf16(PrefillArgs a
         return;  // uniform over the workgroup
     const int L = a.seq_lens[tc.b];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const float sink2 = sink_log2(a, tc.h);
     const int lane = threadIdx.x & 63;
     const int r32 = lane & 31, half = lane >> 5;
     const int shift = L - q_len;  // position of query row i is shift + i
@@ -1535,7 +1550,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_window_bf16(PrefillArgs a
     }
     // the staging area of the epilogue is the wave's own K tile and more:
     // 32 NRB rows of d bf16 fit in its 2 * 32 * d elements
-    store_rows<D>(w, kt, a, q0, q_len, row_w, tc.h, lane);
+    store_rows<D>(w, kt, a, q0, q_len, row_w, tc.h, lane, sink2);
 }
 
 template <int D>

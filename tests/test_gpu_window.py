@@ -54,14 +54,31 @@ PREFILL_CASES = [
 ]
 
 
-@pytest.fixture(params=[False, True], ids=["pipelined", "streamed"])
+# bf16 windowed prefill at d 64 with a group size divisible by 4 runs on the
+# causal kernel's pipeline; a debug setting sends it to the kernel whose
+# waves stream their own blocks, which every other shape takes.
+WINDOW_ROUTES = {
+    "pipelined": {},
+    "streamed": {ga.ATTN_DEBUG_PREFILL_WINDOW_STREAMED: 1},
+}
+
+
+def _with_settings(settings, fn):
+    prev = {k: ga.attn_sinks_set_debug(k, v) for k, v in settings.items()}
+    try:
+        return fn()
+    finally:
+        for k, v in prev.items():
+            ga.attn_sinks_set_debug(k, v)
+
+
+@pytest.fixture(params=list(WINDOW_ROUTES))
 def window_route(request):
-    """bf16 windowed prefill at d 64 with a group size divisible by 4 runs on
-    the causal kernel's pipeline; the debug setting sends it to the kernel
-    whose waves stream their own blocks, which every other shape takes."""
-    ga.attn_sinks_set_debug(ga.ATTN_DEBUG_PREFILL_WINDOW_STREAMED, int(request.param))
+    settings = WINDOW_ROUTES[request.param]
+    prev = {k: ga.attn_sinks_set_debug(k, v) for k, v in settings.items()}
     yield request.param
-    ga.attn_sinks_set_debug(ga.ATTN_DEBUG_PREFILL_WINDOW_STREAMED, 0)
+    for k, v in prev.items():
+        ga.attn_sinks_set_debug(k, v)
 
 
 @pytest.mark.parametrize("case", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
@@ -70,7 +87,7 @@ def test_prefill_window(case, window_route):
     b = wl.small_batch(zlib.crc32(name.encode()) % 1000 + 11, dt, L, Lq, Hq, Hkv, d,
                        sink_mode=sm)
     for w in (1, 17, 32, 64, 128, 300):
-        note(f"prefill window {w} {name} (streamed={window_route}): L={L} Lq={Lq} Hq={Hq} "
+        note(f"prefill window {w} {name} ({window_route}): L={L} Lq={Lq} Hq={Hq} "
              f"Hkv={Hkv} d={d} {dt}")
         compare(run_prefill(b, window=w), oracle_full(b, window=w), dt,
                 f"prefill {name} window {w}")
@@ -147,10 +164,40 @@ def test_prefill_window_tail_on_partial_last_page(d, window_route):
     Lq = [1, 4, 1, 8, 1, 8, 3, 2, 1, 9]
     b = wl.small_batch(321 + d, "bf16", L, Lq, 16, 2, d, sink_mode="normal")
     for w in (1, 2, 8, 9, 17, 40):
-        note(f"prefill window {w} tails on partial pages d={d} (streamed={window_route}): "
+        note(f"prefill window {w} tails on partial pages d={d} ({window_route}): "
              f"L={L} Lq={Lq}")
         compare(run_prefill(b, window=w), oracle_full(b, window=w), "bf16",
                 f"prefill tails d={d} window {w}")
+
+
+PIPELINED_CASES = [
+    # id, seq_lens, q_lens, Hq, Hkv, window, late-key scale: chunks over
+    # prefixes; rows whose windows span small and much larger logits (their
+    # rows take the exact recompute); few-row tails on partial last pages
+    ("chunks", [500, 1000, 64, 2100], [100, 257, 1, 2100], 16, 2, 128, None),
+    ("late_logits", [700, 900], [700, 600], 8, 2, 128, 100.0),
+    ("tails", [97, 310, 1000, 1007, 1010], [1, 8, 1, 8, 3], 16, 2, 1, None),
+]
+
+
+@pytest.mark.parametrize("case", PIPELINED_CASES, ids=[c[0] for c in PIPELINED_CASES])
+def test_prefill_window_pipelined_wait_all_bit_identical(case):
+    """The pipelined windowed prefill with its hand-counted tile waits and
+    with waits that take every load in flight: the same bits (a wait that
+    missed a load would let a wave read a stage before it lands), and within
+    the bar of the oracle."""
+    name, L, Lq, Hq, Hkv, w, late = case
+    b = wl.small_batch(zlib.crc32(name.encode()) % 1000 + 41, "bf16", L, Lq, Hq, Hkv, 64,
+                       sink_mode="normal")
+    if late is not None:
+        b = scale_keys(b, 200, late)
+    note(f"window {w} pipelined, counted and wait-all tile waits, {name}: L={L} Lq={Lq} "
+         f"Hq={Hq} Hkv={Hkv}")
+    outs = {}
+    for route, settings in [("counted", {}), ("wait_all", {ga.ATTN_DEBUG_PREFILL_WAIT_ALL: 1})]:
+        outs[route] = _with_settings(settings, lambda: run_prefill(b, window=w))
+    assert torch.equal(outs["counted"].view(torch.int16), outs["wait_all"].view(torch.int16))
+    compare(outs["counted"], oracle_full(b, window=w), "bf16", f"window {w} {name}")
 
 
 def test_full_gptoss_decode_window128():
