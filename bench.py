@@ -582,8 +582,10 @@ def summarize_trace(outdir: str, name: str, command: str):
     if hits and markers:
         # each dispatch attributed to the leg range (bench.py leg_range) that
         # holds its start
-        ranges = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Message"])
-                  for r in _read_csv(markers[0]) if r.get("Message")]
+        # (the range's name is in "Function" in rocprofv3's marker csv)
+        ranges = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                   r.get("Message") or r.get("Function"))
+                  for r in _read_csv(markers[0]) if r.get("Message") or r.get("Function")]
         legs = {}
         for r in _read_csv(hits[0]):
             t0 = int(r["Start_Timestamp"])
