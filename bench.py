@@ -425,7 +425,8 @@ def bench_ragged(torch, ga, timer, steps, warmup, wl):
 
 def bench_mixed(torch, ga, timer, steps, warmup, wl):
     """The mixed batch: the decode rows (split + merge) and the two prefill
-    chunks, one after the other on one stream.  The decode half and the
+    chunks, one after the other on one stream, and again with the decode half
+    on a second stream beside the prefill half.  The decode half and the
     prefill half are each timed on their own as well as the whole step, with
     events only around what is timed (none between its launches)."""
     full, dec, pre = wl.mixed(0)
@@ -439,6 +440,23 @@ def bench_mixed(torch, ga, timer, steps, warmup, wl):
     rd = timer.run(dstages, steps, warmup, flush=True)
     rp = timer.run(pstage, steps, warmup, flush=True)
     r = timer.run(dstages + pstage, steps, warmup, flush=True)
+    # The same step with the decode half on a second stream (default
+    # priority), started together with the prefill half and joined before
+    # the step's end event: the memory-bound decode's workgroups run beside
+    # the compute-bound prefill's instead of before them.
+    side = torch.cuda.Stream()
+
+    def overlapped():
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            for _, f in dstages:
+                f()
+        for _, f in pstage:
+            f()
+        main.wait_stream(side)
+
+    ro = timer.run([("overlapped", overlapped)], steps, warmup, flush=True)
     nb, fl = decode_bytes(dec), prefill_flops(pre)
     dec_ms, pre_ms = rd["step_ms"], rp["step_ms"]
     bound_ms = (nb / (HBM_PEAK_GBS * 1e9) + fl / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
@@ -456,7 +474,10 @@ def bench_mixed(torch, ga, timer, steps, warmup, wl):
             "prefill_TFLOP_per_s": round(fl / (pre_ms * 1e-3) / 1e12, 1),
             "prefill_mfma_frac": round(fl / (pre_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "serial_bound_ms": round(bound_ms, 4),
-            "frac_of_serial_bound": round(bound_ms / r["step_ms"], 4)}
+            "frac_of_serial_bound": round(bound_ms / r["step_ms"], 4),
+            "two_stream_ms": round(ro["step_ms"], 4),
+            "two_stream_ms_median": round(ro["step_ms_median"], 4),
+            "two_stream_frac_of_serial_bound": round(bound_ms / ro["step_ms"], 4)}
 
 
 # ------------------------------------------------------------ cpu baseline
