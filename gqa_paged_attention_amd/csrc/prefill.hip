@@ -1157,17 +1157,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
         else
             return chunk_pages<D>(bt, t, last_page, wave, k_lo >> 4);
     };
+    // Q first (its rows need only the chunk offsets), then the first tiles
+    // (whose page ids take one more round trip), so that the Q loads are in
+    // flight during that round trip; one wait covers both (the compiler then
+    // knows the Q registers are ready and adds no waits inside the loops)
+    WaveState<D> w;
+    init_rows<D>(w, a, q0, q_len, row_w, h, lane);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
         if (t_lo + t < ntiles)
             load_tile<D, kContig>(sm, a, pages(t_lo + t), t_lo + t, L, kv_off, wave, ll,
                                       k_lo >> 4);
     ChunkPages next_pages = pages(t_lo + 2);
-
-    // Q while the first tiles load; one wait covers both (the compiler then
-    // knows the Q registers are ready and adds no waits inside the loops)
-    WaveState<D> w;
-    init_rows<D>(w, a, q0, q_len, row_w, h, lane);
 
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
