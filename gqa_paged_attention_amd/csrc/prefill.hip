@@ -6,12 +6,21 @@
 // sections 3 and 4.1).  The causal mask is aligned to the end of the visible
 // keys, so a chunk over a cached prefix sees the whole prefix.
 //
-// Work decomposition.  A workgroup of 4 waves owns BM consecutive query rows
-// of one query head of one sequence; each wave owns NRB row blocks of 32 rows
-// (d = 64: NRB = 2, BM = 256; d = 128: NRB = 1, BM = 128).  The 1-D grid is
-// ordered so that every workgroup of one (sequence, KV head) runs on the same
-// XCD (its L2 then serves the K/V tiles to all of them) and the query tiles
-// with the most keys start first.
+// Work decomposition.  Each wave owns NRB row blocks of 32 rows (d = 64:
+// NRB = 2; d = 128: NRB = 1).  At d = 64 with a group size divisible by 4 a
+// workgroup of 4 waves takes the same 64 rows of four query heads of one KV
+// head (every wave sees the same keys and masks, and each K/V tile serves
+// four heads); otherwise its 4 waves take consecutive row blocks of one query
+// head (BM = 256 rows at d = 64, 128 at d = 128).  The 1-D grid is ordered so
+// that every workgroup of one (sequence, KV head) runs on the same XCD (its
+// L2 then serves the K/V tiles to all of them) and the query tiles with the
+// most keys start first.
+//
+// Sliding window.  At d = 64 with four heads per workgroup the windowed
+// prefill runs on this pipeline, over the tiles from the one holding the
+// oldest key the workgroup's rows see, with a band mask and a reference
+// maximum taken lazily (a row's first blocks may hold none of its keys).
+// Other shapes run prefill_window_bf16, whose waves stream their own blocks.
 //
 // Keys are consumed in blocks of 32.  Per block, row block and wave, on
 // 32x32x16 bf16 matrix instructions:
