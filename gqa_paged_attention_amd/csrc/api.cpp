@@ -107,8 +107,9 @@ DecodeShape decode_shape(int num_seqs, int num_kv_heads, int max_seq_len)
 }
 
 // Multi-token decode shapes the split pass takes: G x (query tokens per
-// sequence) packed rows per KV head within its column blocks.
-bool multi_packed(int group, int head_dim, int max_q_len)
+// sequence) packed rows per KV head within its column blocks (the same bound
+// at both head sizes).
+bool multi_packed(int group, int max_q_len)
 {
     const int rows = group * max_q_len;
     return group > 0 && max_q_len >= 1 &&
@@ -668,7 +669,7 @@ size_t attn_sinks_decode_multi_workspace_bytes(int num_seqs, int num_q_heads, in
         max_q_len < 0 || !supported_head_dim(head_dim) || num_q_heads % num_kv_heads != 0 ||
         num_q_heads / num_kv_heads > kMaxGroup)
         return 0;
-    if (!multi_packed(num_q_heads / num_kv_heads, head_dim, max_q_len))
+    if (!multi_packed(num_q_heads / num_kv_heads, max_q_len))
         return 0;  // such calls run the prefill kernel, which needs no scratch
     return decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, nullptr,
                             nullptr, max_q_len);
@@ -683,8 +684,7 @@ int attn_sinks_decode_multi(int dtype, int num_seqs, int num_q_heads, int num_kv
                             size_t workspace_bytes, void *stream)
 {
     const bool packed = dtype == ATTN_DTYPE_BF16 &&
-                        multi_packed(num_kv_heads > 0 ? num_q_heads / num_kv_heads : 0, head_dim,
-                                     max_q_len);
+                        multi_packed(num_kv_heads > 0 ? num_q_heads / num_kv_heads : 0, max_q_len);
     if (!packed)  // fp32, or more packed rows than the split pass takes
         return attn_sinks_prefill(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                   page_size, num_pages, max_pages_per_seq, total_q, max_q_len,
