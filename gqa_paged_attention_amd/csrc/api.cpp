@@ -91,11 +91,19 @@ DecodeShape decode_shape(int num_seqs, int num_kv_heads, int max_seq_len)
     const long long units_max = (long long)num_seqs * ((max_seq_len + 31) / 32);
     long long w = wgs_override();
     if (!w) {
-        // the same number of workgroups on every CU, at least 4 waves per CU
+        // The same number of workgroups on every CU they use, at least 4
+        // waves per CU.  Workgroups of 4 waves use three quarters of the CUs:
+        // measured on the gpt-oss, mixed and Qwen-shaped decodes, 192 of them
+        // beat 256 (one per CU) by 1.3-2.2 %, and counts that put two on some
+        // CUs lose 8-20 %, since every workgroup has an equal share of the
+        // units.  Smaller workgroups share CUs and fill all of them.
         const int waves_per_cu = s.heads_per_wg > attn::kDecodeMinWavesPerCU
                                      ? s.heads_per_wg
                                      : attn::kDecodeMinWavesPerCU;
-        const long long total = (long long)attn::kDeviceCUs * waves_per_cu / s.heads_per_wg;
+        const long long cus = s.heads_per_wg >= attn::kDecodeMinWavesPerCU
+                                  ? (long long)attn::kDeviceCUs * 3 / 4
+                                  : (long long)attn::kDeviceCUs;
+        const long long total = cus * waves_per_cu / s.heads_per_wg;
         w = total / groups;
         if (w < 1)
             w = 1;

@@ -47,12 +47,13 @@ def test_status_strings_and_version(lib):
 
 def _expected_ws(B, Hq, Hkv, d, max_len):
     """The layout the header documents: W workgroups per group of up to 4 KV
-    heads (256 CUs x max(4, heads per workgroup) waves in all, capped by the
-    unit count); slots = B + W; ml [slots][Hq][2] padded to a multiple of 4
-    floats, then acc [slots][Hq][d]."""
+    heads (4-wave workgroups on 192 of the 256 CUs, smaller ones 4 waves per
+    CU on all 256, capped by the unit count); slots = B + W; ml
+    [slots][Hq][2] padded to a multiple of 4 floats, then acc [slots][Hq][d]."""
     per_wg = min(Hkv, 4)
     groups = -(-Hkv // per_wg)
-    w = max((256 * max(4, per_wg) // per_wg) // groups, 1)
+    cus = 192 if per_wg >= 4 else 256
+    w = max((cus * max(4, per_wg) // per_wg) // groups, 1)
     w = min(w, B * ((max_len + 31) // 32))
     if w == 0:
         return 0
