@@ -47,9 +47,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "decode_split_bf16_gptoss_decode_traffic.txt")
 PREFILL_TRAFFIC_FILE = os.path.join(PROFILES, "prefill_bf16_gptoss_prefill_traffic.txt")
 PREFILL_COUNTER_FILE = os.path.join(PROFILES, "prefill_bf16_gptoss_prefill_counters.txt")
-DECODE_SOURCES = ["gqa_paged_attention_amd/csrc/decode.hip", "gqa_paged_attention_amd/csrc/common.h"]
+# (api.cpp decides the launch shapes, kernels.h holds the constants they use)
+DECODE_SOURCES = ["gqa_paged_attention_amd/csrc/decode.hip", "gqa_paged_attention_amd/csrc/common.h",
+                  "gqa_paged_attention_amd/csrc/kernels.h", "gqa_paged_attention_amd/csrc/api.cpp"]
 PREFILL_SOURCES = ["gqa_paged_attention_amd/csrc/prefill.hip",
-                   "gqa_paged_attention_amd/csrc/common.h"]
+                   "gqa_paged_attention_amd/csrc/common.h",
+                   "gqa_paged_attention_amd/csrc/kernels.h", "gqa_paged_attention_amd/csrc/api.cpp"]
 
 
 def kernel_sources(kernel: str):
