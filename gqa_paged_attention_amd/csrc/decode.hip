@@ -433,14 +433,27 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int row0, int b, i
     }
 
     const int32_t *bt = a.block_table + (size_t)b * a.max_pages;
-    if (t_begin < t_lo) {
-        // the block that holds the oldest key of a sliding window
-        Block<D> head;
-        load_block<D, false>(head, a.k_cache, a.v_cache, bt, t_begin, t_end, g, a.num_kv_heads,
+    // The block that holds the oldest key of a sliding window: loaded and
+    // computed first.  At d = 64 with one column block it is computed only
+    // after the ring below has issued its first loads, so that its round trip
+    // overlaps theirs instead of preceding them (the order of the arithmetic,
+    // and so the result, is unchanged); elsewhere the registers it would hold
+    // meanwhile are not there to spare.
+    constexpr bool kHeadLate = D == 64 && NCB == 1;
+    const bool has_head = t_begin < t_lo;
+    const int t_head = t_begin;
+    Block<D> head;
+    auto run_head = [&]() {
+        if (has_head)
+            compute_block<D, NCB, true>(st, head, qop, t_head, t_lo, t_end, col_end,
+                                        a.scale_log2, lg, klds);
+    };
+    if (has_head) {
+        load_block<D, false>(head, a.k_cache, a.v_cache, bt, t_head, t_end, g, a.num_kv_heads,
                              n, lg, t_lo);
-        compute_block<D, NCB, true>(st, head, qop, t_begin, t_lo, t_end, col_end, a.scale_log2,
-                                    lg, klds);
         t_begin += kUnitTokens;
+        if constexpr (!kHeadLate)
+            run_head();
     }
     // Full blocks (keys every row sees) stream through a ring of register
     // buffers with loads issued ahead of the matrix work (two blocks ahead at
@@ -460,6 +473,8 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int row0, int b, i
                                 lg);
             load_block<D, true>(b1, a.k_cache, a.v_cache, bt, at(1), t_end, g, a.num_kv_heads, n,
                                 lg);
+            if constexpr (kHeadLate)
+                run_head();
             for (int ib = 0; ib < nfull; ib += 3) {
                 const int t0 = t_begin + kUnitTokens * ib;
                 load_block<D, true>(b2, a.k_cache, a.v_cache, bt, at(ib + 2), t_end, g,
@@ -508,6 +523,8 @@ __device__ __forceinline__ void run_piece(const SplitArgs &a, int row0, int b, i
                                              a.scale_log2, lg, klds);
             }
         }
+    } else if constexpr (kHeadLate) {
+        run_head();
     }
     for (int t0 = t_begin + kUnitTokens * nfull; t0 < t_end; t0 += kUnitTokens) {
         Block<D> bt_tail;
