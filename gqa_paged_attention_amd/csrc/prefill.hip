@@ -562,16 +562,16 @@ __device__ __forceinline__ void qk_all(f32x16_t (&s)[Cfg<D>::kNRB], const WaveSt
 // the two S^T register sets between steps).  kPV: P*V of block
 // b-1 with the weights in w.pop.  Always: the weights of block b from s_cur,
 // relative to the reference maxima (set from the block itself when kFirst,
-// masked when kMasked).  A row sum too close to overflow (or not finite)
-// marks the lane in `bad`; such a wave is recomputed exactly after the loop
-// (exact_rows), so the loop itself has no rescale branch.  kPhase >= 0: b is
+// masked when kMasked).  A wave with a row sum too close to overflow (or
+// not finite) after the loop is recomputed exactly (exact_rows), so the
+// loop itself has no rescale branch.  kPhase >= 0: b is
 // known to be kPhase modulo the LDS cycle (BPT * S blocks), so the operands'
 // LDS addresses are compile-time constants.
 template <int D, bool kQK, bool kPV, bool kMasked, bool kFirst, int kPhase = -1>
 __device__ __forceinline__ void step(WaveState<D> &w, const Smem<D> &sm, int b,
                                      f32x16_t (&s_cur)[Cfg<D>::kNRB],
                                      f32x16_t (&s_next)[Cfg<D>::kNRB], int thr0, float scale_log2,
-                                     int lane, bool &bad, int rb_step,
+                                     int lane, int rb_step,
                                      const LdsLanes<D> *lanes = nullptr)
 {
     constexpr int NRB = Cfg<D>::kNRB;
@@ -603,7 +603,6 @@ __device__ __forceinline__ void step(WaveState<D> &w, const Smem<D> &sm, int b,
         if (kFirst)
             w.m[rb] = block_max(s_cur[rb], scale_log2);
         w.lsum[rb] = block_weights(s_cur[rb], w.m[rb], w.pop[rb], scale_log2, w.lsum[rb]);
-        bad = bad || !(w.lsum[rb] <= kWeightSumLimit);
         // Keep the weights in this step: without a use here, the compiler
         // moves their computation to the next use, past the branch of the
         // next tile start, where it no longer overlaps this step's matrix
@@ -662,14 +661,13 @@ __device__ __forceinline__ void qk_rb(f32x16_t &s, const u32x4_t (&qop)[D / 16],
 // Weights of one row block (mask, reference maximum on the first block).
 template <bool kMasked, bool kFirst>
 __device__ __forceinline__ void weights_rb(float &m, float &lsum, u32x4_t (&pop)[2], f32x16_t &s,
-                                           int thr, float scale_log2, bool &bad)
+                                           int thr, float scale_log2)
 {
     if (kMasked)
         apply_mask(s, thr);
     if (kFirst)
         m = block_max(s, scale_log2);
     lsum = block_weights(s, m, pop, scale_log2, lsum);
-    bad = bad || !(lsum <= kWeightSumLimit);
     asm volatile("" ::"v"(pop[0]), "v"(pop[1]), "v"(lsum));
 }
 
@@ -683,7 +681,7 @@ template <int D, bool kNext, bool kMasked, bool kFirst, bool kReadK, bool kReadV
 __device__ __forceinline__ void skew_step(WaveState<D> &w, const Smem<D> &sm, int b,
                                           f32x16_t (&s)[2], const u32x4_t (&kcur)[D / 16],
                                           u32x4_t (&knext)[D / 16], u32x4_t (&vop)[D / 32][2],
-                                          int thr, int rbs, float sl2, int lane, bool &bad,
+                                          int thr, int rbs, float sl2, int lane,
                                           const LdsLanes<D> *lanes = nullptr)
 {
     static_assert(Cfg<D>::kNRB == 2, "two row blocks");
@@ -697,8 +695,7 @@ __device__ __forceinline__ void skew_step(WaveState<D> &w, const Smem<D> &sm, in
     if (kNext)
         qk_rb<D>(s[0], w.qop[0], kcur);
     pv_mfma<D>(w.acc[0], vop, w.pop[0]);
-    weights_rb<kMasked, kFirst>(w.m[1], w.lsum[1], w.pop[1], s[1], thr - kKB * b + rbs, sl2,
-                                bad);
+    weights_rb<kMasked, kFirst>(w.m[1], w.lsum[1], w.pop[1], s[1], thr - kKB * b + rbs, sl2);
     if (D == 64) {
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
 #pragma unroll
@@ -713,8 +710,7 @@ __device__ __forceinline__ void skew_step(WaveState<D> &w, const Smem<D> &sm, in
         qk_rb<D>(s[1], w.qop[1], kcur);
     pv_mfma<D>(w.acc[1], vop, w.pop[1]);
     if (kNext)
-        weights_rb<kMasked, false>(w.m[0], w.lsum[0], w.pop[0], s[0], thr - kKB * (b + 1), sl2,
-                                   bad);
+        weights_rb<kMasked, false>(w.m[0], w.lsum[0], w.pop[0], s[0], thr - kKB * (b + 1), sl2);
     if (kReadV) {
         if constexpr (kPhase >= 0)
             read_v_at<D>(vop, v_block<D>(sm, kPhase + 1), *lanes);
@@ -737,7 +733,7 @@ __device__ __forceinline__ void skew_step(WaveState<D> &w, const Smem<D> &sm, in
 // window starts later still have none: their weights are 0).
 __device__ __forceinline__ void win_weights_rb(float &m, float &lsum, u32x4_t (&pop)[2],
                                                f32x16_t &s, int thr, int window, bool masked,
-                                               bool lazy, float scale_log2, bool &bad)
+                                               bool lazy, float scale_log2)
 {
     if (masked)
         apply_band(s, thr, window);
@@ -747,7 +743,6 @@ __device__ __forceinline__ void win_weights_rb(float &m, float &lsum, u32x4_t (&
     }
     const float m_ref = m == kNegInf ? 0.f : m;
     lsum = block_weights(s, m_ref, pop, scale_log2, lsum);
-    bad = bad || !(lsum <= kWeightSumLimit);
     asm volatile("" ::"v"(pop[0]), "v"(pop[1]), "v"(lsum));
 }
 
@@ -758,8 +753,7 @@ template <int D>
 __device__ __forceinline__ void win_step(WaveState<D> &w, const Smem<D> &sm, int b, bool next,
                                          f32x16_t (&s)[2], const u32x4_t (&kcur)[D / 16],
                                          u32x4_t (&knext)[D / 16], u32x4_t (&vop)[D / 32][2],
-                                         int thr, int p0, int window, float sl2, int lane,
-                                         bool &bad)
+                                         int thr, int p0, int window, float sl2, int lane)
 {
     // a block needs the band mask unless every row of the row block sees
     // all of its keys; a row block's rows have all seen a key after block
@@ -774,14 +768,14 @@ __device__ __forceinline__ void win_step(WaveState<D> &w, const Smem<D> &sm, int
         qk_rb<D>(s[0], w.qop[0], kcur);
     pv_mfma<D>(w.acc[0], vop, w.pop[0]);
     win_weights_rb(w.m[1], w.lsum[1], w.pop[1], s[1], thr - kKB * b + 32, window,
-                   masked(b, p0 + 32), lazy(b, p0 + 32), sl2, bad);
+                   masked(b, p0 + 32), lazy(b, p0 + 32), sl2);
     __builtin_amdgcn_sched_barrier(0);
     if (next)
         qk_rb<D>(s[1], w.qop[1], kcur);
     pv_mfma<D>(w.acc[1], vop, w.pop[1]);
     if (next) {
         win_weights_rb(w.m[0], w.lsum[0], w.pop[0], s[0], thr - kKB * (b + 1), window,
-                       masked(b + 1, p0), lazy(b + 1, p0), sl2, bad);
+                       masked(b + 1, p0), lazy(b + 1, p0), sl2);
         read_v<D>(vop, v_block<D>(sm, b + 1), 0, lane);
     }
 }
@@ -1184,7 +1178,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     // blocks from bm on hold keys past the wave's first row: causal mask
     const int bm = (wpf + 1) / kKB;
     const int thr = wpf + row_step * r32 - 4 * half;  // minus the block start
-    bool bad = false;  // a row sum of this lane came too close to overflow
     if constexpr (NRB == 2) {
     // Step j reads K of block j+2 (tile (j+2)/BPT) and V of block j+1.  When
     // block j+2 starts tile T, the wave first waits for tile T, meets the
@@ -1220,15 +1213,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
         qk_rb<D>(s[1], w.qop[1], ka);
         read_k<D>(ka, k_block<D>(sm, j0 + 1), 0, lane);
         read_v<D>(vop, v_block<D>(sm, j0), 0, lane);
-        win_weights_rb(w.m[0], w.lsum[0], w.pop[0], s[0], thr - kKB * j0, window, true, true, sl2,
-                       bad);
+        win_weights_rb(w.m[0], w.lsum[0], w.pop[0], s[0], thr - kKB * j0, window, true, true, sl2);
         for (int j = j0; j < nb; j += 2) {
             tile_start(j);
-            win_step<D>(w, sm, j, j + 1 < nb, s, ka, kb, vop, thr, wpf, window, sl2, lane, bad);
+            win_step<D>(w, sm, j, j + 1 < nb, s, ka, kb, vop, thr, wpf, window, sl2, lane);
             if (j + 1 < nb) {
                 tile_start(j + 1);
-                win_step<D>(w, sm, j + 1, j + 2 < nb, s, kb, ka, vop, thr, wpf, window, sl2, lane,
-                            bad);
+                win_step<D>(w, sm, j + 1, j + 2 < nb, s, kb, ka, vop, thr, wpf, window, sl2, lane);
             }
         }
         for (int j = nb; j + 2 <= C::kBPT * ntiles; ++j)
@@ -1245,22 +1236,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
         read_k<D>(ka, k_block<D>(sm, 1), 0, lane);
         read_v<D>(vop, v_block<D>(sm, 0), 0, lane);
         if (bm == 0)
-            weights_rb<true, true>(w.m[0], w.lsum[0], w.pop[0], s[0], thr, sl2, bad);
+            weights_rb<true, true>(w.m[0], w.lsum[0], w.pop[0], s[0], thr, sl2);
         else
-            weights_rb<false, true>(w.m[0], w.lsum[0], w.pop[0], s[0], thr, sl2, bad);
+            weights_rb<false, true>(w.m[0], w.lsum[0], w.pop[0], s[0], thr, sl2);
     }
     // step 0 (row block 1 takes its reference maximum from block 0)
     tile_start(0);
     if (nb > 1) {
         if (bm <= 1)
             skew_step<D, true, true, true, true, true>(w, sm, 0, s, ka, kb, vop, thr, rbs, sl2,
-                                                       lane, bad);
+                                                       lane);
         else
             skew_step<D, true, false, true, true, true>(w, sm, 0, s, ka, kb, vop, thr, rbs, sl2,
-                                                        lane, bad);
+                                                        lane);
     } else if (nb == 1) {
         skew_step<D, false, true, true, false, false>(w, sm, 0, s, ka, kb, vop, thr, rbs, sl2,
-                                                      lane, bad);
+                                                      lane);
     }
     // Steps 1 .. nb-2 in pairs (odd steps take K from kb and read into ka,
     // even ones the other way round); steps whose weights reach the diagonal
@@ -1279,59 +1270,56 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
                 asm volatile("" : "+v"(lr.v[db]));
             tile_start(jj);
             skew_step<D, true, false, false, true, true, 1>(w, sm, jj, s, kb, ka, vop, thr, rbs,
-                                                            sl2, lane, bad, &lr);
+                                                            sl2, lane, &lr);
             __builtin_amdgcn_sched_barrier(0);
             tile_start(jj + 1);
             skew_step<D, true, false, false, true, true, 2>(w, sm, jj + 1, s, ka, kb, vop, thr,
-                                                            rbs, sl2, lane, bad, &lr);
+                                                            rbs, sl2, lane, &lr);
             __builtin_amdgcn_sched_barrier(0);
             tile_start(jj + 2);
             skew_step<D, true, false, false, true, true, 3>(w, sm, jj + 2, s, kb, ka, vop, thr,
-                                                            rbs, sl2, lane, bad, &lr);
+                                                            rbs, sl2, lane, &lr);
             __builtin_amdgcn_sched_barrier(0);
             tile_start(jj + 3);
             skew_step<D, true, false, false, true, true, 4>(w, sm, jj + 3, s, ka, kb, vop, thr,
-                                                            rbs, sl2, lane, bad, &lr);
+                                                            rbs, sl2, lane, &lr);
             __builtin_amdgcn_sched_barrier(0);
             tile_start(jj + 4);
             skew_step<D, true, false, false, true, true, 5>(w, sm, jj + 4, s, kb, ka, vop, thr,
-                                                            rbs, sl2, lane, bad, &lr);
+                                                            rbs, sl2, lane, &lr);
             __builtin_amdgcn_sched_barrier(0);
             tile_start(jj + 5);
             skew_step<D, true, false, false, true, true, 6>(w, sm, jj + 5, s, ka, kb, vop, thr,
-                                                            rbs, sl2, lane, bad, &lr);
+                                                            rbs, sl2, lane, &lr);
             __builtin_amdgcn_sched_barrier(0);
             tile_start(jj + 6);
             skew_step<D, true, false, false, true, true, 7>(w, sm, jj + 6, s, kb, ka, vop, thr,
-                                                            rbs, sl2, lane, bad, &lr);
+                                                            rbs, sl2, lane, &lr);
             __builtin_amdgcn_sched_barrier(0);
             tile_start(jj + 7);
             skew_step<D, true, false, false, true, true, 0>(w, sm, jj + 7, s, ka, kb, vop, thr,
-                                                            rbs, sl2, lane, bad, &lr);
+                                                            rbs, sl2, lane, &lr);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
     for (; j + 1 < steady_end; j += 2) {
         tile_start(j);
-        skew_step<D, true, false, false, true, true>(w, sm, j, s, kb, ka, vop, thr, rbs, sl2, lane,
-                                                     bad);
+        skew_step<D, true, false, false, true, true>(w, sm, j, s, kb, ka, vop, thr, rbs, sl2, lane);
         tile_start(j + 1);
         skew_step<D, true, false, false, true, true>(w, sm, j + 1, s, ka, kb, vop, thr, rbs, sl2,
-                                                     lane, bad);
+                                                     lane);
     }
     for (; j + 1 < nb - 1; j += 2) {
         tile_start(j);
-        skew_step<D, true, true, false, true, true>(w, sm, j, s, kb, ka, vop, thr, rbs, sl2, lane,
-                                                    bad);
+        skew_step<D, true, true, false, true, true>(w, sm, j, s, kb, ka, vop, thr, rbs, sl2, lane);
         tile_start(j + 1);
         skew_step<D, true, true, false, true, true>(w, sm, j + 1, s, ka, kb, vop, thr, rbs, sl2,
-                                                    lane, bad);
+                                                    lane);
     }
     // an odd count of full steps leaves one (K of block j+1 in kb)
     if (j < nb - 1) {
         tile_start(j);
-        skew_step<D, true, true, false, true, true>(w, sm, j, s, kb, ka, vop, thr, rbs, sl2, lane,
-                                                    bad);
+        skew_step<D, true, true, false, true, true>(w, sm, j, s, kb, ka, vop, thr, rbs, sl2, lane);
         ++j;
     }
     // step nb-1: weights of block nb-1 for row block 1, P*V of block nb-1
@@ -1339,7 +1327,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     if (nb > 1) {
         tile_start(nb - 1);
         skew_step<D, false, true, false, false, false>(w, sm, nb - 1, s, ka, kb, vop, thr, rbs,
-                                                       sl2, lane, bad);
+                                                       sl2, lane);
     }
     for (j = max(nb, 1); j + 2 <= C::kBPT * ntiles; ++j)
         tile_start(j);
@@ -1380,14 +1368,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
     tile_start(0);
     if (nb > 1) {
         if (bm == 0)
-            step<D, true, false, true, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad, rbs);
+            step<D, true, false, true, true>(w, sm, 0, sa, sb, thr, sl2, lane, rbs);
         else
-            step<D, true, false, false, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad, rbs);
+            step<D, true, false, false, true>(w, sm, 0, sa, sb, thr, sl2, lane, rbs);
     } else if (nb == 1) {
         if (bm == 0)
-            step<D, false, false, true, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad, rbs);
+            step<D, false, false, true, true>(w, sm, 0, sa, sb, thr, sl2, lane, rbs);
         else
-            step<D, false, false, false, true>(w, sm, 0, sa, sb, thr, sl2, lane, bad, rbs);
+            step<D, false, false, false, true>(w, sm, 0, sa, sb, thr, sl2, lane, rbs);
     }
     // Steps 1 .. nb-2: all three stages, in pairs (sb then sa holds the
     // current S^T), so that no register copy is needed; step 0 left S^T of
@@ -1415,57 +1403,56 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
             for (int db = 0; db < D / 32; ++db)
                 asm volatile("" : "+v"(lr.v[db]));
             tile_start(jj);
-            step<D, true, true, false, false, 1>(w, sm, jj, sb, sa, 0, sl2, lane, bad, rbs,
+            step<D, true, true, false, false, 1>(w, sm, jj, sb, sa, 0, sl2, lane, rbs,
                                                 &lr);
             __builtin_amdgcn_sched_barrier(0);
             tile_start(jj + 1);
-            step<D, true, true, false, false, 2>(w, sm, jj + 1, sa, sb, 0, sl2, lane, bad, rbs,
+            step<D, true, true, false, false, 2>(w, sm, jj + 1, sa, sb, 0, sl2, lane, rbs,
                                                 &lr);
             __builtin_amdgcn_sched_barrier(0);
             tile_start(jj + 2);
-            step<D, true, true, false, false, 3>(w, sm, jj + 2, sb, sa, 0, sl2, lane, bad, rbs,
+            step<D, true, true, false, false, 3>(w, sm, jj + 2, sb, sa, 0, sl2, lane, rbs,
                                                 &lr);
             __builtin_amdgcn_sched_barrier(0);
             tile_start(jj + 3);
-            step<D, true, true, false, false, 4>(w, sm, jj + 3, sa, sb, 0, sl2, lane, bad, rbs,
+            step<D, true, true, false, false, 4>(w, sm, jj + 3, sa, sb, 0, sl2, lane, rbs,
                                                 &lr);
             __builtin_amdgcn_sched_barrier(0);
             tile_start(jj + 4);
-            step<D, true, true, false, false, 5>(w, sm, jj + 4, sb, sa, 0, sl2, lane, bad, rbs,
+            step<D, true, true, false, false, 5>(w, sm, jj + 4, sb, sa, 0, sl2, lane, rbs,
                                                 &lr);
             __builtin_amdgcn_sched_barrier(0);
             tile_start(jj + 5);
-            step<D, true, true, false, false, 6>(w, sm, jj + 5, sa, sb, 0, sl2, lane, bad, rbs,
+            step<D, true, true, false, false, 6>(w, sm, jj + 5, sa, sb, 0, sl2, lane, rbs,
                                                 &lr);
             __builtin_amdgcn_sched_barrier(0);
             tile_start(jj + 6);
-            step<D, true, true, false, false, 7>(w, sm, jj + 6, sb, sa, 0, sl2, lane, bad, rbs,
+            step<D, true, true, false, false, 7>(w, sm, jj + 6, sb, sa, 0, sl2, lane, rbs,
                                                 &lr);
             __builtin_amdgcn_sched_barrier(0);
             tile_start(jj + 7);
-            step<D, true, true, false, false, 0>(w, sm, jj + 7, sa, sb, 0, sl2, lane, bad, rbs,
+            step<D, true, true, false, false, 0>(w, sm, jj + 7, sa, sb, 0, sl2, lane, rbs,
                                                 &lr);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
     for (; j + 1 < steady_end; j += 2) {
         tile_start(j);
-        step<D, true, true, false, false>(w, sm, j, sb, sa, 0, sl2, lane, bad, rbs);
+        step<D, true, true, false, false>(w, sm, j, sb, sa, 0, sl2, lane, rbs);
         tile_start(j + 1);
-        step<D, true, true, false, false>(w, sm, j + 1, sa, sb, 0, sl2, lane, bad, rbs);
+        step<D, true, true, false, false>(w, sm, j + 1, sa, sb, 0, sl2, lane, rbs);
     }
     for (; j + 1 < nb - 1; j += 2) {
         tile_start(j);
-        step<D, true, true, true, false>(w, sm, j, sb, sa, thr - kKB * j, sl2, lane, bad, rbs);
+        step<D, true, true, true, false>(w, sm, j, sb, sa, thr - kKB * j, sl2, lane, rbs);
         tile_start(j + 1);
-        step<D, true, true, true, false>(w, sm, j + 1, sa, sb, thr - kKB * (j + 1), sl2, lane,
-                                         bad, rbs);
+        step<D, true, true, true, false>(w, sm, j + 1, sa, sb, thr - kKB * (j + 1), sl2, lane, rbs);
     }
     // an odd count of full steps leaves one, which moves its next S^T into sb
     // (the masked variant leaves a block with no invisible key unchanged)
     if (j < nb - 1) {
         tile_start(j);
-        step<D, true, true, true, false>(w, sm, j, sb, sa, thr - kKB * j, sl2, lane, bad, rbs);
+        step<D, true, true, true, false>(w, sm, j, sb, sa, thr - kKB * j, sl2, lane, rbs);
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
             sb[rb] = sa[rb];
@@ -1476,9 +1463,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
         tile_start(nb - 1);
         if (nb - 1 >= bm)
             step<D, false, true, true, false>(w, sm, nb - 1, sb, sb, thr - kKB * (nb - 1), sl2,
-                                              lane, bad, rbs);
+                                              lane, rbs);
         else
-            step<D, false, true, false, false>(w, sm, nb - 1, sb, sb, 0, sl2, lane, bad, rbs);
+            step<D, false, true, false, false>(w, sm, nb - 1, sb, sb, 0, sl2, lane, rbs);
     }
     // step nb: P*V of the last block
     if (nb > 0) {
@@ -1489,6 +1476,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
         tile_start(j);
     }
     __syncthreads();  // every wave is past its last read of the stages
+    // A row sum only grows (its terms are >= 0; inf and NaN stay), so one
+    // test after the loop finds every row whose sum came too close to
+    // overflow (or is not finite) at any step.
+    bool bad = false;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+        bad = bad || !(w.lsum[rb] <= kWeightSumLimit);
     if (__any(bad))
         exact_rows<D, kContig>(w, lds + wave * (C::kLdsBytes / 2 / kWaves), a, bt, L, kv_off, nb,
                                wpf, thr, rbs, lane, window, j0);
