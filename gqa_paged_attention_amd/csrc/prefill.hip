@@ -746,10 +746,17 @@ __device__ __forceinline__ void win_weights_rb(float &m, float &lsum, u32x4_t (&
     asm volatile("" ::"v"(pop[0]), "v"(pop[1]), "v"(lsum));
 }
 
+// Whether any of the 32 rows at positions p .. p+31 sees a key of block blk
+// under a sliding window (row q sees q - window + 1 .. q).
+__device__ __forceinline__ bool win_sees(int blk, int p, int window)
+{
+    return kKB * blk <= p + 31 && kKB * blk + kKB - 1 >= p - window + 1;
+}
+
 // skew_step under a sliding window (runtime mask and first-key flags; the
 // few blocks of a window do not repay compile-time variants).  Row block 0's
 // rows start at position p0; row block 1's at p0 + 32.
-template <int D>
+template <int D, bool kEdges>
 __device__ __forceinline__ void win_step(WaveState<D> &w, const Smem<D> &sm, int b, bool next,
                                          f32x16_t (&s)[2], const u32x4_t (&kcur)[D / 16],
                                          u32x4_t (&knext)[D / 16], u32x4_t (&vop)[D / 32][2],
@@ -762,22 +769,32 @@ __device__ __forceinline__ void win_step(WaveState<D> &w, const Smem<D> &sm, int
         return !(kKB * blk >= p + 32 - window && kKB * blk + kKB - 1 <= p);
     };
     auto lazy = [&](int blk, int p) { return kKB * blk <= max(p + 32 - window, 0); };
+    // kEdges: row block rb (rows p0 + 32 rb ..) skips the blocks none of its
+    // rows sees (all weights 0): its S^T, weights and P*V of them.  Steps
+    // where both row blocks see both blocks run without these branches.
+    const bool cur0 = !kEdges || win_sees(b, p0, window);
+    const bool cur1 = !kEdges || win_sees(b, p0 + 32, window);
+    const bool next0 = next && (!kEdges || win_sees(b + 1, p0, window));
+    const bool next1 = next && (!kEdges || win_sees(b + 1, p0 + 32, window));
     if (next)
         read_k<D>(knext, k_block<D>(sm, b + 2), 0, lane);
-    if (next)
+    if (next0)
         qk_rb<D>(s[0], w.qop[0], kcur);
-    pv_mfma<D>(w.acc[0], vop, w.pop[0]);
-    win_weights_rb(w.m[1], w.lsum[1], w.pop[1], s[1], thr - kKB * b + 32, window,
-                   masked(b, p0 + 32), lazy(b, p0 + 32), sl2);
+    if (cur0)
+        pv_mfma<D>(w.acc[0], vop, w.pop[0]);
+    if (cur1)
+        win_weights_rb(w.m[1], w.lsum[1], w.pop[1], s[1], thr - kKB * b + 32, window,
+                       masked(b, p0 + 32), lazy(b, p0 + 32), sl2);
     __builtin_amdgcn_sched_barrier(0);
-    if (next)
+    if (next1)
         qk_rb<D>(s[1], w.qop[1], kcur);
-    pv_mfma<D>(w.acc[1], vop, w.pop[1]);
-    if (next) {
+    if (cur1)
+        pv_mfma<D>(w.acc[1], vop, w.pop[1]);
+    if (next0)
         win_weights_rb(w.m[0], w.lsum[0], w.pop[0], s[0], thr - kKB * (b + 1), window,
                        masked(b + 1, p0), lazy(b + 1, p0), sl2);
+    if (next)
         read_v<D>(vop, v_block<D>(sm, b + 1), 0, lane);
-    }
 }
 
 // One 32-key block of K and V fetched straight from the paged cache: kPer
@@ -1209,19 +1226,40 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
         tile_start(j0 - 2);
         tile_start(j0 - 1);
         read_k<D>(ka, k_block<D>(sm, j0), 0, lane);
-        qk_rb<D>(s[0], w.qop[0], ka);
-        qk_rb<D>(s[1], w.qop[1], ka);
+        if (win_sees(j0, wpf, window))
+            qk_rb<D>(s[0], w.qop[0], ka);
+        if (win_sees(j0, wpf + 32, window))
+            qk_rb<D>(s[1], w.qop[1], ka);
         read_k<D>(ka, k_block<D>(sm, j0 + 1), 0, lane);
         read_v<D>(vop, v_block<D>(sm, j0), 0, lane);
-        win_weights_rb(w.m[0], w.lsum[0], w.pop[0], s[0], thr - kKB * j0, window, true, true, sl2);
-        for (int j = j0; j < nb; j += 2) {
+        if (win_sees(j0, wpf, window))
+            win_weights_rb(w.m[0], w.lsum[0], w.pop[0], s[0], thr - kKB * j0, window, true, true,
+                           sl2);
+        // Steps in pairs (K of the next block alternates between ka and
+        // kb): first those with blocks row block 1 does not see, then those
+        // whose three blocks j .. j+2 both row blocks see (row block 1's
+        // oldest block lo1 on, up to row block 0's newest, hi0), then the
+        // rest.
+        const int lo1 = max(wpf + 32 - window + 1, 0) / kKB, hi0 = (wpf + 31) / kKB;
+        int j = j0;
+        auto pair = [&](auto edges) {
+            constexpr bool kEdges = decltype(edges)::value;
             tile_start(j);
-            win_step<D>(w, sm, j, j + 1 < nb, s, ka, kb, vop, thr, wpf, window, sl2, lane);
+            win_step<D, kEdges>(w, sm, j, j + 1 < nb, s, ka, kb, vop, thr, wpf, window, sl2,
+                                lane);
             if (j + 1 < nb) {
                 tile_start(j + 1);
-                win_step<D>(w, sm, j + 1, j + 2 < nb, s, kb, ka, vop, thr, wpf, window, sl2, lane);
+                win_step<D, kEdges>(w, sm, j + 1, j + 2 < nb, s, kb, ka, vop, thr, wpf, window,
+                                    sl2, lane);
             }
-        }
+            j += 2;
+        };
+        while (j < nb && j < lo1)
+            pair(std::true_type{});
+        while (j + 1 < nb && j + 2 <= hi0)
+            pair(std::false_type{});
+        while (j < nb)
+            pair(std::true_type{});
         for (int j = nb; j + 2 <= C::kBPT * ntiles; ++j)
             tile_start(j);
     } else {
