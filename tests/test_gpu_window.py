@@ -170,6 +170,23 @@ def test_prefill_window_tail_on_partial_last_page(d, window_route):
                 f"prefill tails d={d} window {w}")
 
 
+def test_prefill_window_block_edges_pipelined():
+    """The pipelined windowed prefill skips, per row block, the 32-key blocks
+    none of its rows sees (the block past row block 0's last row, the blocks
+    below row block 1's window), and runs its middle steps without those
+    tests.  Windows just below, at and above multiples of the block, and
+    chunks whose first row sits at every offset class within a block (the
+    prefix lengths 0, 5, 17, 31 and 870), put the first and last visible
+    block of each row block at every step position."""
+    L = [150, 205, 337, 351, 1000]
+    Lq = [150, 200, 320, 320, 130]
+    b = wl.small_batch(777, "bf16", L, Lq, 16, 2, 64, sink_mode="normal")
+    for w in (31, 32, 33, 63, 64, 65, 95, 96, 97, 160):
+        note(f"prefill window {w} block edges, pipelined: L={L} Lq={Lq}")
+        compare(run_prefill(b, window=w), oracle_full(b, window=w), "bf16",
+                f"prefill block edges window {w}")
+
+
 PIPELINED_CASES = [
     # id, seq_lens, q_lens, Hq, Hkv, window, late-key scale: chunks over
     # prefixes; rows whose windows span small and much larger logits (their
