@@ -769,8 +769,10 @@ __global__ __launch_bounds__(1024) void decode_merge(MergeArgs a)
 // waves would not fit on the chip at once), in the same arithmetic and order
 // (so the two give the same bits).  After the unit scan that places the
 // sequence's pieces, the lanes take one piece each (64 at a time) for the
-// common maximum of every head (sink included); then, 32 pieces at a time,
-// each piece's weight 2^(m_p - M) and sum l_p go to LDS, and every lane takes
+// common maximum of every head (sink included), keeping the (m_p, l_p) of the
+// first 64 pieces; then, 32 pieces at a time, each piece's weight
+// 2^(m_p - M) and sum l_p (from those registers, read again only past 64
+// pieces) go to LDS, and every lane takes
 // its (head, 4-dim chunk) items through the pieces in order: denominator from
 // the sink term on plus f_p l_p, values f_p acc_p, kPB pieces' loads in
 // flight at a time.  Workgroups without a unit wrote nothing; they count
@@ -823,18 +825,29 @@ __global__ __launch_bounds__(64) void decode_merge_group(MergeArgs a)
         return ((size_t)(b + w) * a.q_max + tok) * a.num_q_heads + h0;
     };
 
-    float M[kMaxG];
+    // (m, l) of piece w_lo + lane (the first 64 pieces) stay in registers for
+    // the weights below
+    float M[kMaxG], m_own[kMaxG], l_own[kMaxG];
 #pragma unroll
-    for (int hh = 0; hh < kMaxG; ++hh)
+    for (int hh = 0; hh < kMaxG; ++hh) {
         M[hh] = (hh < G && a.sinks) ? a.sinks[h0 + hh] * kLog2e : kNegInf;
+        m_own[hh] = kNegInf;
+        l_own[hh] = 0.f;
+    }
     for (int w0 = w_lo; w0 <= w_hi; w0 += 64) {
         const int w = w0 + lane;
         if (w <= w_hi && live(w)) {
             const float *ml = a.part_ml + row(w) * 2;
 #pragma unroll
             for (int hh = 0; hh < kMaxG; ++hh)
-                if (hh < G)
-                    M[hh] = fmaxf(M[hh], ml[2 * hh]);
+                if (hh < G) {
+                    const float2 v = *(const float2 *)(ml + 2 * hh);
+                    M[hh] = fmaxf(M[hh], v.x);
+                    if (w0 == w_lo) {
+                        m_own[hh] = v.x;
+                        l_own[hh] = v.y;
+                    }
+                }
         }
     }
 #pragma unroll
@@ -867,16 +880,27 @@ __global__ __launch_bounds__(64) void decode_merge_group(MergeArgs a)
     }
     for (int w0 = w_lo; w0 <= w_hi; w0 += kPiecesPerPass) {
         const int w = w0 + lane;
-        if (lane < kPiecesPerPass) {
-            const bool ok = w <= w_hi && live(w);
+        // the pass's pieces among the first 64 come from the lanes that hold them
+        const int off = w0 - w_lo;
+        const bool ok = lane < kPiecesPerPass && w <= w_hi && live(w);
 #pragma unroll
-            for (int hh = 0; hh < kMaxG; ++hh) {
-                if (hh < G) {
+        for (int hh = 0; hh < kMaxG; ++hh) {
+            if (hh < G) {
+                float mv = kNegInf, lv = 0.f;
+                if (off < 64) {
+                    mv = __shfl(m_own[hh], (off + lane) & 63, 64);
+                    lv = __shfl(l_own[hh], (off + lane) & 63, 64);
+                }
+                if (lane < kPiecesPerPass) {
                     float f = 0.f, l = 0.f;
                     if (ok) {
-                        const float2 ml = *(const float2 *)(a.part_ml + (row(w) + hh) * 2);
-                        f = ml.x == kNegInf ? 0.f : exp2_fast(ml.x - M[hh]);
-                        l = ml.y;
+                        if (off >= 64) {
+                            const float2 ml = *(const float2 *)(a.part_ml + (row(w) + hh) * 2);
+                            mv = ml.x;
+                            lv = ml.y;
+                        }
+                        f = mv == kNegInf ? 0.f : exp2_fast(mv - M[hh]);
+                        l = lv;
                     }
                     wf[lane * kMaxG + hh] = f;
                     wl[lane * kMaxG + hh] = l;
