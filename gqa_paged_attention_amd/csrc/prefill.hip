@@ -7,11 +7,11 @@
 // keys, so a chunk over a cached prefix sees the whole prefix.
 //
 // Work decomposition.  Each wave owns NRB row blocks of 32 rows (d = 64:
-// NRB = 2; d = 128: NRB = 1).  At d = 64 with a group size divisible by 4 a
-// workgroup of 4 waves takes the same 64 rows of four query heads of one KV
-// head (every wave sees the same keys and masks, and each K/V tile serves
-// four heads); otherwise its 4 waves take consecutive row blocks of one query
-// head (BM = 256 rows at d = 64, 128 at d = 128).  The 1-D grid is ordered so
+// NRB = 2; d = 128: NRB = 1).  With a group size divisible by 4 a workgroup
+// of 4 waves takes the same rows (64 at d = 64, 32 at d = 128) of four query
+// heads of one KV head (every wave sees the same keys and masks, and each K/V
+// tile serves four heads); otherwise its 4 waves take consecutive row blocks
+// of one query head (BM = 256 rows at d = 64, 128 at d = 128).  The 1-D grid is ordered so
 // that every workgroup of one (sequence, KV head) runs on the same XCD (its
 // L2 then serves the K/V tiles to all of them) and the query tiles with the
 // most keys start first.
@@ -1697,11 +1697,9 @@ hipError_t launch_d(const PrefillLaunch &p)
                            kWindowLdsBytes<D>, p.stream, a);
         return hipGetLastError();
     }
-    // four query heads per workgroup where the group allows it (d = 64)
-    if constexpr (D == 64) {
-        if (a.group % 4 == 0 && !prefill_one_head())
-            return launch_causal_hpw<D, 4>(a, p);
-    }
+    // four query heads per workgroup where the group allows it
+    if (a.group % 4 == 0 && !prefill_one_head())
+        return launch_causal_hpw<D, 4>(a, p);
     return launch_causal_hpw<D, 1>(a, p);
 }
 

@@ -461,10 +461,10 @@ const char *attn_sinks_status_string(int status);
  * Debug settings, for diagnostics and tests; the first two give the same
  * results bit for bit, the third the same within rounding.  Defaults come
  * from the environment, read once:
- *   ATTN_DEBUG_PREFILL_ONE_HEAD  bf16 causal prefill at head_dim 64 with a
- *                                group size divisible by 4 gives each
- *                                workgroup one query head (256 rows) instead
- *                                of four (64 rows each)
+ *   ATTN_DEBUG_PREFILL_ONE_HEAD  bf16 causal prefill with a group size
+ *                                divisible by 4 gives each workgroup one
+ *                                query head (256 rows at head_dim 64, 128 at
+ *                                128) instead of four (64 or 32 rows each)
  *                                (ATTN_SINKS_PREFILL_ONE_HEAD=1)
  *   ATTN_DEBUG_PREFILL_WAIT_ALL  the prefill's waits for its direct K/V tile
  *                                loads take every load in flight instead of

@@ -1,7 +1,7 @@
 """The prefill's kernel variants give the same bits.
 
-At head_dim 64 with a group size divisible by 4 a prefill workgroup takes
-the same rows of four query heads; the debug settings give each workgroup
+With a group size divisible by 4 a prefill workgroup takes the same rows
+of four query heads (head_dim 64 and 128); the debug settings give each workgroup
 one head instead (ATTN_DEBUG_PREFILL_ONE_HEAD) and make every tile wait
 take all loads in flight (ATTN_DEBUG_PREFILL_WAIT_ALL).  The per-row
 arithmetic is the same in all of them, so their outputs must be
@@ -94,10 +94,19 @@ def test_full_gptoss_prefill_variants():
     check_sampled(out, pre, 256, seed=5, what="gpt-oss prefill, variants")
 
 
-def test_prefill_d128_wait_all_bit_identical():
-    # head_dim 128: one head per workgroup, 4 loads per tile and wave
-    b = wl.small_batch(131, "bf16", [700, 129, 1000], [300, 129, 1000], 16, 4, 128,
-                       sink_mode="normal")
-    note("prefill d=128 variants")
+@pytest.mark.parametrize("hkv", [4, 2], ids=["group_4", "group_16"])
+def test_prefill_d128_variants_bit_identical(hkv):
+    # head_dim 128: 32 rows of four heads per workgroup or 128 rows of one,
+    # 4 loads per tile and wave; chunks over prefixes and a ragged tail
+    b = wl.small_batch(131 + hkv, "bf16", [700, 129, 1000, 45], [300, 129, 1000, 45], 32, hkv,
+                       128, sink_mode="normal")
+    note(f"prefill d=128 variants, Hq=32 Hkv={hkv}")
     out = _each_variant(lambda: run_prefill(b))
-    compare(out, oracle_full(b), "bf16", "prefill d=128 variants")
+    compare(out, oracle_full(b), "bf16", f"prefill d=128 variants Hkv={hkv}")
+
+
+def test_ragged_d128_variants_bit_identical():
+    r = wl.ragged_batch(97, "bf16", [300, 1000, 17], [300, 1000, 17], 16, 4, 128)
+    note("ragged d=128 variants, causal")
+    out = _each_variant(lambda: run_ragged(r, True, with_lse=False)[0])
+    compare(out, oracle_full(r.paged), "bf16", "ragged d=128 variants")
