@@ -10,8 +10,8 @@ context lengths uniform in [1024, 8192], 16-token HND pages, bf16, seeded
 synthetic data.  Inputs are resident in HBM before timing starts.  L2 and the
 Infinity Cache are flushed (a 1 GiB write) before every step, outside the
 timed events.  The headline value is decode KV-read GB/s; the same line also
-carries the causal prefill (TFLOP/s), the Qwen3-235B-shaped decode, the
-mixed batch and the sliding-window, multi-token, ragged, KV-append and
+carries the causal prefill (TFLOP/s), the Qwen3-235B-shaped decode and
+causal prefill (head_dim 128), the mixed batch and the sliding-window, multi-token, ragged, KV-append and
 RoPE-append legs, each against its own roofline, plus the fp64 CPU oracle
 timed on the host cores (a baseline, not a target).  Every leg reports the
 mean step time with the median and minimum beside it.  The RoPE-append leg
@@ -842,6 +842,15 @@ def main():
         del keep, qw
         extra["qwen_decode"] = q_res
         log(json.dumps(q_res))
+        qp = wl.qwen_prefill(0)
+        with leg_range(torch, "qwen_prefill"):
+            qp_res, _ = bench_prefill(torch, ga, timer, qp, max(K // 2, 3), max(W // 2, 1),
+                                      "Qwen3-235B-shaped causal prefill, bf16: 4 seqs x 4096 "
+                                      "tokens, 64 q / 4 KV heads, head_dim 128, sinks -inf, "
+                                      "seed 0")
+        del qp
+        extra["qwen_prefill"] = qp_res
+        log(json.dumps(qp_res))
 
     if args.profile_run:
         # a plain 1 GiB device copy: its FETCH_SIZE / WRITE_SIZE counters give

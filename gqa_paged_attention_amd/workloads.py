@@ -426,6 +426,17 @@ def qwen_decode(seed: int = 0, keep_logical: bool = False, sink_mode: str = "neg
     return b
 
 
+def qwen_prefill(seed: int = 0, keep_logical: bool = False) -> PagedBatch:
+    """bf16 causal prefill in the Qwen decode's head shape: 4 seqs x 4096
+    tokens, 64/4 heads, d=128, sinks = -inf."""
+    gen = torch.Generator().manual_seed(seed)
+    L = torch.full((4,), 4096, dtype=torch.int32)
+    b = build_batch(gen, "bf16", L, L, 64, 4, 128, sink_mode="neginf",
+                    keep_logical=keep_logical)
+    b.meta["name"] = "qwen_prefill"
+    return b
+
+
 def mixed(seed: int = 0, keep_logical: bool = False):
     """bf16, 64/8, d=64, sinks ~ N(0, 2): 32 decode seqs (L ~ U[2048, 16384])
     and 2 prefill chunks of 2048 tokens over 8192-token cached prefixes, all in
