@@ -1473,6 +1473,35 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
                                                 &lr);
             __builtin_amdgcn_sched_barrier(0);
         }
+    } else if constexpr (kLdsCycle<D> == 5) {
+        // One block per tile and five stages (d = 128): runs of ten steps
+        // (two LDS cycles, an even count for the register-set swap) from
+        // block 1, so every run starts at a block that is 1 modulo the cycle.
+        for (; j + 9 < steady_end; j += 10) {
+            LdsLanes<D> lr = lane_ofs;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+                asm volatile("" : "+v"(lr.k[kk]));
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                asm volatile("" : "+v"(lr.v[db]));
+            auto two = [&](auto p0) {
+                constexpr int kP = decltype(p0)::value;
+                tile_start(j + kP - 1);
+                step<D, true, true, false, false, kP % 5>(w, sm, j + kP - 1, sb, sa, 0, sl2, lane,
+                                                          rbs, &lr);
+                __builtin_amdgcn_sched_barrier(0);
+                tile_start(j + kP);
+                step<D, true, true, false, false, (kP + 1) % 5>(w, sm, j + kP, sa, sb, 0, sl2,
+                                                                lane, rbs, &lr);
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            two(std::integral_constant<int, 1>{});
+            two(std::integral_constant<int, 3>{});
+            two(std::integral_constant<int, 5>{});
+            two(std::integral_constant<int, 7>{});
+            two(std::integral_constant<int, 9>{});
+        }
     }
     for (; j + 1 < steady_end; j += 2) {
         tile_start(j);
