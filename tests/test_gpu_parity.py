@@ -53,6 +53,8 @@ PREFILL_CASES = [
     ("d64_chunks_over_prefix", "bf16", [500, 1000, 64], [100, 257, 1], 16, 2, 64, "normal", 2.0),
     ("d128_full", "bf16", [200, 333], [200, 333], 8, 2, 128, "normal", 1.0),
     ("d128_chunk", "bf16", [700], [129], 16, 1, 128, "none", 1.0),
+    # waves whose unmasked steps fill one run of ten (369) and two (736)
+    ("d128_full_steady_runs", "bf16", [736, 369], [736, 369], 8, 2, 128, "normal", 1.0),
     ("d64_empty_chunk_between", "bf16", [50, 80, 90], [50, 0, 90], 8, 8, 64, "normal", 1.0),
     ("d64_g1_tail", "bf16", [255, 256, 257], [255, 256, 257], 4, 4, 64, "neginf", 1.0),
     ("f32_d64", "f32", [40, 150], [40, 100], 8, 2, 64, "normal", 1.0),
