@@ -1485,6 +1485,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
                 asm volatile("" : "+v"(lr.v[db]));
+            // two(P): the steps of blocks j+P-1 and j+P, which are P and
+            // P+1 modulo the cycle
             auto two = [&](auto p0) {
                 constexpr int kP = decltype(p0)::value;
                 tile_start(j + kP - 1);
