@@ -48,9 +48,10 @@ TRAFFIC_FILE = os.path.join(PROFILES, "decode_split_bf16_gptoss_decode_traffic.t
 PREFILL_TRAFFIC_FILE = os.path.join(PROFILES, "prefill_bf16_gptoss_prefill_traffic.txt")
 PREFILL_COUNTER_FILE = os.path.join(PROFILES, "prefill_bf16_gptoss_prefill_counters.txt")
 # (api.cpp decides the launch shapes, kernels.h holds the constants they use)
-DECODE_SOURCES = ["gqa_paged_attention_amd/csrc/decode.hip", "gqa_paged_attention_amd/csrc/common.h",
+DECODE_SOURCES = ["gqa_paged_attention_amd/csrc/decode.hip", "gqa_paged_attention_amd/csrc/split.h",
+                  "gqa_paged_attention_amd/csrc/common.h",
                   "gqa_paged_attention_amd/csrc/kernels.h", "gqa_paged_attention_amd/csrc/api.cpp"]
-PREFILL_SOURCES = ["gqa_paged_attention_amd/csrc/prefill.hip",
+PREFILL_SOURCES = ["gqa_paged_attention_amd/csrc/prefill.hip", "gqa_paged_attention_amd/csrc/split.h",
                    "gqa_paged_attention_amd/csrc/common.h",
                    "gqa_paged_attention_amd/csrc/kernels.h", "gqa_paged_attention_amd/csrc/api.cpp"]
 
@@ -429,7 +430,8 @@ def bench_ragged(torch, ga, timer, steps, warmup, wl):
 def bench_mixed(torch, ga, timer, steps, warmup, wl):
     """The mixed batch: the decode rows (split + merge) and the two prefill
     chunks, one after the other on one stream, and again with the decode half
-    on a second stream beside the prefill half.  The decode half and the
+    on a second stream beside the prefill half, and as one attn_sinks_mixed
+    call (one launch for both halves, then the merge).  The decode half and the
     prefill half are each timed on their own as well as the whole step, with
     events only around what is timed (none between its launches)."""
     full, dec, pre = wl.mixed(0)
@@ -460,6 +462,20 @@ def bench_mixed(torch, ga, timer, steps, warmup, wl):
         main.wait_stream(side)
 
     ro = timer.run([("overlapped", overlapped)], steps, warmup, flush=True)
+    # The same step as one attn_sinks_mixed call over the whole batch: the
+    # decode rows' split pass and the chunks' prefill in one launch (the split
+    # workgroups first), then the merge.
+    gf = full.to("cuda")
+    out_f = torch.empty_like(gf.q)
+    ws_f = torch.empty(ga.attn_sinks_decode_workspace_bytes(
+        dec.num_seqs, dec.num_q_heads, dec.num_kv_heads, dec.head_dim, dec.max_seq_len),
+        dtype=torch.uint8, device="cuda")
+    rm = timer.run([("one_launch", lambda: ga.attn_sinks_mixed(
+        gf.q, gf.k_cache, gf.v_cache, gf.block_table, gf.seq_lens, gf.cu_seqlens_q, gf.sinks,
+        gf.scale, out_f, dec.num_seqs, dec.max_seq_len, pre.max_q_len, pre.max_seq_len,
+        ws_f))], steps, warmup, flush=True)
+    if not (torch.equal(out_f[:dec.num_seqs], out_d) and torch.equal(out_f[dec.num_seqs:], out_p)):
+        raise RuntimeError("attn_sinks_mixed differs from the decode and prefill calls")
     nb, fl = decode_bytes(dec), prefill_flops(pre)
     dec_ms, pre_ms = rd["step_ms"], rp["step_ms"]
     bound_ms = (nb / (HBM_PEAK_GBS * 1e9) + fl / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
@@ -480,7 +496,10 @@ def bench_mixed(torch, ga, timer, steps, warmup, wl):
             "frac_of_serial_bound": round(bound_ms / r["step_ms"], 4),
             "two_stream_ms": round(ro["step_ms"], 4),
             "two_stream_ms_median": round(ro["step_ms_median"], 4),
-            "two_stream_frac_of_serial_bound": round(bound_ms / ro["step_ms"], 4)}
+            "two_stream_frac_of_serial_bound": round(bound_ms / ro["step_ms"], 4),
+            "one_launch_ms": round(rm["step_ms"], 4), "one_launch_ms_median":
+            round(rm["step_ms_median"], 4),
+            "one_launch_frac_of_serial_bound": round(bound_ms / rm["step_ms"], 4)}
 
 
 # ------------------------------------------------------------ cpu baseline

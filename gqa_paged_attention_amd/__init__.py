@@ -74,6 +74,8 @@ def library():
     lib.attn_sinks_decode_multi.argtypes = [I] * 11 + [P] * 7 + [F, P, P, Z, P]
     lib.attn_sinks_decode_multi.restype = I
     lib.attn_sinks_ragged.argtypes = [I] * 10 + [P] * 6 + [F, P, P, P]
+    lib.attn_sinks_mixed.argtypes = [I] * 13 + [P] * 7 + [F, P, P, Z, P]
+    lib.attn_sinks_mixed.restype = I
     lib.attn_sinks_ragged.restype = I
     lib.attn_sinks_status_string.argtypes = [I]
     lib.attn_sinks_status_string.restype = ctypes.c_char_p
@@ -203,6 +205,45 @@ def _decode(window, q, k_cache, v_cache, block_table, seq_lens, sinks, scale, ou
     else:
         status = library().attn_sinks_decode_window(*head, window, *tail)
     _raise(status)
+
+
+def attn_sinks_mixed(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     block_table: torch.Tensor, seq_lens: torch.Tensor,
+                     cu_seqlens_q: torch.Tensor, sinks: Optional[torch.Tensor], scale: float,
+                     out: torch.Tensor, num_decode_seqs: int, decode_max_seq_len: int,
+                     max_q_len: int, max_seq_len: int, workspace: Optional[torch.Tensor],
+                     stream=None) -> None:
+    """Enqueue attn_sinks_mixed: sequences [0, num_decode_seqs) are
+    single-token decodes in rows 0 .. num_decode_seqs - 1 of q [total_q][Hq][d],
+    the rest prefill chunks by cu_seqlens_q [B+1]; workspace as for
+    attn_sinks_decode over the decode sequences."""
+    dt = _DTYPE_CODE.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out)):
+        _check_dense(name, t, q.dtype)
+    for name, t in (("block_table", block_table), ("seq_lens", seq_lens),
+                    ("cu_seqlens_q", cu_seqlens_q)):
+        _check_dense(name, t, torch.int32)
+    _check_dense("sinks", sinks, torch.float32)
+    _check_dense("workspace", workspace)
+    total_q, Hq, d = q.shape
+    num_pages, Hkv, P, d2 = k_cache.shape
+    B = seq_lens.numel()
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q / k_cache / v_cache / out shapes disagree")
+    if block_table.dim() != 2 or block_table.shape[0] != B or cu_seqlens_q.numel() != B + 1:
+        raise ValueError("block_table / cu_seqlens_q do not match the batch")
+    nd = int(num_decode_seqs)
+    if not 0 <= nd <= B:
+        raise ValueError("num_decode_seqs out of range")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _raise(library().attn_sinks_mixed(
+        dt, nd, B - nd, Hq, Hkv, d, P, num_pages, block_table.shape[1],
+        int(decode_max_seq_len), total_q, int(max_q_len), int(max_seq_len), _ptr(q),
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(cu_seqlens_q),
+        _ptr(sinks), ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+        ctypes.c_size_t(ws_bytes), _stream_handle(stream)))
 
 
 def attn_sinks_decode_partials(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

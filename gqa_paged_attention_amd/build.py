@@ -53,7 +53,7 @@ COMMON_FLAGS = [
 # operations in the loop, so a register spill (scratch traffic) there would
 # let a wave read an LDS stage before it lands.  The build refuses them with
 # any scratch.
-NO_SCRATCH_KERNELS = ("prefill_bf16I",)
+NO_SCRATCH_KERNELS = ("prefill_bf16I", "mixed_bf16I")
 
 
 def check_no_scratch(remarks: str, src: str) -> None:

@@ -456,14 +456,19 @@ int attn_sinks_prefill(int dtype, int num_seqs, int num_q_heads, int num_kv_head
                                      cu_seqlens_q, sinks, scale, 0, out, stream);
 }
 
-int attn_sinks_prefill_window(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
-                              int head_dim, int page_size, int num_pages, int max_pages_per_seq,
-                              int total_q, int max_q_len, int max_seq_len, const void *q,
-                              const void *k_cache, const void *v_cache,
-                              const int32_t *block_table, const int32_t *seq_lens,
-                              const int32_t *cu_seqlens_q, const float *sinks, float scale,
-                              int window, void *out, void *stream)
+// Checks of a paged causal prefill call; fills the launch description (the
+// bf16 kernels') and returns ATTN_OK, or the error code with nothing
+// enqueued.  *empty is set when there is nothing to compute.
+static int prepare_prefill(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                           int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                           int total_q, int max_q_len, int max_seq_len, const void *q,
+                           const void *k_cache, const void *v_cache,
+                           const int32_t *block_table, const int32_t *seq_lens,
+                           const int32_t *cu_seqlens_q, const float *sinks, float scale,
+                           int window, void *out, void *stream, attn::PrefillLaunch *pl,
+                           bool *empty)
 {
+    *empty = false;
     int rc = check_common(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                           num_pages, max_pages_per_seq, max_seq_len);
     if (rc != ATTN_OK)
@@ -472,8 +477,10 @@ int attn_sinks_prefill_window(int dtype, int num_seqs, int num_q_heads, int num_
         return ATTN_ERR_SHAPE;
     if (!std::isfinite(scale) || window < 0)
         return ATTN_ERR_SHAPE;
-    if (num_seqs == 0 || total_q == 0)
+    if (num_seqs == 0 || total_q == 0) {
+        *empty = true;
         return ATTN_OK;
+    }
     if (!q || !out || !seq_lens || !cu_seqlens_q || !k_cache || !v_cache || !block_table)
         return ATTN_ERR_NULL;
     const void *vec[] = {q, k_cache, v_cache, out};
@@ -485,15 +492,7 @@ int attn_sinks_prefill_window(int dtype, int num_seqs, int num_q_heads, int num_
         if (p && !aligned4(p))
             return ATTN_ERR_ALIGN;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-
-    if (dtype == ATTN_DTYPE_F32) {
-        hipError_t e = attn::launch_rows_f32(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                             max_pages_per_seq, total_q, q, k_cache, v_cache,
-                                             block_table, seq_lens, cu_seqlens_q, sinks, scale,
-                                             window, out, s);
-        return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-    }
-    attn::PrefillLaunch p;
+    attn::PrefillLaunch &p = *pl;
     p.dtype = dtype;
     p.num_seqs = num_seqs;
     p.num_q_heads = num_q_heads;
@@ -517,7 +516,101 @@ int attn_sinks_prefill_window(int dtype, int num_seqs, int num_q_heads, int num_
     p.scale = scale;
     p.out = out;
     p.stream = s;
+    return ATTN_OK;
+}
+
+int attn_sinks_prefill_window(int dtype, int num_seqs, int num_q_heads, int num_kv_heads,
+                              int head_dim, int page_size, int num_pages, int max_pages_per_seq,
+                              int total_q, int max_q_len, int max_seq_len, const void *q,
+                              const void *k_cache, const void *v_cache,
+                              const int32_t *block_table, const int32_t *seq_lens,
+                              const int32_t *cu_seqlens_q, const float *sinks, float scale,
+                              int window, void *out, void *stream)
+{
+    attn::PrefillLaunch p;
+    bool empty = false;
+    int rc = prepare_prefill(dtype, num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                             num_pages, max_pages_per_seq, total_q, max_q_len, max_seq_len, q,
+                             k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, sinks, scale,
+                             window, out, stream, &p, &empty);
+    if (rc != ATTN_OK || empty)
+        return rc;
+    if (dtype == ATTN_DTYPE_F32) {
+        hipError_t e = attn::launch_rows_f32(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             max_pages_per_seq, total_q, q, k_cache, v_cache,
+                                             block_table, seq_lens, cu_seqlens_q, sinks, scale,
+                                             window, out, p.stream);
+        return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    }
     return attn::launch_prefill_bf16(p) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_sinks_mixed(int dtype, int num_decode_seqs, int num_prefill_seqs, int num_q_heads,
+                     int num_kv_heads, int head_dim, int page_size, int num_pages,
+                     int max_pages_per_seq, int decode_max_seq_len, int total_q, int max_q_len,
+                     int max_seq_len, const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *block_table, const int32_t *seq_lens,
+                     const int32_t *cu_seqlens_q, const float *sinks, float scale, void *out,
+                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    const int nd = num_decode_seqs, np = num_prefill_seqs;
+    if (nd < 0 || np < 0 || (long long)nd + np > 65535 || total_q < nd)
+        return ATTN_ERR_SHAPE;
+    // the decode part: sequences [0, nd), query rows 0 .. nd - 1
+    attn::DecodeLaunch dp;
+    int rc = prepare_decode(dtype, nd, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                            max_pages_per_seq, decode_max_seq_len, q, k_cache, v_cache,
+                            block_table, seq_lens, sinks, scale, 0, out, workspace,
+                            workspace_bytes, stream, true, true, &dp);
+    if (rc != ATTN_OK)
+        return rc;
+    // the prefill part: sequences [nd, nd + np), their rows by cu_seqlens_q
+    const size_t table_off = (size_t)nd * (size_t)max_pages_per_seq;
+    const int32_t *bt_p = block_table ? block_table + table_off : nullptr;
+    const int32_t *lens_p = seq_lens ? seq_lens + nd : nullptr;
+    const int32_t *cu_p = cu_seqlens_q ? cu_seqlens_q + nd : nullptr;
+    attn::PrefillLaunch pp;
+    bool empty = false;
+    rc = prepare_prefill(dtype, np, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                         max_pages_per_seq, total_q, max_q_len, max_seq_len, q, k_cache, v_cache,
+                         bt_p, lens_p, cu_p, sinks, scale, 0, out, stream, &pp, &empty);
+    if (rc != ATTN_OK)
+        return rc;
+    // one launch where the decode part takes the split pass and both parts
+    // have work; otherwise (and for fp32) the two calls one after the other
+    const bool fused = nd > 0 && !empty &&
+                       decode_max_seq_len > attn::kDirectWindowMax && dp.num_wgs > 0 &&
+                       !attn::debug_setting(attn::kDebugPrefillWaitAll);
+    if (dtype == ATTN_DTYPE_F32) {
+        // every row of the batch in one row-kernel launch: a decode row is a
+        // one-row sequence there, computed as attn_sinks_decode computes it
+        hipError_t e = attn::launch_rows_f32(nd + np, num_q_heads, num_kv_heads, head_dim,
+                                             max_pages_per_seq, total_q, q, k_cache, v_cache,
+                                             block_table, seq_lens, cu_seqlens_q, sinks, scale,
+                                             0, out, reinterpret_cast<hipStream_t>(stream));
+        return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    }
+    if (!fused) {
+        // (the bf16 prefill addresses q and out by the absolute row offsets
+        // in cu_seqlens_q, so the chunks' part of the arrays is theirs alone)
+        if (nd > 0) {
+            rc = attn_sinks_decode(dtype, nd, num_q_heads, num_kv_heads, head_dim, page_size,
+                                   num_pages, max_pages_per_seq, decode_max_seq_len, q, k_cache,
+                                   v_cache, block_table, seq_lens, sinks, scale, out, workspace,
+                                   workspace_bytes, stream);
+            if (rc != ATTN_OK)
+                return rc;
+        }
+        if (empty)
+            return ATTN_OK;
+        return attn_sinks_prefill(dtype, np, num_q_heads, num_kv_heads, head_dim, page_size,
+                                  num_pages, max_pages_per_seq, total_q, max_q_len, max_seq_len,
+                                  q, k_cache, v_cache, bt_p, lens_p, cu_p, sinks, scale, out,
+                                  stream);
+    }
+    if (attn::launch_mixed_bf16(dp, pp) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return attn::launch_decode_merge(dp) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_sinks_append_kv(int dtype, int num_seqs, int num_kv_heads, int head_dim, int page_size,

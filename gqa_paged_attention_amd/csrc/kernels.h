@@ -83,6 +83,10 @@ hipError_t launch_decode_merge(const DecodeLaunch &p);
 constexpr int kDirectWindowMax = 512;
 hipError_t launch_decode_direct_bf16(const DecodeLaunch &p);
 hipError_t launch_prefill_bf16(const PrefillLaunch &p);
+// The split pass of a single-token decode batch (d) and the causal prefill of
+// chunks (p) in one launch, the split workgroups first; the caller then runs
+// launch_decode_merge(d).  Both on p.stream; same results as the two kernels.
+hipError_t launch_mixed_bf16(const DecodeLaunch &d, const PrefillLaunch &p);
 // KV append: new rows [total_new][Hkv][d] into their page slots (f32 or bf16,
 // elem_bytes 4 or 2); cu_seqlens_new NULL means one new token per sequence.
 hipError_t launch_append_kv(int elem_bytes, int num_seqs, int num_kv_heads, int head_dim,

@@ -64,6 +64,7 @@
 // tile T+2.
 #include "common.h"
 #include "kernels.h"
+#include "split.h"
 
 namespace attn {
 namespace {
@@ -174,6 +175,11 @@ struct PrefillArgs {
     int causal;        // 1: bottom-right causal; 0: every row sees all keys
     float *__restrict__ lse;  // [total_q][Hq] natural-log row LSE (sink included), or NULL
     float scale_log2;
+    // The one-launch mixed batch only: workgroups [0, split_wgs) run the
+    // split pass of its decode rows with these arguments (split_wgs_x of them
+    // per KV-head group); the prefill's own workgroups follow.
+    split::SplitArgs split;
+    int split_wgs_x, split_wgs;
 };
 
 // LDS tile layouts (bf16 elements).  K: 16-byte chunk c of key row r stored at
@@ -984,12 +990,12 @@ struct TileCoords {
     int b, g, h, qt;
 };
 
-template <int HPW>
+template <int HPW, bool kMixed = false>
 __device__ __forceinline__ TileCoords tile_of(const PrefillArgs &a)
 {
     const int hgroups = a.group / HPW;
     const int per_group = hgroups * a.num_q_tiles;
-    const int id = blockIdx.x;
+    const int id = kMixed ? (int)blockIdx.x - a.split_wgs : (int)blockIdx.x;
     int grp, r;
     const int main_ids = a.xcd_groups * per_group;
     if (id < main_ids) {
@@ -1107,15 +1113,31 @@ __device__ __forceinline__ void store_rows(const WaveState<D> &w, uint16_t *stag
 // one KV head, so every wave sees the same keys, masks and block count (no
 // wave waits at the tile barriers for the others' extra diagonal blocks) and
 // the causal range of a workgroup's tiles is 4 times finer.
-template <int D, bool kContig, bool kWaitAll, int HPW, bool kWin = false>
+// kMixed: the mixed batch in one launch.  Its first a.split_wgs workgroups
+// run the split pass of the batch's single-token decode rows instead (as
+// decode_split_bf16 runs it: workgroup id % split_wgs_x of KV-head group
+// id / split_wgs_x), so that they are dispatched before the prefill's
+// workgroups fill the chip and the memory-bound pass runs beside the
+// compute-bound one; the others run the prefill of its chunks.
+template <int D, bool kContig, bool kWaitAll, int HPW, bool kWin = false, bool kMixed = false>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16(PrefillArgs a)
 {
     static_assert(!kWin || (D == 64 && HPW == 4 && !kContig), "windowed layout");
+    static_assert(!kMixed || (!kContig && !kWin), "mixed batch: paged, causal, no window");
+    if constexpr (kMixed) {
+        if ((int)blockIdx.x < a.split_wgs) {
+            // waves past the workgroup's KV heads have no work (the split
+            // pass has no barrier)
+            if ((int)(threadIdx.x >> 6) < a.split.heads_per_wg)
+                split::split_body<D, 1>(a.split, split::FlatIdx{(unsigned)a.split_wgs_x});
+            return;
+        }
+    }
     using C = Cfg<D>;
     constexpr int NRB = C::kNRB;
     constexpr int kWavesPerHead = kWaves / HPW;
     constexpr int kRowsPerWg = 32 * NRB * kWavesPerHead;
-    const TileCoords tc = tile_of<HPW>(a);
+    const TileCoords tc = tile_of<HPW, kMixed>(a);
     const int b = tc.b, g = tc.g, qt = tc.qt;
 
     const int q0 = a.cu_seqlens_q[b];
@@ -1681,11 +1703,12 @@ hipError_t launch_window64(PrefillArgs a, const PrefillLaunch &p)
                               : launch_causal<64, false, false, 4, true>(a, wgs, p.stream);
 }
 
+// The prefill kernels' arguments for a launch description.
 template <int D>
-hipError_t launch_d(const PrefillLaunch &p)
+PrefillArgs prefill_args(const PrefillLaunch &p)
 {
     using C = Cfg<D>;
-    PrefillArgs a;
+    PrefillArgs a = {};
     a.q = (const uint16_t *)p.q;
     a.k_cache = (const uint16_t *)p.k_cache;
     a.v_cache = (const uint16_t *)p.v_cache;
@@ -1708,6 +1731,14 @@ hipError_t launch_d(const PrefillLaunch &p)
     a.causal = p.causal;
     a.lse = p.lse;
     a.scale_log2 = p.scale * kLog2e;
+    return a;
+}
+
+template <int D>
+hipError_t launch_d(const PrefillLaunch &p)
+{
+    const PrefillArgs a = prefill_args<D>(p);
+    const int groups = p.num_seqs * p.num_kv_heads;
     const long long wgs = (long long)groups * a.group * a.num_q_tiles;
     if (wgs > 0x7fffffffLL)
         return hipErrorInvalidValue;
@@ -1734,7 +1765,49 @@ hipError_t launch_d(const PrefillLaunch &p)
     return launch_causal_hpw<D, 1>(a, p);
 }
 
+// The mixed batch in one launch: the split pass of the decode part, its
+// workgroups rounded up to a multiple of 8 (the extra ones find no KV head
+// and return) so that the prefill workgroups keep their XCD grouping, then
+// the prefill of the chunks.
+template <int D, int HPW>
+hipError_t launch_mixed_d(const DecodeLaunch &dp, const PrefillLaunch &pp)
+{
+    PrefillArgs a = prefill_args<D>(pp);
+    const long long pwgs = causal_grid<D, HPW>(a, pp);
+    const int split_x = dp.num_wgs;
+    const int split_y = (dp.num_kv_heads + dp.heads_per_wg - 1) / dp.heads_per_wg;
+    const long long swgs = ((long long)split_x * split_y + 7) / 8 * 8;
+    if (split_x <= 0 || dp.heads_per_wg > kWaves || dp.q_max != 1 || pwgs + swgs > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    a.split = split::split_args(dp);
+    a.split_wgs_x = split_x;
+    a.split_wgs = (int)swgs;
+    constexpr int kLds = Cfg<D>::kLdsBytes;
+    static_assert(split::split_lds_bytes<D>(kDecodeMaxHeadsPerWg) <= (size_t)kLds, "split LDS");
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void *)prefill_bf16<D, false, false, HPW, false, true>,
+        hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (attr != hipSuccess)
+        return attr;
+    hipLaunchKernelGGL((prefill_bf16<D, false, false, HPW, false, true>),
+                       dim3((unsigned)(pwgs + swgs)), dim3(kThreads), kLds, pp.stream, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_mixed_hpw(const DecodeLaunch &dp, const PrefillLaunch &pp)
+{
+    if ((pp.num_q_heads / pp.num_kv_heads) % 4 == 0 && !prefill_one_head())
+        return launch_mixed_d<D, 4>(dp, pp);
+    return launch_mixed_d<D, 1>(dp, pp);
+}
+
 }  // namespace
+
+hipError_t launch_mixed_bf16(const DecodeLaunch &dp, const PrefillLaunch &pp)
+{
+    return pp.head_dim == 64 ? launch_mixed_hpw<64>(dp, pp) : launch_mixed_hpw<128>(dp, pp);
+}
 
 hipError_t launch_prefill_bf16(const PrefillLaunch &p)
 {

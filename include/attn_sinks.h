@@ -282,6 +282,42 @@ int attn_sinks_prefill_window(int dtype, int num_seqs, int num_q_heads, int num_
                               int window, void *out, void *stream);
 
 /*
+ * attn_sinks_mixed -- one batch of single-token decode sequences and causal
+ * prefill chunks over one page pool: the step of continuous batching, which
+ * serves concurrent requests, new prompts and running generations, in one
+ * batched paged forward ("GPT OSS" model notes, section 11).  The operation
+ * of each part is the one at the top of this file.
+ *
+ *   Sequences 0 .. num_decode_seqs - 1 are decodes: one query token each, in
+ *   row b of q and out (so cu_seqlens_q[b] = b for b <= num_decode_seqs, a
+ *   device-side precondition like those above), their lengths bounded by
+ *   decode_max_seq_len.  Sequences num_decode_seqs .. +num_prefill_seqs - 1
+ *   are prefill chunks: rows cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1,
+ *   bounded by max_q_len and max_seq_len; total_q counts every row of both.
+ *   seq_lens, block_table (max_pages_per_seq entries per sequence) and
+ *   cu_seqlens_q cover the whole batch.
+ *   The decode rows equal, bit for bit, attn_sinks_decode over the first
+ *   num_decode_seqs sequences, and the chunk rows those of attn_sinks_prefill
+ *   over the chunks alone (their rows, lengths and table rows taken as a
+ *   batch of their own).  fp32 computes every row in one row-kernel launch;
+ *   bf16 runs the two calls one after the other when either part is empty or
+ *   the decode part is short enough for its direct pass, and otherwise the
+ *   decode part's split pass and the prefill in one launch, the split pass's
+ *   workgroups first in the grid (so the memory-bound pass runs beside the
+ *   compute-bound prefill instead of before it), then the merge.
+ *   workspace: attn_sinks_decode_workspace_bytes(num_decode_seqs, num_q_heads,
+ *   num_kv_heads, head_dim, decode_max_seq_len) bytes.  Checks of both parts
+ *   run before anything is enqueued; codes as for the two calls.
+ */
+int attn_sinks_mixed(int dtype, int num_decode_seqs, int num_prefill_seqs, int num_q_heads,
+                     int num_kv_heads, int head_dim, int page_size, int num_pages,
+                     int max_pages_per_seq, int decode_max_seq_len, int total_q, int max_q_len,
+                     int max_seq_len, const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *block_table, const int32_t *seq_lens,
+                     const int32_t *cu_seqlens_q, const float *sinks, float scale, void *out,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * KV append.  Before the attention step each layer appends the new tokens'
  * K and V to its KV cache ("GPT OSS" model notes, section 3, forward graph;
  * section 11: per-layer paged K/V).  The n_b new tokens of sequence b are its
