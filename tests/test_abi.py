@@ -432,3 +432,44 @@ def test_debug_settings(lib):
         assert ga.attn_sinks_set_debug(s, before) == 0
     assert ga.attn_sinks_set_debug(3, 1) == -1
     assert ga.attn_sinks_set_debug(-1, 1) == -1
+
+
+def _mixed(lib, **kw):
+    # 2 decode sequences (rows 0, 1) and 1 prefill chunk of 30 rows
+    args = dict(dtype=1, nd=2, np=1, Hq=8, Hkv=2, d=64, P=16, pages=16, max_pages=4,
+                dec_len=64, Tq=32, mq=30, max_len=64, q=FAKE, k=FAKE, v=FAKE, bt=FAKE,
+                sl=FAKE, cu=FAKE, sinks=None, scale=0.125, out=FAKE, ws=FAKE,
+                ws_bytes=1 << 20)
+    args.update(kw)
+    return lib.attn_sinks_mixed(
+        args["dtype"], args["nd"], args["np"], args["Hq"], args["Hkv"], args["d"], args["P"],
+        args["pages"], args["max_pages"], args["dec_len"], args["Tq"], args["mq"],
+        args["max_len"], args["q"], args["k"], args["v"], args["bt"], args["sl"], args["cu"],
+        args["sinks"], ctypes.c_float(args["scale"]), args["out"], args["ws"],
+        ctypes.c_size_t(args["ws_bytes"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), ERR_UNSUPPORTED),
+    (dict(nd=-1), ERR_SHAPE),
+    (dict(np=-1), ERR_SHAPE),
+    (dict(nd=40000, np=30000), ERR_SHAPE),
+    (dict(Tq=1), ERR_SHAPE),              # fewer rows than decode sequences
+    (dict(dec_len=65), ERR_SHAPE),        # beyond max_pages * 16
+    (dict(mq=33), ERR_SHAPE),             # more chunk rows than rows
+    (dict(scale=float("inf")), ERR_SHAPE),
+    (dict(q=None), ERR_NULL),
+    (dict(cu=None), ERR_NULL),
+    (dict(ws=None), ERR_NULL),
+    (dict(ws_bytes=16), ERR_WORKSPACE),
+    (dict(out=FAKE + 4), ERR_ALIGN),
+    (dict(cu=FAKE + 2), ERR_ALIGN),
+])
+def test_mixed_rejects(lib, kw, code):
+    assert _mixed(lib, **kw) == code
+
+
+def test_mixed_empty_parts_enqueue_nothing(lib):
+    # nothing to compute in either part: checks pass, nothing is launched
+    assert _mixed(lib, nd=0, np=0, Tq=0, mq=0, dec_len=0, max_len=0) == OK
+    assert _mixed(lib, nd=0, np=1, Tq=0, mq=0) == OK
