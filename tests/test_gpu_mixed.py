@@ -70,7 +70,10 @@ def test_full_mixed_one_launch_equals_the_two_calls():
     check_sampled(got[32:], pre, 256, 11, "mixed call, prefill rows (256 sampled)")
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(64, 4, 128), (16, 8, 64), (32, 8, 64)])
+# (16, 2) and (4, 1): split workgroups with fewer KV heads than waves, whose
+# spare waves return at once beside the prefill's workgroups
+@pytest.mark.parametrize("hq,hkv,d", [(64, 4, 128), (16, 8, 64), (32, 8, 64), (16, 2, 64),
+                                      (4, 1, 128)])
 def test_small_mixed_against_oracle(hq, hkv, d):
     note(f"mixed call: small batch hq={hq} hkv={hkv} d={d}")
     # three decodes past the direct pass's bound (the one-launch route), then
